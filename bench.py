@@ -1,0 +1,270 @@
+#!/usr/bin/env python3
+"""Throughput of the ragged BF16 grouped GEMM on one MI355X.
+
+One step = one pass of the hot path over one batch of the MoE gate_up
+workload (E = 8 experts, 131072 tokens with balanced routing, d_model
+K = 2048, per-expert N = 1536, BF16 inputs, BF16 outputs, deterministic
+variant): forward Y = X W^T, data gradient dX = G W and weight gradient
+dW = G^T X, i.e. the three programs of an expert layer's training step.
+Inputs are seeded synthetic data resident in HBM before timing starts.
+
+Prints ONE JSON line: value = TFLOP/s of the whole step (3 x 2*M*N*K
+algorithmic FLOP per step / time per step), plus
+* roofline: the dominant kernel's achieved TFLOP/s (algorithmic FLOP per
+  launch / its average duration from HIP events on the launch stream)
+  against the MI355X dense BF16 MFMA peak;
+* cpu_baseline: the CPU oracle timed on this host's cores on a bounded
+  sample of the same workload;
+* programs: per-program times; with --all, the other measured workloads.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--all] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense BF16 MFMA (published)
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
+METRIC = "TFLOP/s and % of BF16 MFMA peak, grouped GEMM fwd/dgrad/wgrad (det, 1 GPU)"
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--reps", type=int, default=20, help="per-program timing repetitions")
+    ap.add_argument("--all", action="store_true", help="also time the other workloads")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--only", default="", help="profiling aid: run only these programs (comma list)")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def to_dev_bf16(torch, u16):
+    return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def time_call(torch, drgg, fn, reps):
+    """Mean per-kernel milliseconds of `fn` over reps calls, from the
+    library's HIP events on the launch stream."""
+    drgg.set_knob(drgg.KNOB_TIMING, 1)
+    acc = {}
+    try:
+        for _ in range(reps):
+            fn()
+            for name, ms in drgg.last_call_kernel_times():
+                acc.setdefault(name, []).append(ms)
+    finally:
+        drgg.set_knob(drgg.KNOB_TIMING, 0)
+    torch.cuda.synchronize()
+    return {k: float(np.mean(v)) for k, v in acc.items()}
+
+
+def gate_up_step(torch, drgg, prob):
+    X = to_dev_bf16(torch, prob.X)
+    W = to_dev_bf16(torch, prob.W)
+    G = to_dev_bf16(torch, prob.G)
+    offs = torch.from_numpy(prob.offs).cuda()
+    Y = torch.empty((prob.M, prob.N), dtype=torch.bfloat16, device="cuda")
+    dX = torch.empty((prob.M, prob.K), dtype=torch.bfloat16, device="cuda")
+    dW = torch.empty((prob.E, prob.N, prob.K), dtype=torch.bfloat16, device="cuda")
+    ws = drgg.Workspace()
+
+    def fwd():
+        drgg.grouped_gemm_fwd(X, W, offs, out_dtype=torch.bfloat16, out=Y)
+
+    def dgrad():
+        drgg.grouped_gemm_dgrad(G, W, offs, out_dtype=torch.bfloat16, out=dX)
+
+    def wgrad():
+        drgg.grouped_gemm_wgrad(X, G, offs, out_dtype=torch.bfloat16, deterministic=True, out=dW, workspace=ws)
+
+    return {"fwd": fwd, "dgrad": dgrad, "wgrad": wgrad}
+
+
+def cpu_baseline(prob):
+    """The oracle as it stands, on a bounded sample of the gate_up workload:
+    forward rows 0..4095 (all N), data-gradient rows 0..2047 (all K), weight
+    gradient of expert 0 for output rows n = 0..63 (all K, 16384 tokens)."""
+    import oracle
+    N, K = prob.N, prob.K
+    T0 = int(prob.offs[1] - prob.offs[0])
+    jobs = [
+        ("fwd", lambda: oracle.fwd(prob.X, prob.W, prob.offs, np.arange(4096 * N)), 2.0 * 4096 * N * K),
+        ("dgrad", lambda: oracle.dgrad(prob.G, prob.W, prob.offs, np.arange(2048 * K)), 2.0 * 2048 * K * N),
+        ("wgrad", lambda: oracle.wgrad(prob.X, prob.G, prob.offs, np.arange(64 * K)), 2.0 * 64 * K * T0),
+    ]
+    flops = secs = 0.0
+    for name, fn, f in jobs:
+        t = time.perf_counter()
+        fn()
+        dt = time.perf_counter() - t
+        log(f"cpu oracle {name}: {dt:.2f} s, {f / dt / 1e9:.2f} GFLOP/s")
+        flops += f
+        secs += dt
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": "fwd rows 0-4095 x all 1536 cols, dgrad rows 0-2047 x all 2048 cols, "
+                      "wgrad expert 0 rows n 0-63 x all 2048 cols over its 16384 tokens "
+                      f"({flops / 1e9:.1f} GFLOP in {secs:.1f} s, binary64 accumulation)"}
+
+
+def other_workloads(torch, drgg, synth, reps):
+    """Per-program times of the other measured workloads (context lines)."""
+    out = {}
+    for d_out in (48, 64, 512, 1024):
+        p = synth.config2(d_out)
+        X, G = to_dev_bf16(torch, p.X), to_dev_bf16(torch, p.G)
+        offs = torch.from_numpy(p.offs).cuda()
+        dW = torch.empty((1, p.N, p.K), dtype=torch.float32, device="cuda")
+        ws = drgg.Workspace()
+        for det in (True, False):
+            fn = lambda: drgg.grouped_gemm_wgrad(X, G, offs, out_dtype=torch.float32, deterministic=det,
+                                                 out=dW, workspace=ws)
+            fn()
+            t = time_call(torch, drgg, fn, reps)
+            ms = sum(t.values())
+            flop = 2.0 * p.M * p.N * p.K
+            byt = 2.0 * p.M * (p.N + p.K) + 4.0 * p.N * p.K
+            out[f"dense_wgrad_n{d_out}_{'det' if det else 'splitk'}"] = {
+                "us": ms * 1e3, "tflops": flop / ms / 1e9, "gbs_algorithmic": byt / ms / 1e6, "kernels_ms": t}
+        del X, G, dW
+    p = synth.config4()
+    X, G = to_dev_bf16(torch, p.X), to_dev_bf16(torch, p.G)
+    offs = torch.from_numpy(p.offs).cuda()
+    dW = torch.empty((p.E, p.N, p.K), dtype=torch.float32, device="cuda")
+    for det in (True, False):
+        ws = drgg.Workspace()
+        fn = lambda: drgg.grouped_gemm_wgrad(X, G, offs, out_dtype=torch.float32, deterministic=det,
+                                             out=dW, workspace=ws)
+        fn()
+        t = time_call(torch, drgg, fn, reps)
+        ms = sum(t.values())
+        flop = 2.0 * p.M * p.N * p.K
+        out[f"moe_down_zipf_wgrad_{'det' if det else 'splitk'}"] = {
+            "us": ms * 1e3, "tflops": flop / ms / 1e9, "pct_peak": 100 * flop / ms / 1e9 / PEAK_BF16_TFLOPS,
+            "kernels_ms": t}
+    del X, G, dW
+    p = synth.config5()
+    X, W, G = to_dev_bf16(torch, p.X), to_dev_bf16(torch, p.W), to_dev_bf16(torch, p.G)
+    offs = torch.from_numpy(p.offs).cuda()
+    flop = 2.0 * p.M * p.N * p.K
+    fns = {
+        "fwd": lambda: drgg.grouped_gemm_fwd(X, W, offs),
+        "dgrad": lambda: drgg.grouped_gemm_dgrad(G, W, offs),
+        "wgrad": lambda: drgg.grouped_gemm_wgrad(X, G, offs),
+    }
+    for name, fn in fns.items():
+        fn()
+        t = time_call(torch, drgg, fn, reps)
+        ms = sum(t.values())
+        out[f"dense_square_{name}"] = {"us": ms * 1e3, "tflops": flop / ms / 1e9,
+                                       "pct_peak": 100 * flop / ms / 1e9 / PEAK_BF16_TFLOPS, "kernels_ms": t}
+    del X, W, G
+    Xr, Wr = synth.router_inputs()
+    Xr, Wr = torch.from_numpy(Xr).cuda(), torch.from_numpy(Wr).cuda()
+    fn = lambda: drgg.router_gemm_fp32_bf16x3(Xr, Wr)
+    fn()
+    t = time_call(torch, drgg, fn, reps)
+    ms = sum(t.values())
+    flop = 2.0 * 16384 * 256 * 4096
+    out["router_fp32_bf16x3"] = {"us": ms * 1e3, "tflops_fp32_logical": flop / ms / 1e9,
+                                 "tflops_mfma": 3 * flop / ms / 1e9,
+                                 "gbs_algorithmic": 4.0 * (16384 * 4096 + 256 * 4096 + 16384 * 256) / ms / 1e6,
+                                 "kernels_ms": t}
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
+              "(the grouped GEMM runs on a single MI355X with no collectives)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(2)
+    import dense_ragged_grouped_amd as drgg
+    import synth
+
+    t0 = time.time()
+    prob = synth.config3()
+    log(f"inputs generated in {time.time() - t0:.1f} s")
+    progs = gate_up_step(torch, drgg, prob)
+    only = [p for p in args.only.split(",") if p] or ["fwd", "dgrad", "wgrad"]
+    step_fns = [progs[p] for p in only]
+
+    def step():
+        for f in step_fns:
+            f()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t) * 1e3 / args.steps
+    flop_prog = 2.0 * prob.M * prob.N * prob.K
+    value = len(step_fns) * flop_prog / ms_per_step / 1e9
+    log(f"step: {ms_per_step:.3f} ms, {value:.1f} TFLOP/s ({100 * value / PEAK_BF16_TFLOPS:.1f} % of peak)")
+
+    kernels = {}
+    programs = {}
+    for name in only:
+        times = time_call(torch, drgg, progs[name], args.reps)
+        kernels.update(times)
+        ms = sum(times.values())
+        programs[name] = {"us": ms * 1e3, "tflops": flop_prog / ms / 1e9,
+                          "pct_peak": 100 * flop_prog / ms / 1e9 / PEAK_BF16_TFLOPS, "kernels_ms": times}
+        log(f"{name}: {ms * 1e3:.1f} us, {flop_prog / ms / 1e9:.1f} TFLOP/s {times}")
+    # the dominant kernel: the one with the longest mean duration; every
+    # program's algorithmic FLOP (2*M*N*K) is carried by its main kernel
+    main_kernels = {k: v for k, v in kernels.items() if k != "gg_wgrad_fold_kernel"}
+    dom = max(main_kernels, key=main_kernels.get)
+    dom_ms = main_kernels[dom]
+    achieved = flop_prog / dom_ms / 1e9
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                "avg_launch_us": dom_ms * 1e3,
+                "flop_per_launch": flop_prog}
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(prob)
+        log(f"cpu baseline: {cpu['value'] * 1e3:.3f} GFLOP/s on {cpu['cores']} threads")
+
+    extra = other_workloads(torch, drgg, synth, args.reps) if args.all else None
+
+    line = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "moe_gate_up_e8_t131072_k2048_n1536", "experts": prob.E, "tokens": prob.M,
+                   "N": prob.N, "K": prob.K, "routing": "balanced", "programs": "+".join(only),
+                   "variant": "deterministic", "out_dtype": "bf16"},
+        "pct_of_peak": 100 * value / PEAK_BF16_TFLOPS,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "programs": programs,
+    }
+    if extra is not None:
+        line["other_workloads"] = extra
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

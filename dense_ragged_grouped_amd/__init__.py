@@ -1,0 +1,331 @@
+"""Python binding of libdrgg.so, the MI355X (gfx950) ragged BF16 grouped GEMM.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI (include/drgg.h).  PyTorch supplies device memory
+and the current stream.  If the library is missing the import fails loudly:
+there is no fallback of any kind.
+
+Programs (flashinfer PR #8258, opening summary paragraph), shapes row-major:
+
+    grouped_gemm_fwd(X [M,K], W [E,N,K], offsets [E+1])   -> Y  [M,N]    = X W_e^T
+    grouped_gemm_dgrad(G [M,N], W [E,N,K], offsets)       -> dX [M,K]    = G W_e
+    grouped_gemm_wgrad(X [M,K], G [M,N], offsets)         -> dW [E,N,K]  = G_e^T X_e
+    router_gemm_fp32_bf16x3(X [M,K] fp32, Wr [N,K] fp32)  -> out [M,N] fp32
+
+``offsets`` is an int32 CUDA tensor: offsets[0] = 0, non-decreasing,
+offsets[E] = M; expert e owns tokens offsets[e] .. offsets[e+1]-1.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdrgg.so")
+
+BF16, FP32 = 0, 1
+OP_FWD, OP_DGRAD, OP_WGRAD = 0, 1, 2
+KNOB_TILE, KNOB_GRID, KNOB_REVERSE, KNOB_TIMING = 1, 2, 3, 4
+TILE_AUTO, TILE_256x256, TILE_128x128, TILE_256x128, TILE_128x256, TILE_64x256 = range(6)
+
+# the symbols include/drgg.h declares
+EXPORTS = (
+    "grouped_gemm_fwd", "grouped_gemm_dgrad", "grouped_gemm_wgrad", "router_gemm_fp32_bf16x3",
+    "grouped_gemm_workspace_size", "drgg_workspace_init", "drgg_plan", "drgg_wgrad_chunking",
+    "drgg_set_knob", "drgg_timing_count", "drgg_timing_read", "drgg_status_string", "drgg_abi_version",
+)
+
+
+class DrggError(RuntimeError):
+    """A non-zero status from the C ABI; the message is drgg_status_string."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32), ("tile_k", ctypes.c_int32),
+        ("mfma_m", ctypes.c_int32), ("mfma_n", ctypes.c_int32), ("mfma_k", ctypes.c_int32),
+        ("grid", ctypes.c_int64), ("chunk_max", ctypes.c_int64), ("unit", ctypes.c_int64),
+        ("max_partials", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m dense_ragged_grouped_amd.build` "
+            "(the grouped GEMM has no fallback path)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz, c_int = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+    gemm = [vp, vp, vp, i32, i64, i64, i64, c_int, c_int, vp, vp, sz, vp]
+    for name in ("grouped_gemm_fwd", "grouped_gemm_dgrad", "grouped_gemm_wgrad"):
+        getattr(lib, name).argtypes = gemm
+        getattr(lib, name).restype = c_int
+    lib.router_gemm_fp32_bf16x3.argtypes = [vp, vp, i64, i64, i64, vp, vp]
+    lib.router_gemm_fp32_bf16x3.restype = c_int
+    lib.grouped_gemm_workspace_size.argtypes = [c_int, i32, i64, i64, i64, c_int, c_int, c_int,
+                                                ctypes.POINTER(sz)]
+    lib.grouped_gemm_workspace_size.restype = c_int
+    lib.drgg_workspace_init.argtypes = [vp, sz, vp]
+    lib.drgg_workspace_init.restype = c_int
+    lib.drgg_plan.argtypes = [c_int, i32, i64, i64, i64, c_int, c_int, c_int, ctypes.POINTER(PlanInfo)]
+    lib.drgg_plan.restype = c_int
+    lib.drgg_wgrad_chunking.argtypes = [i64, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    lib.drgg_wgrad_chunking.restype = c_int
+    lib.drgg_set_knob.argtypes = [c_int, i64]
+    lib.drgg_set_knob.restype = c_int
+    lib.drgg_timing_count.argtypes = []
+    lib.drgg_timing_count.restype = c_int
+    lib.drgg_timing_read.argtypes = [c_int, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float)]
+    lib.drgg_timing_read.restype = c_int
+    lib.drgg_status_string.argtypes = [c_int]
+    lib.drgg_status_string.restype = ctypes.c_char_p
+    lib.drgg_abi_version.argtypes = []
+    lib.drgg_abi_version.restype = c_int
+    return lib
+
+
+lib = _load()
+
+
+def status_string(status: int) -> str:
+    return lib.drgg_status_string(status).decode()
+
+
+def abi_version() -> int:
+    return lib.drgg_abi_version()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise DrggError(status, where)
+
+
+# ---- host-only queries ------------------------------------------------------
+
+def plan(op: int, E: int, M: int, N: int, K: int, out_dtype: int = BF16, deterministic: bool = True,
+         cu_count: int = 256) -> dict:
+    """The plan a call would use (no GPU needed when cu_count > 0)."""
+    info = PlanInfo()
+    _check(lib.drgg_plan(op, E, M, N, K, out_dtype, int(bool(deterministic)), cu_count, ctypes.byref(info)),
+           "drgg_plan")
+    return info.as_dict()
+
+
+def wgrad_chunking(T: int, chunk_max: int):
+    """(chunk length, chunk count) of an expert with T tokens."""
+    ln, n = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib.drgg_wgrad_chunking(T, chunk_max, ctypes.byref(ln), ctypes.byref(n)), "drgg_wgrad_chunking")
+    return ln.value, n.value
+
+
+def set_knob(knob: int, value: int):
+    """Test knobs (tile shape, stream-K grid, reverse walk); 0 restores the default."""
+    _check(lib.drgg_set_knob(knob, int(value)), "drgg_set_knob")
+
+
+def last_call_kernel_times():
+    """With KNOB_TIMING on: [(kernel name, milliseconds)] of the most recent
+    call's kernel launches, timed by HIP events on the launch stream."""
+    out = []
+    for i in range(lib.drgg_timing_count()):
+        name, ms = ctypes.c_char_p(), ctypes.c_float()
+        _check(lib.drgg_timing_read(i, ctypes.byref(name), ctypes.byref(ms)), "drgg_timing_read")
+        out.append((name.value.decode(), ms.value))
+    return out
+
+
+def workspace_size(op: int, E: int, M: int, N: int, K: int, out_dtype: int = BF16,
+                   deterministic: bool = True, cu_count: int = 0) -> int:
+    n = ctypes.c_size_t()
+    _check(lib.grouped_gemm_workspace_size(op, E, M, N, K, out_dtype, int(bool(deterministic)), cu_count,
+                                           ctypes.byref(n)), "grouped_gemm_workspace_size")
+    return n.value
+
+
+# ---- torch marshalling ---------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(dt) -> int:
+    torch = _torch()
+    if dt in (torch.bfloat16, BF16, "bf16"):
+        return BF16
+    if dt in (torch.float32, FP32, "fp32"):
+        return FP32
+    raise ValueError(f"unsupported output dtype {dt!r}")
+
+
+def _torch_dtype(code: int):
+    torch = _torch()
+    return torch.bfloat16 if code == BF16 else torch.float32
+
+
+def _need(t, dtype, name, ndim):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a CUDA tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {ndim}-d tensor")
+
+
+def _stream(device, stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+class Workspace:
+    """Device workspace for the weight gradient, grown on demand.
+
+    Allocated zeroed; the non-deterministic program leaves its tile sums and
+    tickets zero after every call, so the buffer stays valid for later calls.
+    One Workspace must not serve two calls in flight on different streams.
+    """
+
+    def __init__(self, device=None):
+        torch = _torch()
+        self.device = torch.device(device if device is not None else "cuda")
+        self.buf = None
+
+    def get(self, nbytes: int):
+        torch = _torch()
+        if nbytes == 0:
+            return None
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.zeros(nbytes + 256, dtype=torch.uint8, device=self.device)
+        return self.buf
+
+
+# Default workspaces, one per (device, variant): a deterministic call leaves
+# its FP32 partials in the buffer, while the non-deterministic program needs
+# its tile sums and tickets to be zero, so the two never share a buffer.
+_default_ws = {}
+
+
+def _workspace(device, nbytes, workspace, deterministic):
+    if workspace is not None:
+        buf = workspace.get(nbytes) if isinstance(workspace, Workspace) else workspace
+    else:
+        key = (str(device), bool(deterministic))
+        if key not in _default_ws:
+            _default_ws[key] = Workspace(device)
+        buf = _default_ws[key].get(nbytes)
+    if buf is None:
+        return None, 0
+    return ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size()
+
+
+def _offsets(offsets, E_hint=None):
+    torch = _torch()
+    _need(offsets, torch.int32, "group_offsets", 1)
+    return offsets.numel() - 1
+
+
+def grouped_gemm_fwd(X, W, group_offsets, out_dtype=None, deterministic=True, out=None, stream=None):
+    """Y[t] = X[t] W[e(t)]^T with FP32 accumulation; out_dtype bf16 (default) or fp32."""
+    torch = _torch()
+    _need(X, torch.bfloat16, "X", 2)
+    _need(W, torch.bfloat16, "W", 3)
+    E = _offsets(group_offsets)
+    M, K = X.shape
+    En, N, Kw = W.shape
+    if En != E or Kw != K:
+        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, W {tuple(W.shape)}, E={E}")
+    code = _dtype_code(out_dtype if out_dtype is not None else torch.bfloat16)
+    if out is None:
+        out = torch.empty((M, N), dtype=_torch_dtype(code), device=X.device)
+    else:
+        _need(out, _torch_dtype(code), "out", 2)
+        if tuple(out.shape) != (M, N):
+            raise ValueError("out has the wrong shape")
+    st = lib.grouped_gemm_fwd(X.data_ptr(), W.data_ptr(), group_offsets.data_ptr(), E, M, N, K, code,
+                              int(bool(deterministic)), out.data_ptr(), None, 0, _stream(X.device, stream))
+    _check(st, "grouped_gemm_fwd")
+    return out
+
+
+def grouped_gemm_dgrad(G, W, group_offsets, out_dtype=None, deterministic=True, out=None, stream=None):
+    """dX[t] = G[t] W[e(t)] with FP32 accumulation."""
+    torch = _torch()
+    _need(G, torch.bfloat16, "G", 2)
+    _need(W, torch.bfloat16, "W", 3)
+    E = _offsets(group_offsets)
+    M, N = G.shape
+    En, Nw, K = W.shape
+    if En != E or Nw != N:
+        raise ValueError(f"shape mismatch: G {tuple(G.shape)}, W {tuple(W.shape)}, E={E}")
+    code = _dtype_code(out_dtype if out_dtype is not None else torch.bfloat16)
+    if out is None:
+        out = torch.empty((M, K), dtype=_torch_dtype(code), device=G.device)
+    else:
+        _need(out, _torch_dtype(code), "out", 2)
+        if tuple(out.shape) != (M, K):
+            raise ValueError("out has the wrong shape")
+    st = lib.grouped_gemm_dgrad(G.data_ptr(), W.data_ptr(), group_offsets.data_ptr(), E, M, N, K, code,
+                                int(bool(deterministic)), out.data_ptr(), None, 0, _stream(G.device, stream))
+    _check(st, "grouped_gemm_dgrad")
+    return out
+
+
+def grouped_gemm_wgrad(X, G, group_offsets, out_dtype=None, deterministic=True, out=None, workspace=None,
+                       stream=None):
+    """dW[e] = G_e^T X_e over each expert's tokens (+0 for experts without tokens)."""
+    torch = _torch()
+    _need(X, torch.bfloat16, "X", 2)
+    _need(G, torch.bfloat16, "G", 2)
+    E = _offsets(group_offsets)
+    M, K = X.shape
+    Mg, N = G.shape
+    if Mg != M:
+        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, G {tuple(G.shape)}")
+    code = _dtype_code(out_dtype if out_dtype is not None else torch.bfloat16)
+    if out is None:
+        out = torch.empty((E, N, K), dtype=_torch_dtype(code), device=X.device)
+    else:
+        _need(out, _torch_dtype(code), "out", 3)
+        if tuple(out.shape) != (E, N, K):
+            raise ValueError("out has the wrong shape")
+    nbytes = workspace_size(OP_WGRAD, E, M, N, K, code, deterministic)
+    ws_ptr, ws_bytes = _workspace(X.device, nbytes, workspace, deterministic)
+    st = lib.grouped_gemm_wgrad(X.data_ptr(), G.data_ptr(), group_offsets.data_ptr(), E, M, N, K, code,
+                                int(bool(deterministic)), out.data_ptr(), ws_ptr, ws_bytes,
+                                _stream(X.device, stream))
+    _check(st, "grouped_gemm_wgrad")
+    return out
+
+
+def router_gemm_fp32_bf16x3(X, Wr, out=None, stream=None):
+    """FP32 router GEMM out = X Wr^T on BF16 MFMA via the BF16x3 split."""
+    torch = _torch()
+    _need(X, torch.float32, "X", 2)
+    _need(Wr, torch.float32, "Wr", 2)
+    M, K = X.shape
+    N, Kw = Wr.shape
+    if Kw != K:
+        raise ValueError("shape mismatch")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    else:
+        _need(out, torch.float32, "out", 2)
+    st = lib.router_gemm_fp32_bf16x3(X.data_ptr(), Wr.data_ptr(), M, N, K, out.data_ptr(),
+                                     _stream(X.device, stream))
+    _check(st, "router_gemm_fp32_bf16x3")
+    return out
+
+
+def workspace_init(buf, stream=None):
+    """Zero a workspace tensor with the library's fill kernel."""
+    _check(lib.drgg_workspace_init(buf.data_ptr(), buf.numel() * buf.element_size(),
+                                   _stream(buf.device, stream)), "drgg_workspace_init")

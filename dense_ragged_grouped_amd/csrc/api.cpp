@@ -1,0 +1,363 @@
+// api.cpp -- the C ABI of libdrgg.so (declared in include/drgg.h).
+//
+// Host-side argument checks in checked 64-bit arithmetic, planning (plan.hpp)
+// and kernel launches (kernels.hip) on the caller's stream.  Nothing here
+// allocates device memory or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/drgg.h"
+#include "internal.hpp"
+#include "plan.hpp"
+
+namespace drgg {
+
+namespace {
+
+std::atomic<int64_t> g_knob_tile{0}, g_knob_grid{0}, g_knob_reverse{0};
+
+constexpr int64_t kMaxBytes = (int64_t)1 << 62;
+constexpr int kMaxDevices = 64;
+
+// checked a * b for non-negative operands
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+    if (a < 0 || b < 0) return false;
+    if (a != 0 && b > kMaxBytes / a) return false;
+    *out = a * b;
+    return true;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// CU count of the current device, cached per device.
+drgg_status current_cu_count(int* cus) {
+    static std::mutex mu;
+    static int cache[kMaxDevices] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return DRGG_EDEVICE;
+    if (dev < 0 || dev >= kMaxDevices) return DRGG_EDEVICE;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            return DRGG_EDEVICE;
+        cache[dev] = n;
+    }
+    *cus = cache[dev];
+    return DRGG_OK;
+}
+
+// Shape checks shared by the three programs.
+drgg_status check_problem(int32_t E, int64_t M, int64_t N, int64_t K, drgg_dtype dt) {
+    if (E < 1 || E > kMaxExperts) return DRGG_EINVAL;
+    if (dt != DRGG_BF16 && dt != DRGG_FP32) return DRGG_EINVAL;
+    if (M < 0 || N < 8 || K < 8) return DRGG_ESHAPE;
+    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return DRGG_ESHAPE;
+    if (N % 8 != 0 || K % 8 != 0) return DRGG_EALIGN;
+    int64_t t;
+    // every buffer: X [M,K], G [M,N], W/dW [E,N,K] (x4 bytes for FP32)
+    if (!mul_ok(M, K, &t) || !mul_ok(t, 4, &t)) return DRGG_EOVERFLOW;
+    if (!mul_ok(M, N, &t) || !mul_ok(t, 4, &t)) return DRGG_EOVERFLOW;
+    if (!mul_ok(N, K, &t) || !mul_ok(t, E, &t) || !mul_ok(t, 4, &t)) return DRGG_EOVERFLOW;
+    return DRGG_OK;
+}
+
+struct Plan {
+    int tile;
+    TileShape ts;
+    int64_t grid;
+    int64_t chunk_max;
+    int64_t max_partials;
+    size_t ws_bytes;
+};
+
+// ws layout, non-det weight gradient: [tile sums: E*P*BM*BN fp32][tickets: E*P u32]
+drgg_status make_plan(drgg_op op, int32_t E, int64_t M, int64_t N, int64_t K, int det, int cu_count,
+                      Plan* p) {
+    std::memset(p, 0, sizeof *p);
+    int tile = (int)g_knob_tile.load();
+    if (tile < kTileAuto || tile > kTile64x256) tile = kTileAuto;
+    if (tile == kTile64x256 && op != DRGG_OP_WGRAD) tile = kTileAuto;
+    if (tile == kTileAuto) tile = default_tile((int)op, N, K);
+    p->tile = tile;
+    p->ts = tile_shape(tile);
+    const int64_t bm = p->ts.bm, bn = p->ts.bn;
+    if (op == DRGG_OP_FWD || op == DRGG_OP_DGRAD) {
+        const int64_t ncols = op == DRGG_OP_FWD ? N : K;
+        p->grid = (M / bm + E) * ceil_div(ncols, bn);
+        return DRGG_OK;
+    }
+    const int64_t P = ceil_div(N, bm) * ceil_div(K, bn);
+    if (det) {
+        p->chunk_max = wgrad_chunk_max(E, M, N, K);
+        p->max_partials = wgrad_max_partials(M, p->chunk_max);
+        // chunks_e <= ceil(T_e / chunk_max) <= T_e / chunk_max + 1
+        p->grid = P * (M / p->chunk_max + E);
+        int64_t b;
+        if (!mul_ok(p->max_partials, N * K, &b) || !mul_ok(b, 4, &b)) return DRGG_EOVERFLOW;
+        p->ws_bytes = (size_t)b;
+    } else {
+        int64_t g = g_knob_grid.load();
+        p->grid = g > 0 ? g : cu_count;
+        int64_t sums, tk;
+        if (!mul_ok(P * E, bm * bn, &sums) || !mul_ok(sums, 4, &sums)) return DRGG_EOVERFLOW;
+        tk = P * E * 4;
+        p->ws_bytes = (size_t)(round_up(sums, 256) + round_up(tk, 256));
+    }
+    if (p->grid > INT32_MAX) return DRGG_ESHAPE;
+    return DRGG_OK;
+}
+
+drgg_status launch_status(hipError_t e) { return e == hipSuccess ? DRGG_OK : DRGG_EDEVICE; }
+
+// ---- timing marks (DRGG_KNOB_TIMING) ----------------------------------------
+constexpr int kMaxMarks = 8;
+std::atomic<int> g_timing_on{0};
+struct TimingMarks {
+    std::mutex mu;
+    hipEvent_t ev[kMaxMarks + 1] = {};
+    const char* name[kMaxMarks] = {};
+    int n = 0;          // kernels marked in the current call
+    bool ended = false;
+    int dev = -1;
+} g_marks;
+
+}  // namespace
+
+void timing_mark(const char* kernel, hipStream_t s) {
+    if (!g_timing_on.load(std::memory_order_relaxed)) return;
+    std::lock_guard<std::mutex> lock(g_marks.mu);
+    if (g_marks.ended) { g_marks.n = 0; g_marks.ended = false; }
+    if (g_marks.n >= kMaxMarks) return;
+    hipEvent_t& e = g_marks.ev[g_marks.n];
+    if (!e && hipEventCreate(&e) != hipSuccess) return;
+    if (hipEventRecord(e, s) != hipSuccess) return;
+    g_marks.name[g_marks.n++] = kernel;
+}
+
+void timing_end(hipStream_t s) {
+    if (!g_timing_on.load(std::memory_order_relaxed)) return;
+    std::lock_guard<std::mutex> lock(g_marks.mu);
+    hipEvent_t& e = g_marks.ev[g_marks.n];
+    if (!e && hipEventCreate(&e) != hipSuccess) return;
+    if (hipEventRecord(e, s) == hipSuccess) g_marks.ended = true;
+}
+
+namespace {
+
+drgg_status run_fwd_dgrad(drgg_op op, const void* A, const void* W, const int32_t* offs, int32_t E,
+                          int64_t M, int64_t N, int64_t K, drgg_dtype dt, void* out, hipStream_t s) {
+    drgg_status st = check_problem(E, M, N, K, dt);
+    if (st != DRGG_OK) return st;
+    // with no tokens the token-indexed buffers may be empty (null)
+    if (!W || !offs || (M > 0 && (!A || !out))) return DRGG_EINVAL;
+    if (!aligned16(A) || !aligned16(W) || !aligned16(out) || (reinterpret_cast<uintptr_t>(offs) & 3u))
+        return DRGG_EALIGN;
+    Plan p;
+    st = make_plan(op, E, M, N, K, 1, 0, &p);
+    if (st != DRGG_OK) return st;
+    if (M == 0) return DRGG_OK;   // no rows to write
+    GemmArgs a{};
+    a.A = static_cast<const uint16_t*>(A);
+    a.B = static_cast<const uint16_t*>(W);
+    a.offs = offs;
+    a.out = out;
+    a.M = M; a.N = N; a.K = K; a.E = E;
+    a.items_max = p.grid;
+    a.reverse = (int32_t)(g_knob_reverse.load() != 0);
+    return launch_status(launch_fwd_dgrad((int)op, p.tile, a, dt == DRGG_BF16, s));
+}
+
+}  // namespace
+}  // namespace drgg
+
+using namespace drgg;
+
+extern "C" {
+
+drgg_status grouped_gemm_fwd(const void* X, const void* W, const int32_t* group_offsets, int32_t E,
+                             int64_t M, int64_t N, int64_t K, drgg_dtype out_dtype, int deterministic,
+                             void* Y, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    (void)deterministic; (void)workspace; (void)workspace_bytes;   // one program for both variants
+    return run_fwd_dgrad(DRGG_OP_FWD, X, W, group_offsets, E, M, N, K, out_dtype, Y, stream);
+}
+
+drgg_status grouped_gemm_dgrad(const void* G, const void* W, const int32_t* group_offsets, int32_t E,
+                               int64_t M, int64_t N, int64_t K, drgg_dtype out_dtype, int deterministic,
+                               void* dX, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    (void)deterministic; (void)workspace; (void)workspace_bytes;
+    return run_fwd_dgrad(DRGG_OP_DGRAD, G, W, group_offsets, E, M, N, K, out_dtype, dX, stream);
+}
+
+drgg_status grouped_gemm_wgrad(const void* X, const void* G, const int32_t* group_offsets, int32_t E,
+                               int64_t M, int64_t N, int64_t K, drgg_dtype out_dtype, int deterministic,
+                               void* dW, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    drgg_status st = check_problem(E, M, N, K, out_dtype);
+    if (st != DRGG_OK) return st;
+    if (!group_offsets || !dW || (M > 0 && (!X || !G))) return DRGG_EINVAL;
+    if (!aligned16(X) || !aligned16(G) || !aligned16(dW) ||
+        (reinterpret_cast<uintptr_t>(group_offsets) & 3u))
+        return DRGG_EALIGN;
+    int cus = 0;
+    if (!deterministic) {
+        st = current_cu_count(&cus);
+        if (st != DRGG_OK) return st;
+    }
+    Plan p;
+    st = make_plan(DRGG_OP_WGRAD, E, M, N, K, deterministic, cus, &p);
+    if (st != DRGG_OK) return st;
+    if (p.ws_bytes > 0) {
+        if (!workspace || workspace_bytes < p.ws_bytes) return DRGG_EWORKSPACE;
+        if (!aligned16(workspace)) return DRGG_EALIGN;
+    }
+    GemmArgs a{};
+    a.A = static_cast<const uint16_t*>(G);   // A rows: output rows n of dW (from G)
+    a.B = static_cast<const uint16_t*>(X);   // B rows: output cols k of dW (from X)
+    a.offs = group_offsets;
+    a.out = dW;
+    a.M = M; a.N = N; a.K = K; a.E = E;
+    a.reverse = (int32_t)(g_knob_reverse.load() != 0);
+    const bool bf16 = out_dtype == DRGG_BF16;
+    if (deterministic) {
+        a.partial = static_cast<float*>(workspace);
+        a.chunk_max = p.chunk_max;
+        a.items_max = M > 0 ? p.grid : 0;
+        return launch_status(launch_wgrad_det(p.tile, a, bf16, stream));
+    }
+    const int64_t P = ceil_div(N, p.ts.bm) * ceil_div(K, p.ts.bn);
+    const int64_t sums = round_up(P * E * p.ts.bm * p.ts.bn * 4, 256);
+    a.tilesum = static_cast<float*>(workspace);
+    a.tickets = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + sums);
+    return launch_status(launch_wgrad_streamk(p.tile, a, p.grid, bf16, stream));
+}
+
+drgg_status router_gemm_fp32_bf16x3(const float* X, const float* Wr, int64_t M, int64_t N, int64_t K,
+                                    float* out, hipStream_t stream) {
+    if (!X || !Wr || !out) return DRGG_EINVAL;
+    if (M < 0 || N < 1 || K < 8 || M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return DRGG_ESHAPE;
+    if (K % 8 != 0) return DRGG_EALIGN;
+    if (!aligned16(X) || !aligned16(Wr) || !aligned16(out)) return DRGG_EALIGN;
+    int64_t t;
+    if (!mul_ok(M, K, &t) || !mul_ok(t, 4, &t) || !mul_ok(M, N, &t) || !mul_ok(t, 4, &t) ||
+        !mul_ok(N, K, &t) || !mul_ok(t, 4, &t))
+        return DRGG_EOVERFLOW;
+    if (M == 0) return DRGG_OK;
+    return launch_status(launch_router(X, Wr, out, M, N, K, stream));
+}
+
+drgg_status grouped_gemm_workspace_size(drgg_op op, int32_t E, int64_t M, int64_t N, int64_t K,
+                                        drgg_dtype out_dtype, int deterministic, int cu_count,
+                                        size_t* bytes) {
+    if (!bytes) return DRGG_EINVAL;
+    if (op != DRGG_OP_FWD && op != DRGG_OP_DGRAD && op != DRGG_OP_WGRAD) return DRGG_EINVAL;
+    drgg_status st = check_problem(E, M, N, K, out_dtype);
+    if (st != DRGG_OK) return st;
+    if (op == DRGG_OP_WGRAD && !deterministic && cu_count <= 0) {
+        st = current_cu_count(&cu_count);
+        if (st != DRGG_OK) return st;
+    }
+    Plan p;
+    st = make_plan(op, E, M, N, K, deterministic, cu_count, &p);
+    if (st != DRGG_OK) return st;
+    *bytes = p.ws_bytes;
+    return DRGG_OK;
+}
+
+drgg_status drgg_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (workspace_bytes == 0) return DRGG_OK;
+    if (!workspace) return DRGG_EINVAL;
+    return launch_status(launch_zero(workspace, workspace_bytes, stream));
+}
+
+drgg_status drgg_plan(drgg_op op, int32_t E, int64_t M, int64_t N, int64_t K, drgg_dtype out_dtype,
+                      int deterministic, int cu_count, drgg_plan_info* out) {
+    if (!out) return DRGG_EINVAL;
+    if (op != DRGG_OP_FWD && op != DRGG_OP_DGRAD && op != DRGG_OP_WGRAD) return DRGG_EINVAL;
+    drgg_status st = check_problem(E, M, N, K, out_dtype);
+    if (st != DRGG_OK) return st;
+    if (op == DRGG_OP_WGRAD && !deterministic && cu_count <= 0) {
+        st = current_cu_count(&cu_count);
+        if (st != DRGG_OK) return st;
+    }
+    Plan p;
+    st = make_plan(op, E, M, N, K, deterministic, cu_count, &p);
+    if (st != DRGG_OK) return st;
+    std::memset(out, 0, sizeof *out);
+    out->tile_m = p.ts.bm;
+    out->tile_n = p.ts.bn;
+    out->tile_k = kTileK;
+    out->mfma_m = kMfmaM;
+    out->mfma_n = kMfmaN;
+    out->mfma_k = kMfmaK;
+    out->grid = p.grid;
+    out->chunk_max = p.chunk_max;
+    out->unit = (op == DRGG_OP_WGRAD && !deterministic) ? kStreamKUnit : 0;
+    out->max_partials = p.max_partials;
+    out->workspace_bytes = p.ws_bytes;
+    return DRGG_OK;
+}
+
+drgg_status drgg_wgrad_chunking(int64_t T, int64_t chunk_max, int64_t* chunk_len, int64_t* chunks) {
+    if (!chunk_len || !chunks || chunk_max < kTileK || chunk_max % kTileK != 0 || T < 0 || T > INT32_MAX)
+        return DRGG_EINVAL;
+    wgrad_chunking(T, chunk_max, chunk_len, chunks);
+    return DRGG_OK;
+}
+
+drgg_status drgg_set_knob(int knob, int64_t value) {
+    switch (knob) {
+        case DRGG_KNOB_TILE:
+            if (value < 0 || value > kTile64x256) return DRGG_EINVAL;
+            g_knob_tile.store(value);
+            return DRGG_OK;
+        case DRGG_KNOB_GRID:
+            if (value < 0 || value > INT32_MAX) return DRGG_EINVAL;
+            g_knob_grid.store(value);
+            return DRGG_OK;
+        case DRGG_KNOB_REVERSE:
+            g_knob_reverse.store(value != 0);
+            return DRGG_OK;
+        case DRGG_KNOB_TIMING:
+            g_timing_on.store(value != 0);
+            return DRGG_OK;
+        default:
+            return DRGG_EINVAL;
+    }
+}
+
+int drgg_timing_count(void) {
+    std::lock_guard<std::mutex> lock(g_marks.mu);
+    return g_marks.ended ? g_marks.n : 0;
+}
+
+drgg_status drgg_timing_read(int i, const char** kernel, float* ms) {
+    if (!kernel || !ms) return DRGG_EINVAL;
+    std::lock_guard<std::mutex> lock(g_marks.mu);
+    if (!g_marks.ended || i < 0 || i >= g_marks.n) return DRGG_EINVAL;
+    if (hipEventSynchronize(g_marks.ev[i + 1]) != hipSuccess) return DRGG_EDEVICE;
+    if (hipEventElapsedTime(ms, g_marks.ev[i], g_marks.ev[i + 1]) != hipSuccess) return DRGG_EDEVICE;
+    *kernel = g_marks.name[i];
+    return DRGG_OK;
+}
+
+const char* drgg_status_string(drgg_status s) {
+    switch (s) {
+        case DRGG_OK: return "ok";
+        case DRGG_EINVAL: return "invalid argument (null pointer, bad enum value or E outside 1..1024)";
+        case DRGG_ESHAPE: return "invalid shape (negative or too large dimension)";
+        case DRGG_EALIGN: return "misaligned (pointers must be 16-byte aligned, N and K multiples of 8)";
+        case DRGG_EOVERFLOW: return "size overflow in 64-bit arithmetic";
+        case DRGG_EWORKSPACE: return "workspace missing or too small";
+        case DRGG_EUNSUPPORTED: return "unsupported on this device or combination";
+        case DRGG_EDEVICE: return "HIP error while querying the device or launching";
+    }
+    return "unknown status";
+}
+
+int drgg_abi_version(void) { return DRGG_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,41 @@
+// internal.hpp -- declarations shared by the C ABI (api.cpp) and the kernel
+// launchers (kernels.hip).  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace drgg {
+
+// Arguments of the grouped-GEMM kernels, passed by value.
+struct GemmArgs {
+    const uint16_t* A;     // fwd: X   dgrad: G   wgrad: G  (BF16 bits)
+    const uint16_t* B;     // fwd: W   dgrad: W   wgrad: X
+    const int32_t* offs;   // group offsets [E+1], device
+    void* out;             // Y / dX / dW
+    float* partial;        // det wgrad: chunk partial slots [slot][N][K]
+    float* tilesum;        // non-det wgrad: FP32 tile sums [E*P][BM*BN]
+    uint32_t* tickets;     // non-det wgrad: [E*P]
+    int64_t M, N, K;
+    int64_t chunk_max;     // det wgrad: longest chunk
+    int64_t items_max;     // workgroups launched (fwd/dgrad/det wgrad)
+    int32_t E;
+    int32_t reverse;       // walk work items in reverse (test knob)
+};
+
+hipError_t launch_fwd_dgrad(int op, int tile, const GemmArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_wgrad_det(int tile, const GemmArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_wgrad_streamk(int tile, const GemmArgs& a, int64_t grid_n, bool bf16, hipStream_t s);
+hipError_t launch_router(const float* X, const float* Wr, float* out, int64_t M, int64_t N, int64_t K,
+                         hipStream_t s);
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
+
+// Per-launch timing marks (a measurement knob, off by default): when on, an
+// event is recorded on the stream before every kernel launch of a call and
+// once after the last one, so each kernel's duration can be read back.
+void timing_mark(const char* kernel, hipStream_t s);   // before a launch
+void timing_end(hipStream_t s);                         // after the last launch
+
+}  // namespace drgg

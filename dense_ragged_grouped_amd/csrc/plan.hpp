@@ -1,0 +1,101 @@
+// plan.hpp -- host-side planning for the ragged grouped GEMM on gfx950.
+//
+// Pure functions of the problem (and, for the non-deterministic weight
+// gradient only, of the CU count).  Shared by the C ABI (api.cpp) and the
+// kernel launchers (kernels.hip); nothing here touches the GPU.
+#pragma once
+
+#include <cstdint>
+
+namespace drgg {
+
+// Reduction step of every main loop and the MFMA shape every program uses:
+// v_mfma_f32_32x32x16_bf16 (32x32 output block, 16 reduction values per
+// instruction).  One fixed instruction and step per program keeps each output
+// element's accumulation order independent of the tile shape.
+constexpr int kTileK = 64;
+constexpr int kMfmaM = 32, kMfmaN = 32, kMfmaK = 16;
+
+// Token unit of the non-deterministic (stream-K) weight gradient: the K range
+// of a split tile is handed out in 512-token units (flashinfer PR #8258,
+// summary: the "unordered K=512 path").
+constexpr int64_t kStreamKUnit = 512;
+
+// The reference CU count the deterministic chunk rule is written against.  It
+// is a constant of the rule, never the live device's count, so that the
+// deterministic weight gradient is the same on any number of CUs.
+constexpr int64_t kRuleCUs = 256;
+
+constexpr int kMaxExperts = 1024;
+
+enum TileId { kTileAuto = 0, kTile256x256 = 1, kTile128x128 = 2, kTile256x128 = 3,
+              kTile128x256 = 4, kTile64x256 = 5 };
+
+struct TileShape { int bm, bn; };
+
+inline TileShape tile_shape(int id) {
+    switch (id) {
+        case kTile128x128: return {128, 128};
+        case kTile256x128: return {256, 128};
+        case kTile128x256: return {128, 256};
+        case kTile64x256: return {64, 256};
+        default: return {256, 256};
+    }
+}
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+// Deterministic weight gradient, chunk rule part 1 (host): the longest chunk
+// an expert's token range is cut into.  A function of (E, M, N, K) only.
+//   P0    = output tiles per expert at a 256x256 reference tile
+//   S     = smallest chunk count per (balanced) expert whose item count fills
+//           whole waves of kRuleCUs to >= 90 %
+//   chunk_max = max(ceil(M / (E*S)), half a reference CU's share of the
+//               token-tile work, 512), rounded up to a multiple of 64.
+// Long experts are cut into more chunks; short ones are never cut.
+inline int64_t wgrad_chunk_max(int32_t E, int64_t M, int64_t N, int64_t K) {
+    if (M <= 0) return 512;
+    const int64_t p0 = ceil_div(N, 256) * ceil_div(K, 256);
+    const int64_t base = p0 * E;
+    int64_t s = 1;
+    for (; s < 64; ++s) {
+        const int64_t items = base * s;
+        const int64_t slots = kRuleCUs * ceil_div(items, kRuleCUs);
+        if (items * 10 >= slots * 9) break;
+    }
+    int64_t a = ceil_div(M, (int64_t)E * s);
+    int64_t b = ceil_div(ceil_div(M * p0, kRuleCUs), 2);
+    int64_t c = a > b ? a : b;
+    if (c < 512) c = 512;
+    return round_up(c, kTileK);
+}
+
+// Chunk rule part 2 (host mirror of the device function): an expert with T
+// tokens is cut into chunks of `len` tokens (the last one shorter), starting
+// at its first token.  S = ceil(T / chunk_max), len = ceil(T / S) rounded up
+// to a multiple of 64, chunks = ceil(T / len).
+inline void wgrad_chunking(int64_t T, int64_t chunk_max, int64_t* len, int64_t* chunks) {
+    if (T <= 0) { *len = 0; *chunks = 0; return; }
+    const int64_t s = ceil_div(T, chunk_max);
+    const int64_t l = round_up(ceil_div(T, s), kTileK);
+    *len = l;
+    *chunks = ceil_div(T, l);
+}
+
+// Partial slots the deterministic weight gradient may need: only experts cut
+// into more than one chunk write partials.  Such an expert has
+// T > chunk_max and at most T / chunk_max + 1 < 2 T / chunk_max chunks, so the
+// total is below 2 M / chunk_max.
+inline int64_t wgrad_max_partials(int64_t M, int64_t chunk_max) {
+    return M <= 0 ? 0 : (2 * M) / chunk_max + 1;
+}
+
+// Default output tile per program.
+inline int default_tile(int op, int64_t N, int64_t K) {
+    if (op == 2 && N <= 64) return kTile64x256;   // skinny weight gradient
+    (void)K;
+    return kTile256x256;
+}
+
+}  // namespace drgg

@@ -1,0 +1,218 @@
+/*
+ * drgg.h -- C ABI of the MI355X (gfx950) ragged BF16 grouped GEMM library
+ * (libdrgg.so).
+ *
+ * The operation (flashinfer PR #8258, "run the split k512 wgrad tail whole
+ * on the least-loaded clusters on sm_107a", opening summary paragraph): a
+ * grouped GEMM for mixture-of-experts training whose E experts own
+ * contiguous, ragged token ranges.  Three programs, all accumulating in FP32:
+ *
+ *   forward          Y  = X W^T     Y[t,:]  = X[t,:] W[e(t)]^T
+ *   data gradient    dX = G W       dX[t,:] = G[t,:] W[e(t)]
+ *   weight gradient  dW = G^T X     dW[e]   = sum over e's tokens of G[t,:]^T X[t,:]
+ *
+ * The dense projection GEMM (flashinfer PR #8363, "run the deterministic
+ * program at the sm_107a token counts its new plans win", Summary) is the
+ * E = 1 case with group_offsets = {0, M}.
+ *
+ * Shapes (all row-major and contiguous, BF16 unless stated):
+ *   X [M, K]     activations / layer input       (M = total tokens)
+ *   W [E, N, K]  expert weights, nn.Linear [out, in] layout per expert
+ *   G [M, N]     output gradient
+ *   Y [M, N], dX [M, K], dW [E, N, K]   outputs, BF16 or FP32
+ *   group_offsets  int32 [E + 1] on the DEVICE: o[0] = 0, non-decreasing,
+ *                  o[E] = M; expert e owns tokens o[e] .. o[e+1]-1.
+ *
+ * Variants (PR #8258 summary):
+ *   deterministic != 0  bitwise reproducible from run to run, independent of
+ *                       the CU count and of the work-to-CU mapping.  The
+ *                       weight gradient cuts an expert's token range into
+ *                       chunks by a rule that depends only on the problem
+ *                       (never on the device), writes one FP32 partial per
+ *                       chunk and folds the partials in chunk order before a
+ *                       single rounding.
+ *   deterministic == 0  the weight gradient splits the token range of tiles
+ *                       across workgroups in 512-token units (stream-K); the
+ *                       pieces of a split tile add their FP32 partials into
+ *                       an FP32 tile sum with atomic adds, a per-tile ticket
+ *                       picks the last arrival, which reads and clears the sum
+ *                       and writes the output tile.  The summation order of a
+ *                       split tile can differ from run to run.  Forward and
+ *                       data gradient have no split and are identical in both
+ *                       modes (PR #8363, Summary: the dense non-deterministic
+ *                       forward and input gradient are the deterministic
+ *                       programs).
+ *
+ * Conventions for every entry point:
+ *   * Pointers are device pointers unless a comment says "host".
+ *   * The caller owns every buffer, including outputs and the workspace; the
+ *     library allocates no device memory on any call path.
+ *   * Calls are asynchronous on `stream` (NULL = the default stream) and do
+ *     not synchronise; group_offsets is read only by the kernels.  Calls are
+ *     capturable into a HIP graph.
+ *   * Argument checks run on the host before anything is enqueued; on any
+ *     error nothing is enqueued and the status says why
+ *     (drgg_status_string).  Offsets are not checked on the host (they live
+ *     on the device); the kernels clamp every offset into [0, M] so that no
+ *     access leaves the buffers, and the result for invalid offsets is
+ *     unspecified.
+ *   * Alignment: every pointer 16-byte aligned; N and K multiples of 8.
+ *   * Limits: 1 <= E <= 1024, 0 <= M < 2^31, 8 <= N, K < 2^31, and every
+ *     buffer size below 2^62 bytes (checked in 64-bit arithmetic).
+ */
+#ifndef DRGG_H
+#define DRGG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DRGG_ABI_VERSION 1
+
+typedef enum {
+    DRGG_BF16 = 0,
+    DRGG_FP32 = 1
+} drgg_dtype;
+
+typedef enum {
+    DRGG_OP_FWD = 0,
+    DRGG_OP_DGRAD = 1,
+    DRGG_OP_WGRAD = 2
+} drgg_op;
+
+typedef enum {
+    DRGG_OK = 0,
+    DRGG_EINVAL = 1,        /* null pointer, bad enum value, E out of range   */
+    DRGG_ESHAPE = 2,        /* negative or too large dimension                */
+    DRGG_EALIGN = 3,        /* pointer not 16-byte aligned, N or K not % 8    */
+    DRGG_EOVERFLOW = 4,     /* a size product overflows 64-bit arithmetic     */
+    DRGG_EWORKSPACE = 5,    /* workspace missing or smaller than required     */
+    DRGG_EUNSUPPORTED = 6,  /* no program for this device or combination      */
+    DRGG_EDEVICE = 7        /* HIP error while querying the device or launching */
+} drgg_status;
+
+/*
+ * Forward: Y[t,n] = sum_k X[t,k] * W[e(t),n,k], FP32 accumulation, one
+ * rounding to out_dtype.  X [M,K] BF16, W [E,N,K] BF16, Y [M,N] out_dtype.
+ * Rows of Y are written only for tokens 0..M-1 (all of them, since the
+ * experts' ranges cover [0, M)).  No workspace is needed (workspace may be
+ * NULL with workspace_bytes = 0).
+ */
+drgg_status grouped_gemm_fwd(const void *X, const void *W, const int32_t *group_offsets,
+                             int32_t E, int64_t M, int64_t N, int64_t K,
+                             drgg_dtype out_dtype, int deterministic, void *Y,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Data gradient: dX[t,k] = sum_n G[t,n] * W[e(t),n,k].  G [M,N] BF16,
+ * W [E,N,K] BF16, dX [M,K] out_dtype.  No workspace is needed.
+ */
+drgg_status grouped_gemm_dgrad(const void *G, const void *W, const int32_t *group_offsets,
+                               int32_t E, int64_t M, int64_t N, int64_t K,
+                               drgg_dtype out_dtype, int deterministic, void *dX,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Weight gradient: dW[e,n,k] = sum_{t = o[e]}^{o[e+1]-1} G[t,n] * X[t,k];
+ * experts without tokens get dW[e] = +0.  X [M,K] BF16, G [M,N] BF16,
+ * dW [E,N,K] out_dtype.
+ * Workspace: at least grouped_gemm_workspace_size(DRGG_OP_WGRAD, ...) bytes.
+ *   deterministic != 0: FP32 chunk partials; no initialisation needed.
+ *   deterministic == 0: FP32 tile sums and tickets that must be zero before
+ *     the first call (drgg_workspace_init); every call leaves them zero
+ *     again.  A buffer that served a deterministic call holds partials
+ *     afterwards and must be zeroed again before a non-deterministic call.
+ *   Two calls in flight at once must not share a workspace.
+ */
+drgg_status grouped_gemm_wgrad(const void *X, const void *G, const int32_t *group_offsets,
+                               int32_t E, int64_t M, int64_t N, int64_t K,
+                               drgg_dtype out_dtype, int deterministic, void *dW,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * FP32 router GEMM out[m,n] = sum_k X[m,k] * Wr[n,k] computed on BF16 MFMA
+ * as a BF16x3 split (PR #8363, Summary: "FP32 router GEMM (256 experts,
+ * BF16x3 emulation)"): each FP32 operand value v is split into
+ * hi = bf16(v), lo = bf16(v - hi) (round to nearest even) and every product
+ * is taken as hi*hi + hi*lo + lo*hi with FP32 accumulation.
+ * X [M,K] FP32, Wr [N,K] FP32, out [M,N] FP32.  K must be a multiple of 8.
+ * Deterministic (one fixed order).
+ */
+drgg_status router_gemm_fp32_bf16x3(const float *X, const float *Wr, int64_t M, int64_t N,
+                                    int64_t K, float *out, hipStream_t stream);
+
+/*
+ * Workspace bytes (written to *bytes, a HOST pointer) that a call with these
+ * arguments needs.  cu_count = 0 means the current device's CU count; the
+ * deterministic plan does not depend on it.  0 bytes for fwd and dgrad.
+ */
+drgg_status grouped_gemm_workspace_size(drgg_op op, int32_t E, int64_t M, int64_t N, int64_t K,
+                                        drgg_dtype out_dtype, int deterministic, int cu_count,
+                                        size_t *bytes);
+
+/* Zero a workspace on `stream` (needed once before its first
+ * non-deterministic weight-gradient call). */
+drgg_status drgg_workspace_init(void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The plan a call would use, for inspection (HOST only, touches no GPU when
+ * cu_count > 0).  Fields are written to *out (a host pointer).
+ */
+typedef struct {
+    int32_t tile_m, tile_n, tile_k;   /* output tile and reduction step        */
+    int32_t mfma_m, mfma_n, mfma_k;   /* MFMA instruction shape               */
+    int64_t grid;                     /* workgroups launched                  */
+    int64_t chunk_max;                /* wgrad det: longest token chunk; 0 otherwise */
+    int64_t unit;                     /* wgrad non-det: token units; 0 otherwise */
+    int64_t max_partials;             /* wgrad det: partial slots reserved     */
+    size_t workspace_bytes;
+} drgg_plan_info;
+
+drgg_status drgg_plan(drgg_op op, int32_t E, int64_t M, int64_t N, int64_t K,
+                      drgg_dtype out_dtype, int deterministic, int cu_count, drgg_plan_info *out);
+
+/*
+ * The chunk rule of the deterministic weight gradient (HOST): the token count
+ * of each chunk of an expert with T tokens is returned in *chunk_len (host),
+ * and the number of chunks in *chunks.  chunk_max comes from drgg_plan.
+ * Mirrors exactly what the device computes.
+ */
+drgg_status drgg_wgrad_chunking(int64_t T, int64_t chunk_max, int64_t *chunk_len, int64_t *chunks);
+
+/*
+ * Test knobs (process-wide; not thread-safe; 0 restores the default):
+ *   DRGG_KNOB_TILE        force the output tile of fwd/dgrad/det-wgrad:
+ *                         1 = 256x256, 2 = 128x128, 3 = 256x128, 4 = 128x256
+ *   DRGG_KNOB_GRID        force the workgroup count of the non-deterministic
+ *                         weight gradient (stream-K) to this value
+ *   DRGG_KNOB_REVERSE     1 = walk the work items in reverse order
+ *   DRGG_KNOB_TIMING      1 = record a HIP event on the stream before every
+ *                         kernel launch of a call and after its last launch
+ *                         (read back with drgg_timing_read)
+ * None of them changes the arithmetic of the deterministic variant.
+ */
+enum { DRGG_KNOB_TILE = 1, DRGG_KNOB_GRID = 2, DRGG_KNOB_REVERSE = 3, DRGG_KNOB_TIMING = 4 };
+drgg_status drgg_set_knob(int knob, int64_t value);
+
+/*
+ * With DRGG_KNOB_TIMING on: the number of kernels the most recent call
+ * launched, and for kernel i (0-based, launch order) its name (*kernel, a
+ * static string) and duration in milliseconds (*ms), both HOST pointers.
+ * drgg_timing_read waits for that kernel to finish.
+ */
+int drgg_timing_count(void);
+drgg_status drgg_timing_read(int i, const char **kernel, float *ms);
+
+const char *drgg_status_string(drgg_status status);
+int drgg_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DRGG_H */

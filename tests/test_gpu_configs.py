@@ -1,0 +1,141 @@
+"""GPU parity at the full sizes of the five measured workloads, in the launch
+configuration the benchmark times.
+
+Every output element at these sizes would take the CPU oracle minutes, so
+each program is checked on sampled elements the oracle computes one by one
+(random elements plus every expert's and every 256-row tile's first and last
+row, the last column, every expert's output corners), at the tolerances of
+tests/parity.py.  Integer-valued inputs of the same shapes are compared bit
+for bit on the same samples, empty experts are checked in full, and the
+deterministic variant is re-run and compared bit for bit.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import parity
+from tests.test_gpu_parity import dev_inputs, run_program
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def drgg():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import dense_ragged_grouped_amd as d
+    return d
+
+
+def bits(t):
+    return parity.from_dev(t).view(np.uint16 if t.dtype == torch.bfloat16 else np.uint32).copy()
+
+
+def sampled_check(prob, program, out, out_bf16, integer=False, what=""):
+    idx = parity.sample_indices(prob, program)
+    n = parity.compare(prob, program, parity.from_dev(out), out_bf16, idx=idx, integer=integer, what=what)
+    print(f"{what}: {idx.size} sampled elements ok; {n} needed the FP32-accumulation floor", flush=True)
+
+
+def empty_experts_zero(prob, out):
+    v = bits(out).reshape(prob.E, prob.N, prob.K)
+    for e in np.flatnonzero(prob.counts == 0):
+        assert not np.any(v[e]), f"expert {e} has no tokens but a non-zero gradient"
+
+
+# ---- workload 2: dense projection weight gradient, one group -----------------
+
+@pytest.mark.parametrize("d_out", [48, 64, 512, 1024])
+def test_dense_wgrad(drgg, d_out):
+    for integer in (False, True):
+        prob = synth.config2(d_out, integer=integer)
+        dv = dev_inputs(prob)
+        print(f"dense wgrad d_out={d_out} integer={integer}", flush=True)
+        det = run_program(drgg, "wgrad", dv, torch.float32, True)
+        sampled_check(prob, "wgrad", det, False, integer, f"dense {d_out} det")
+        again = run_program(drgg, "wgrad", dv, torch.float32, True)
+        assert np.array_equal(bits(again), bits(det))
+        nd = run_program(drgg, "wgrad", dv, torch.float32, False)
+        sampled_check(prob, "wgrad", nd, False, integer, f"dense {d_out} split")
+        if integer:
+            assert np.array_equal(bits(nd), bits(det))
+
+
+# ---- workload 3: MoE gate_up, E=8 balanced -------------------------------------
+
+@pytest.fixture(scope="module")
+def moe_gate_up():
+    return synth.config3()
+
+
+@pytest.mark.parametrize("program", ["fwd", "dgrad", "wgrad"])
+def test_moe_gate_up_bf16(drgg, moe_gate_up, program):
+    prob = moe_gate_up
+    dv = dev_inputs(prob)
+    out = run_program(drgg, program, dv, torch.bfloat16, True)
+    sampled_check(prob, program, out, True, what=f"gate_up {program} det")
+    assert np.array_equal(bits(run_program(drgg, program, dv, torch.bfloat16, True)), bits(out))
+    if program == "wgrad":
+        nd = run_program(drgg, program, dv, torch.bfloat16, False)
+        sampled_check(prob, program, nd, True, what=f"gate_up {program} split")
+
+
+@pytest.mark.parametrize("program", ["fwd", "dgrad", "wgrad"])
+def test_moe_gate_up_integer_bitwise(drgg, program):
+    prob = synth.config3(integer=True)
+    dv = dev_inputs(prob)
+    for det in (True, False) if program == "wgrad" else (True,):
+        out = run_program(drgg, program, dv, torch.bfloat16, det)
+        sampled_check(prob, program, out, True, integer=True, what=f"gate_up integer {program} det={det}")
+
+
+# ---- workload 4: MoE down, Zipf-skewed, 2 empty experts --------------------------
+
+@pytest.mark.parametrize("integer", [False, True])
+def test_moe_down_skewed_wgrad(drgg, integer):
+    prob = synth.config4(integer=integer)
+    assert np.sum(prob.counts == 0) == 2
+    dv = dev_inputs(prob)
+    det = run_program(drgg, "wgrad", dv, torch.float32, True)
+    sampled_check(prob, "wgrad", det, False, integer, f"down det integer={integer}")
+    empty_experts_zero(prob, det)
+    assert np.array_equal(bits(run_program(drgg, "wgrad", dv, torch.float32, True)), bits(det))
+    nd = run_program(drgg, "wgrad", dv, torch.float32, False)
+    sampled_check(prob, "wgrad", nd, False, integer, f"down split integer={integer}")
+    empty_experts_zero(prob, nd)
+    a = parity.from_dev(det).astype(np.float64)
+    b = parity.from_dev(nd).astype(np.float64)
+    assert np.linalg.norm(a - b) <= 1e-6 * np.linalg.norm(a)
+    if integer:
+        assert np.array_equal(bits(nd), bits(det))
+
+
+# ---- workload 5: square dense projection + FP32 router -------------------------
+
+@pytest.mark.parametrize("program", ["fwd", "dgrad", "wgrad"])
+def test_dense_square_bf16(drgg, program):
+    prob = synth.config5(need=("X", "W") if program == "fwd" else ("G", "W") if program == "dgrad" else ("X", "G"))
+    dv = dev_inputs(prob)
+    out = run_program(drgg, program, dv, torch.bfloat16, True)
+    sampled_check(prob, program, out, True, what=f"square {program}")
+    assert np.array_equal(bits(run_program(drgg, program, dv, torch.bfloat16, True)), bits(out))
+
+
+def test_router_full_size(drgg):
+    X, Wr = synth.router_inputs()
+    out = drgg.router_gemm_fp32_bf16x3(parity.to_dev(X), parity.to_dev(Wr))
+    o = parity.from_dev(out).ravel().astype(np.float64)
+    rng = np.random.default_rng(0)
+    idx = np.unique(np.concatenate([rng.integers(0, o.size, 4000), [0, o.size - 1]]))
+    emul = oracle.router_bf16x3(X, Wr, idx)
+    exact = oracle.router_exact(X, Wr, idx)
+    assert np.linalg.norm(o[idx] - emul) <= 1e-6 * np.linalg.norm(emul)
+    M, N = out.shape
+    ax = np.abs(X).max(axis=1)[idx // N]
+    aw = np.abs(Wr).max(axis=1)[idx % N]
+    parity.check_fp32(o[idx], exact, np.full(idx.size, X.shape[1]), ax, aw, what="router full size")
+    rel = np.linalg.norm(o[idx] - exact) / np.linalg.norm(exact)
+    print(f"router: relative Frobenius error vs exact FP32 product {rel:.2e}", flush=True)

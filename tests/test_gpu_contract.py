@@ -1,0 +1,257 @@
+"""GPU tests of the variants' contracts and of the boundary's behaviour.
+
+* deterministic variant: bitwise identical over 20 runs, across output tile
+  shapes, across the order the work items are walked in, and on a stream
+  restricted to a subset of the CUs (fewer CUs, same bits);
+* non-deterministic variant: the tile sums and tickets are zero again after
+  every call; every stream-K partition (grid sizes from 1 to more workgroups
+  than units) matches the oracle;
+* the router's BF16x3 split against both oracles;
+* edge cases: no tokens, one token per expert, 1024 experts, the smallest N
+  and K, all tokens on one expert;
+* error paths: misaligned pointers, a short workspace, bad dtypes.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import parity
+from tests.test_gpu_parity import dev_inputs, ragged_problem, run_program
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def drgg():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import dense_ragged_grouped_amd as d
+    return d
+
+
+def bits(t):
+    return parity.from_dev(t).view(np.uint16 if t.dtype == torch.bfloat16 else np.uint32).copy()
+
+
+DET_CASE = (301, 4, 3000, 264, 520, (1,))   # multi-chunk wgrad, ragged, an empty expert
+
+
+@pytest.mark.parametrize("program", ["fwd", "dgrad", "wgrad"])
+def test_deterministic_20_runs_bitwise(drgg, program):
+    prob = ragged_problem(*DET_CASE)
+    dv = dev_inputs(prob)
+    for out_dtype in (torch.float32, torch.bfloat16):
+        ref = bits(run_program(drgg, program, dv, out_dtype, True))
+        for i in range(19):
+            got = bits(run_program(drgg, program, dv, out_dtype, True))
+            assert np.array_equal(got, ref), f"run {i + 2} differs"
+
+
+@pytest.mark.parametrize("program", ["fwd", "dgrad", "wgrad"])
+def test_deterministic_across_tile_shapes_and_walk_order(drgg, program):
+    """The tile shape and the order of the work items are free choices of the
+    deterministic variant: they must not change a bit."""
+    prob = ragged_problem(*DET_CASE)
+    dv = dev_inputs(prob)
+    tiles = [1, 2, 3, 4] + ([5] if program == "wgrad" else [])
+    for out_dtype in (torch.float32, torch.bfloat16):
+        ref = bits(run_program(drgg, program, dv, out_dtype, True))
+        try:
+            for tile in tiles:
+                for rev in (0, 1):
+                    drgg.set_knob(drgg.KNOB_TILE, tile)
+                    drgg.set_knob(drgg.KNOB_REVERSE, rev)
+                    got = bits(run_program(drgg, program, dv, out_dtype, True))
+                    assert np.array_equal(got, ref), f"tile {tile} reverse {rev} changed the bits"
+        finally:
+            drgg.set_knob(drgg.KNOB_TILE, 0)
+            drgg.set_knob(drgg.KNOB_REVERSE, 0)
+    parity.compare(prob, program, parity.from_dev(run_program(drgg, program, dv, torch.float32, True)), False)
+
+
+def _hip():
+    return ctypes.CDLL("libamdhip64.so")
+
+
+def test_deterministic_on_fewer_cus(drgg):
+    """Run on a stream whose CU mask enables a quarter of the CUs: the
+    deterministic results must equal those on the full device."""
+    hip = _hip()
+    props = torch.cuda.get_device_properties(0)
+    ncu = props.multi_processor_count
+    words = (ncu + 31) // 32
+    mask = (ctypes.c_uint32 * words)()
+    for cu in range(0, ncu, 4):
+        mask[cu // 32] |= 1 << (cu % 32)
+    stream = ctypes.c_void_p()
+    hip.hipExtStreamCreateWithCUMask.restype = ctypes.c_int
+    rc = hip.hipExtStreamCreateWithCUMask(ctypes.byref(stream), ctypes.c_uint32(words), mask)
+    if rc != 0:
+        hip.hipGetLastError()      # clear the error so that later calls do not report it
+        pytest.skip(f"hipExtStreamCreateWithCUMask returned {rc}: CU masks unavailable here")
+    try:
+        ext = torch.cuda.ExternalStream(stream.value)
+        prob = ragged_problem(*DET_CASE)
+        dv = dev_inputs(prob)
+        for program in ("fwd", "dgrad", "wgrad"):
+            ref = bits(run_program(drgg, program, dv, torch.bfloat16, True))
+            torch.cuda.synchronize()
+            with torch.cuda.stream(ext):
+                out = run_program(drgg, program, dv, torch.bfloat16, True)
+            ext.synchronize()
+            assert np.array_equal(bits(out), ref), f"{program}: CU mask changed the bits"
+    finally:
+        torch.cuda.synchronize()
+        hip.hipStreamDestroy(stream)
+
+
+def _nondet_ws(drgg, prob, out_code):
+    n = drgg.workspace_size(drgg.OP_WGRAD, prob.E, prob.M, prob.N, prob.K, out_code, False)
+    return torch.zeros(n, dtype=torch.uint8, device="cuda")
+
+
+@pytest.mark.parametrize("grid", [0, 1, 3, 7, 100, 1000, 5000])
+def test_nondet_stream_k_partitions(drgg, grid):
+    prob = ragged_problem(311, 3, 2500, 136, 392, (2,))
+    dv = dev_inputs(prob)
+    drgg.set_knob(drgg.KNOB_GRID, grid)
+    try:
+        for out_dtype, code in ((torch.float32, drgg.FP32), (torch.bfloat16, drgg.BF16)):
+            ws = _nondet_ws(drgg, prob, code)
+            out = drgg.grouped_gemm_wgrad(dv["X"], dv["G"], dv["offs"], out_dtype=out_dtype,
+                                          deterministic=False, workspace=ws)
+            torch.cuda.synchronize()
+            assert int(torch.count_nonzero(ws)) == 0, "tile sums / tickets not cleared"
+            parity.compare(prob, "wgrad", parity.from_dev(out), out_dtype == torch.bfloat16,
+                           what=f"stream-K grid {grid}")
+    finally:
+        drgg.set_knob(drgg.KNOB_GRID, 0)
+
+
+def test_nondet_repeated_calls_keep_workspace_zero(drgg):
+    prob = ragged_problem(312, 4, 3000, 256, 256, ())
+    dv = dev_inputs(prob)
+    ws = _nondet_ws(drgg, prob, drgg.FP32)
+    det = parity.from_dev(run_program(drgg, "wgrad", dv, torch.float32, True)).astype(np.float64)
+    for _ in range(10):
+        out = drgg.grouped_gemm_wgrad(dv["X"], dv["G"], dv["offs"], out_dtype=torch.float32,
+                                      deterministic=False, workspace=ws)
+        torch.cuda.synchronize()
+        assert int(torch.count_nonzero(ws)) == 0
+        g = parity.from_dev(out).astype(np.float64)
+        assert np.linalg.norm(g - det) <= 1e-6 * np.linalg.norm(det)
+
+
+def test_nondet_integer_inputs_match_det_bitwise(drgg):
+    prob = ragged_problem(313, 4, 3000, 256, 256, (3,), integer=True)
+    dv = dev_inputs(prob)
+    det = bits(run_program(drgg, "wgrad", dv, torch.float32, True))
+    ws = _nondet_ws(drgg, prob, drgg.FP32)
+    for grid in (0, 5, 300):
+        drgg.set_knob(drgg.KNOB_GRID, grid)
+        try:
+            out = drgg.grouped_gemm_wgrad(dv["X"], dv["G"], dv["offs"], out_dtype=torch.float32,
+                                          deterministic=False, workspace=ws)
+        finally:
+            drgg.set_knob(drgg.KNOB_GRID, 0)
+        assert np.array_equal(bits(out), det)
+
+
+# ---- router ------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", [(300, 256, 520), (128, 128, 64), (1000, 40, 264), (1, 8, 8)])
+def test_router_bf16x3(drgg, shape):
+    M, N, K = shape
+    X, Wr = synth.router_inputs(M, N, K, cfg_seed=7)
+    out = parity.from_dev(drgg.router_gemm_fp32_bf16x3(parity.to_dev(X), parity.to_dev(Wr))).astype(np.float64)
+    emul = oracle.router_bf16x3(X, Wr)
+    exact = oracle.router_exact(X, Wr)
+    # against the step-by-step emulation: only the FP32 accumulation order differs
+    assert np.linalg.norm(out - emul) <= 1e-6 * np.linalg.norm(emul)
+    # against the exact product: the FP32-output tolerance
+    kred = np.full(out.size, K)
+    ax = np.abs(X).max(axis=1)[:, None] * np.ones((1, N))
+    aw = np.ones((M, 1)) * np.abs(Wr).max(axis=1)[None, :]
+    parity.check_fp32(out, exact, kred, ax, aw, what=f"router {shape}")
+
+
+def test_router_bf16_representable_inputs_exact(drgg):
+    """Inputs with at most 8 significant bits make lo = 0; with small integers
+    every sum is exact too, so the router equals the exact product bit for bit."""
+    rng = np.random.default_rng(5)
+    X = rng.integers(-4, 5, size=(256, 512)).astype(np.float32)
+    Wr = rng.integers(-4, 5, size=(256, 512)).astype(np.float32)
+    out = parity.from_dev(drgg.router_gemm_fp32_bf16x3(parity.to_dev(X), parity.to_dev(Wr)))
+    assert np.array_equal(out, oracle.round_f32(oracle.router_exact(X, Wr)))
+
+
+# ---- edge cases --------------------------------------------------------------
+
+def test_no_tokens(drgg):
+    E, N, K = 3, 64, 72
+    offs = torch.zeros(E + 1, dtype=torch.int32, device="cuda")
+    X = torch.zeros((0, K), dtype=torch.bfloat16, device="cuda")
+    G = torch.zeros((0, N), dtype=torch.bfloat16, device="cuda")
+    W = torch.ones((E, N, K), dtype=torch.bfloat16, device="cuda")
+    assert drgg.grouped_gemm_fwd(X, W, offs).shape == (0, N)
+    assert drgg.grouped_gemm_dgrad(G, W, offs).shape == (0, K)
+    for det in (True, False):
+        for dt in (torch.float32, torch.bfloat16):
+            dW = torch.full((E, N, K), 7.0, dtype=dt, device="cuda")
+            drgg.grouped_gemm_wgrad(X, G, offs, out_dtype=dt, deterministic=det, out=dW)
+            torch.cuda.synchronize()
+            assert not np.any(bits(dW)), "experts without tokens must get +0"
+
+
+@pytest.mark.parametrize("det", [True, False])
+def test_tiny_experts_and_many_groups(drgg, det):
+    # 1024 experts, most with 0..3 tokens; smallest N and K
+    rng = np.random.default_rng(9)
+    counts = rng.integers(0, 4, size=1024)
+    prob = synth.make_problem("many", 91, counts, N=8, K=8)
+    dv = dev_inputs(prob)
+    for program in ("fwd", "dgrad", "wgrad"):
+        out = run_program(drgg, program, dv, torch.float32, det)
+        torch.cuda.synchronize()
+        parity.compare(prob, program, parity.from_dev(out), False, what=f"many {program}")
+
+
+@pytest.mark.parametrize("det", [True, False])
+def test_one_hot_routing_equals_dense_call(drgg, det):
+    prob = ragged_problem(321, 4, 1500, 200, 136, (0, 1, 3))   # all tokens on expert 2
+    dense = synth.Problem("dense", 1, prob.M, prob.N, prob.K, np.array([0, prob.M], dtype=np.int32),
+                          prob.X, prob.W[2:3].copy(), prob.G)
+    dv, dd = dev_inputs(prob), dev_inputs(dense)
+    for program in ("fwd", "dgrad", "wgrad"):
+        g = bits(run_program(drgg, program, dv, torch.float32, True))
+        d = bits(run_program(drgg, program, dd, torch.float32, True))
+        if program == "wgrad":
+            g = g.reshape(4, prob.N, prob.K)
+            assert np.array_equal(g[2], d.reshape(prob.N, prob.K))
+            assert not np.any(g[[0, 1, 3]])
+        else:
+            assert np.array_equal(g, d)
+
+
+# ---- errors ------------------------------------------------------------------
+
+def test_error_paths(drgg):
+    prob = ragged_problem(331, 2, 100, 64, 64, ())
+    dv = dev_inputs(prob)
+    with pytest.raises(TypeError):
+        drgg.grouped_gemm_fwd(dv["X"].float(), dv["W"], dv["offs"])
+    # a pointer that is not 16-byte aligned: reaches the C ABI, which refuses
+    x_off = torch.empty(prob.M * prob.K + 8, dtype=torch.bfloat16, device="cuda")[1:1 + prob.M * prob.K]
+    x_off = x_off.view(prob.M, prob.K)
+    with pytest.raises(drgg.DrggError) as ei:
+        drgg.grouped_gemm_fwd(x_off, dv["W"], dv["offs"])
+    assert ei.value.status == 3
+    small = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(drgg.DrggError) as ei:
+        drgg.grouped_gemm_wgrad(dv["X"], dv["G"], dv["offs"], deterministic=False, workspace=small)
+    assert ei.value.status == 5
