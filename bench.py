@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--all", action="store_true", help="also time the other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", default="", help="profiling aid: run only these programs (comma list)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run a plain 1 GiB device-to-device copy 5 times (HBM counter calibration) and exit")
     return ap.parse_args()
 
 
@@ -118,6 +120,34 @@ def cpu_baseline(prob):
             "sample": "fwd rows 0-4095 x all 1536 cols, dgrad rows 0-2047 x all 2048 cols, "
                       "wgrad expert 0 rows n 0-63 x all 2048 cols over its 16384 tokens "
                       f"({flops / 1e9:.1f} GFLOP in {secs:.1f} s, binary64 accumulation)"}
+
+
+PROFILE = os.path.join(ROOT, "profiles", "gg_kernels_moe_gate_up_e8_t131072_k2048_n1536.md")
+KERNEL_SRC = os.path.join(ROOT, "dense_ragged_grouped_amd", "csrc", "kernels.hip")
+PROFILE_KEYS = {"gg_fwd_kernel": "gg_fwd_dgrad_kernel<0,", "gg_dgrad_kernel": "gg_fwd_dgrad_kernel<1,",
+                "gg_wgrad_det_kernel": "gg_wgrad_det_kernel<", "gg_wgrad_fold_kernel": "gg_wgrad_fold_kernel<"}
+
+
+def measured_traffic(kernel):
+    """HBM-side bytes per launch of `kernel` from the committed rocprofv3
+    counter summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy's
+    readings), or None when the kernel source changed since it was taken."""
+    import hashlib
+    try:
+        text = open(PROFILE).read()
+        sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    except OSError:
+        return None
+    if f"`{sha}`" not in text:
+        return None
+    for line in text.splitlines():
+        if line.startswith("traffic_bytes_per_launch:"):
+            table = json.loads(line.split(":", 1)[1])
+            key = PROFILE_KEYS.get(kernel, kernel)
+            for name, val in table.items():
+                if name.startswith(key):
+                    return float(val)
+    return None
 
 
 def other_workloads(torch, drgg, synth, reps):
@@ -196,6 +226,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs an MI355X GPU", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        # a plain copy kernel of known size: 1 GiB read + 1 GiB written per launch
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 5 launches of a 1 GiB copy")
+        return
     import dense_ragged_grouped_amd as drgg
     import synth
 
@@ -238,7 +277,7 @@ def main():
     dom_ms = main_kernels[dom]
     achieved = flop_prog / dom_ms / 1e9
     roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(dom),
                 "avg_launch_us": dom_ms * 1e3,
                 "flop_per_launch": flop_prog}
 

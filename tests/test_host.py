@@ -1,0 +1,194 @@
+"""Host-side tests of the C ABI (no GPU needed).
+
+* libdrgg.so loads and exports every function include/drgg.h declares;
+* argument checks reject bad calls before anything reaches the GPU;
+* the planner: the deterministic chunk rule's properties, its independence
+  from the CU count, and the bounds the kernels rely on (launched grid and
+  partial slots cover every ragged distribution).
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "drgg.h")
+LIB = os.path.join(ROOT, "dense_ragged_grouped_amd", "libdrgg.so")
+
+
+@pytest.fixture(scope="module")
+def drgg():
+    if not os.path.exists(LIB):   # build only when nothing is built
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "_drgg_build", os.path.join(ROOT, "dense_ragged_grouped_amd", "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
+    import dense_ragged_grouped_amd as d
+    return d
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\([^;{]*\)\s*;", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol(drgg):
+    names = header_functions()
+    assert len(names) >= 12
+    lib = ctypes.CDLL(LIB)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, f"declared in drgg.h but not exported: {missing}"
+    assert sorted(drgg.EXPORTS) == names
+    assert drgg.abi_version() == 1
+
+
+def test_status_strings(drgg):
+    for code in range(8):
+        assert drgg.status_string(code) and drgg.status_string(code) != "unknown status"
+    assert drgg.status_string(99) == "unknown status"
+
+
+# ---- argument checks (all rejected on the host, before any HIP call) ----------
+
+A16 = 0x10000          # a fake, 16-byte aligned "device" address (never dereferenced)
+
+
+def fwd(drgg, *, X=A16, W=A16, offs=A16, E=2, M=64, N=64, K=64, dt=1, Y=A16):
+    return drgg.lib.grouped_gemm_fwd(X, W, offs, E, M, N, K, dt, 1, Y, None, 0, None)
+
+
+def test_fwd_argument_checks(drgg):
+    assert fwd(drgg, E=0) == 1
+    assert fwd(drgg, E=1025) == 1
+    assert fwd(drgg, dt=7) == 1
+    assert fwd(drgg, W=0) == 1
+    assert fwd(drgg, X=0) == 1
+    assert fwd(drgg, M=-1) == 2
+    assert fwd(drgg, N=4) == 2
+    assert fwd(drgg, N=12) == 3
+    assert fwd(drgg, K=20) == 3
+    assert fwd(drgg, X=A16 + 2) == 3
+    assert fwd(drgg, offs=A16 + 2) == 3
+    assert fwd(drgg, M=2 ** 31 - 1, K=2 ** 31 - 8) == 4
+    assert fwd(drgg, M=2 ** 31) == 2
+
+
+def test_wgrad_workspace_checks(drgg):
+    lib = drgg.lib
+    # deterministic: needs partial slots when experts may be cut into chunks
+    need = drgg.workspace_size(drgg.OP_WGRAD, 2, 100000, 256, 256, drgg.FP32, True)
+    assert need > 0
+    assert lib.grouped_gemm_wgrad(A16, A16, A16, 2, 100000, 256, 256, 1, 1, A16, None, 0, None) == 5
+    assert lib.grouped_gemm_wgrad(A16, A16, A16, 2, 100000, 256, 256, 1, 1, A16, A16, need - 1, None) == 5
+    assert lib.grouped_gemm_wgrad(A16, A16, A16, 2, 100000, 256, 256, 1, 1, A16, A16 + 8, need, None) == 3
+    assert lib.grouped_gemm_wgrad(A16, A16, 0, 2, 100000, 256, 256, 1, 1, A16, A16, need, None) == 1
+
+
+def test_router_argument_checks(drgg):
+    r = drgg.lib.router_gemm_fp32_bf16x3
+    assert r(0, A16, 16, 16, 16, A16, None) == 1
+    assert r(A16, A16, -1, 16, 16, A16, None) == 2
+    assert r(A16, A16, 16, 16, 12, A16, None) == 3
+    assert r(A16, A16, 16, 16, 16, A16 + 4, None) == 3
+
+
+def test_knob_checks(drgg):
+    assert drgg.lib.drgg_set_knob(99, 1) == 1
+    assert drgg.lib.drgg_set_knob(drgg.KNOB_TILE, 42) == 1
+    assert drgg.lib.drgg_set_knob(drgg.KNOB_TILE, 0) == 0
+
+
+# ---- planner -------------------------------------------------------------------
+
+WORKLOADS = {
+    "gate_up": (8, 131072, 1536, 2048),
+    "down": (32, 131072, 2048, 768),
+    "square": (1, 16384, 4096, 4096),
+    "dense48": (1, 16384, 48, 4096),
+    "dense1024": (1, 16384, 1024, 4096),
+    "tiny": (4, 512, 512, 256),
+}
+
+
+def test_chunk_rule_values(drgg):
+    cm = {k: drgg.plan(drgg.OP_WGRAD, *v, drgg.FP32, True)["chunk_max"] for k, v in WORKLOADS.items()}
+    assert cm["gate_up"] == 12288 and drgg.wgrad_chunking(16384, cm["gate_up"]) == (8192, 2)
+    assert cm["down"] == 6144 and drgg.wgrad_chunking(42987, cm["down"])[1] == 7
+    assert cm["square"] == 16384 and drgg.wgrad_chunking(16384, cm["square"]) == (16384, 1)
+    assert drgg.wgrad_chunking(128, cm["tiny"]) == (128, 1)
+
+
+@pytest.mark.parametrize("chunk_max", [512, 1152, 6144, 12288, 16384])
+def test_chunking_properties(drgg, chunk_max):
+    for T in list(range(0, 300)) + list(np.random.default_rng(1).integers(1, 200000, 300)):
+        T = int(T)
+        ln, n = drgg.wgrad_chunking(T, chunk_max)
+        if T == 0:
+            assert (ln, n) == (0, 0)
+            continue
+        assert ln % 64 == 0 and ln > 0
+        assert n * ln >= T and (n - 1) * ln < T                  # chunks tile [0, T)
+        assert n <= -(-T // chunk_max)                            # no more than ceil(T/chunk_max)
+        assert ln <= -(-chunk_max // 64) * 64 or n == 1
+        if T <= chunk_max:
+            assert n == 1
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_det_plan_does_not_depend_on_cu_count(drgg, name):
+    plans = [drgg.plan(drgg.OP_WGRAD, *WORKLOADS[name], drgg.BF16, True, cu) for cu in (1, 64, 80, 256, 304)]
+    assert all(p == plans[0] for p in plans)
+    for op in (drgg.OP_FWD, drgg.OP_DGRAD):
+        plans = [drgg.plan(op, *WORKLOADS[name], drgg.BF16, True, cu) for cu in (1, 256, 304)]
+        assert all(p == plans[0] for p in plans)
+
+
+def _distributions(E, M, rng):
+    yield np.full(E, M // E) + (np.arange(E) < M % E)            # balanced
+    c = np.zeros(E, dtype=np.int64); c[0] = M; yield c            # all on one expert
+    c = np.zeros(E, dtype=np.int64); c[-1] = M; yield c
+    for _ in range(20):
+        p = rng.dirichlet(np.full(E, 0.3))
+        yield rng.multinomial(M, p)
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_grid_and_slot_bounds_cover_every_distribution(drgg, name):
+    E, M, N, K = WORKLOADS[name]
+    rng = np.random.default_rng(7)
+    for tile in (0, 1, 2, 3, 4, 5):
+        drgg.set_knob(drgg.KNOB_TILE, tile)
+        try:
+            pw = drgg.plan(drgg.OP_WGRAD, E, M, N, K, drgg.FP32, True)
+            pf = drgg.plan(drgg.OP_FWD, E, M, N, K, drgg.FP32, True)
+            pd = drgg.plan(drgg.OP_DGRAD, E, M, N, K, drgg.FP32, True)
+        finally:
+            drgg.set_knob(drgg.KNOB_TILE, 0)
+        P = -(-N // pw["tile_m"]) * -(-K // pw["tile_n"])
+        for counts in _distributions(E, M, rng):
+            assert counts.sum() == M
+            chunks = np.array([drgg.wgrad_chunking(int(t), pw["chunk_max"])[1] for t in counts])
+            assert P * chunks.sum() <= pw["grid"]
+            assert chunks[chunks > 1].sum() <= pw["max_partials"]
+            for p, cols in ((pf, N), (pd, K)):
+                items = sum(-(-int(t) // p["tile_m"]) for t in counts) * -(-cols // p["tile_n"])
+                assert items <= p["grid"]
+
+
+def test_nondet_plan_uses_the_cu_count_and_unit(drgg):
+    p = drgg.plan(drgg.OP_WGRAD, 32, 131072, 2048, 768, drgg.FP32, False, 256)
+    assert p["grid"] == 256 and p["unit"] == 512
+    P = (2048 // 256) * (768 // 256)
+    assert p["workspace_bytes"] >= 32 * P * 256 * 256 * 4 + 32 * P * 4
+    assert drgg.plan(drgg.OP_WGRAD, 32, 131072, 2048, 768, drgg.FP32, False, 80)["grid"] == 80
+    drgg.set_knob(drgg.KNOB_GRID, 7)
+    try:
+        assert drgg.plan(drgg.OP_WGRAD, 32, 131072, 2048, 768, drgg.FP32, False, 256)["grid"] == 7
+    finally:
+        drgg.set_knob(drgg.KNOB_GRID, 0)
