@@ -56,12 +56,12 @@ class PlanInfo(ctypes.Structure):
         return {name: getattr(self, name) for name, _ in self._fields_}
 
 
-def _load():
-    if not os.path.exists(LIB_PATH):
+def _load(path=LIB_PATH):
+    if not os.path.exists(path):
         raise ImportError(
-            f"{LIB_PATH} is not built; run `python -m dense_ragged_grouped_amd.build` "
+            f"{path} is not built; run `python -m dense_ragged_grouped_amd.build` "
             "(the grouped GEMM has no fallback path)")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     vp, i32, i64, sz, c_int = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
     gemm = [vp, vp, vp, i32, i64, i64, i64, c_int, c_int, vp, vp, sz, vp]
     for name in ("grouped_gemm_fwd", "grouped_gemm_dgrad", "grouped_gemm_wgrad"):

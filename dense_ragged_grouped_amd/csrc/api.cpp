@@ -56,7 +56,8 @@ drgg_status check_problem(int32_t E, int64_t M, int64_t N, int64_t K, drgg_dtype
     if (E < 1 || E > kMaxExperts) return DRGG_EINVAL;
     if (dt != DRGG_BF16 && dt != DRGG_FP32) return DRGG_EINVAL;
     if (M < 0 || N < 8 || K < 8) return DRGG_ESHAPE;
-    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return DRGG_ESHAPE;
+    // N, K <= 2^22 keep every per-lane byte offset inside a tile below 2^31
+    if (M > INT32_MAX || N > (1 << 22) || K > (1 << 22)) return DRGG_ESHAPE;
     if (N % 8 != 0 || K % 8 != 0) return DRGG_EALIGN;
     int64_t t;
     // every buffer: X [M,K], G [M,N], W/dW [E,N,K] (x4 bytes for FP32)
@@ -86,23 +87,30 @@ drgg_status make_plan(drgg_op op, int32_t E, int64_t M, int64_t N, int64_t K, in
     p->tile = tile;
     p->ts = tile_shape(tile);
     const int64_t bm = p->ts.bm, bn = p->ts.bn;
+    // persistent grid: as many workgroups as fit on the device at once, never
+    // more than there are work items (a bound that holds for any offsets)
+    const int64_t g_knob = g_knob_grid.load();
+    const int64_t resident = (int64_t)cu_count * wgs_per_cu(p->ts);
+    auto grid_for = [&](int64_t items_max) {
+        int64_t g = g_knob > 0 ? g_knob : (resident < items_max ? resident : items_max);
+        return g < 1 ? (int64_t)1 : g;
+    };
     if (op == DRGG_OP_FWD || op == DRGG_OP_DGRAD) {
         const int64_t ncols = op == DRGG_OP_FWD ? N : K;
-        p->grid = (M / bm + E) * ceil_div(ncols, bn);
-        return DRGG_OK;
+        p->grid = grid_for((M / bm + E) * ceil_div(ncols, bn));
+        return p->grid > INT32_MAX ? DRGG_ESHAPE : DRGG_OK;
     }
     const int64_t P = ceil_div(N, bm) * ceil_div(K, bn);
     if (det) {
         p->chunk_max = wgrad_chunk_max(E, M, N, K);
         p->max_partials = wgrad_max_partials(M, p->chunk_max);
         // chunks_e <= ceil(T_e / chunk_max) <= T_e / chunk_max + 1
-        p->grid = P * (M / p->chunk_max + E);
+        p->grid = grid_for(P * (M / p->chunk_max + E));
         int64_t b;
         if (!mul_ok(p->max_partials, N * K, &b) || !mul_ok(b, 4, &b)) return DRGG_EOVERFLOW;
         p->ws_bytes = (size_t)b;
     } else {
-        int64_t g = g_knob_grid.load();
-        p->grid = g > 0 ? g : cu_count;
+        p->grid = g_knob > 0 ? g_knob : resident;
         int64_t sums, tk;
         if (!mul_ok(P * E, bm * bn, &sums) || !mul_ok(sums, 4, &sums)) return DRGG_EOVERFLOW;
         tk = P * E * 4;
@@ -157,10 +165,13 @@ drgg_status run_fwd_dgrad(drgg_op op, const void* A, const void* W, const int32_
     if (!W || !offs || (M > 0 && (!A || !out))) return DRGG_EINVAL;
     if (!aligned16(A) || !aligned16(W) || !aligned16(out) || (reinterpret_cast<uintptr_t>(offs) & 3u))
         return DRGG_EALIGN;
-    Plan p;
-    st = make_plan(op, E, M, N, K, 1, 0, &p);
-    if (st != DRGG_OK) return st;
     if (M == 0) return DRGG_OK;   // no rows to write
+    int cus = 0;
+    st = current_cu_count(&cus);
+    if (st != DRGG_OK) return st;
+    Plan p;
+    st = make_plan(op, E, M, N, K, 1, cus, &p);
+    if (st != DRGG_OK) return st;
     GemmArgs a{};
     a.A = static_cast<const uint16_t*>(A);
     a.B = static_cast<const uint16_t*>(W);
@@ -202,18 +213,19 @@ drgg_status grouped_gemm_wgrad(const void* X, const void* G, const int32_t* grou
     if (!aligned16(X) || !aligned16(G) || !aligned16(dW) ||
         (reinterpret_cast<uintptr_t>(group_offsets) & 3u))
         return DRGG_EALIGN;
-    int cus = 0;
-    if (!deterministic) {
-        st = current_cu_count(&cus);
-        if (st != DRGG_OK) return st;
-    }
+    // the workspace size does not depend on the CU count: check it first
     Plan p;
-    st = make_plan(DRGG_OP_WGRAD, E, M, N, K, deterministic, cus, &p);
+    st = make_plan(DRGG_OP_WGRAD, E, M, N, K, deterministic, 1, &p);
     if (st != DRGG_OK) return st;
     if (p.ws_bytes > 0) {
         if (!workspace || workspace_bytes < p.ws_bytes) return DRGG_EWORKSPACE;
         if (!aligned16(workspace)) return DRGG_EALIGN;
     }
+    int cus = 0;
+    st = current_cu_count(&cus);
+    if (st != DRGG_OK) return st;
+    st = make_plan(DRGG_OP_WGRAD, E, M, N, K, deterministic, cus, &p);
+    if (st != DRGG_OK) return st;
     GemmArgs a{};
     a.A = static_cast<const uint16_t*>(G);   // A rows: output rows n of dW (from G)
     a.B = static_cast<const uint16_t*>(X);   // B rows: output cols k of dW (from X)
@@ -256,12 +268,8 @@ drgg_status grouped_gemm_workspace_size(drgg_op op, int32_t E, int64_t M, int64_
     if (op != DRGG_OP_FWD && op != DRGG_OP_DGRAD && op != DRGG_OP_WGRAD) return DRGG_EINVAL;
     drgg_status st = check_problem(E, M, N, K, out_dtype);
     if (st != DRGG_OK) return st;
-    if (op == DRGG_OP_WGRAD && !deterministic && cu_count <= 0) {
-        st = current_cu_count(&cu_count);
-        if (st != DRGG_OK) return st;
-    }
-    Plan p;
-    st = make_plan(op, E, M, N, K, deterministic, cu_count, &p);
+    Plan p;   // the workspace size does not depend on the CU count
+    st = make_plan(op, E, M, N, K, deterministic, cu_count > 0 ? cu_count : 1, &p);
     if (st != DRGG_OK) return st;
     *bytes = p.ws_bytes;
     return DRGG_OK;
@@ -279,7 +287,7 @@ drgg_status drgg_plan(drgg_op op, int32_t E, int64_t M, int64_t N, int64_t K, dr
     if (op != DRGG_OP_FWD && op != DRGG_OP_DGRAD && op != DRGG_OP_WGRAD) return DRGG_EINVAL;
     drgg_status st = check_problem(E, M, N, K, out_dtype);
     if (st != DRGG_OK) return st;
-    if (op == DRGG_OP_WGRAD && !deterministic && cu_count <= 0) {
+    if (cu_count <= 0) {
         st = current_cu_count(&cu_count);
         if (st != DRGG_OK) return st;
     }

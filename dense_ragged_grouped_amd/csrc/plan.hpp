@@ -91,6 +91,15 @@ inline int64_t wgrad_max_partials(int64_t M, int64_t chunk_max) {
     return M <= 0 ? 0 : (2 * M) / chunk_max + 1;
 }
 
+// Workgroups of a persistent grouped-GEMM kernel that fit on one CU (LDS:
+// two stages of (BM + BN) x 64 BF16 plus about 11 KB of schedule tables, out
+// of 160 KB).
+inline int64_t wgs_per_cu(TileShape t) {
+    const int64_t lds = 2 * (int64_t)(t.bm + t.bn) * 128 + 11 * 1024;
+    const int64_t n = (160 * 1024) / lds;
+    return n < 1 ? 1 : n;
+}
+
 // Default output tile per program.
 inline int default_tile(int op, int64_t N, int64_t K) {
     if (op == 2 && N <= 64) return kTile64x256;   // skinny weight gradient

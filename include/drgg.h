@@ -57,7 +57,7 @@
  *     access leaves the buffers, and the result for invalid offsets is
  *     unspecified.
  *   * Alignment: every pointer 16-byte aligned; N and K multiples of 8.
- *   * Limits: 1 <= E <= 1024, 0 <= M < 2^31, 8 <= N, K < 2^31, and every
+ *   * Limits: 1 <= E <= 1024, 0 <= M < 2^31, 8 <= N, K <= 2^22, and every
  *     buffer size below 2^62 bytes (checked in 64-bit arithmetic).
  */
 #ifndef DRGG_H
@@ -148,8 +148,8 @@ drgg_status router_gemm_fp32_bf16x3(const float *X, const float *Wr, int64_t M, 
 
 /*
  * Workspace bytes (written to *bytes, a HOST pointer) that a call with these
- * arguments needs.  cu_count = 0 means the current device's CU count; the
- * deterministic plan does not depend on it.  0 bytes for fwd and dgrad.
+ * arguments needs; they do not depend on the CU count (cu_count is accepted
+ * for symmetry with drgg_plan and ignored).  0 bytes for fwd and dgrad.
  */
 drgg_status grouped_gemm_workspace_size(drgg_op op, int32_t E, int64_t M, int64_t N, int64_t K,
                                         drgg_dtype out_dtype, int deterministic, int cu_count,
@@ -166,7 +166,7 @@ drgg_status drgg_workspace_init(void *workspace, size_t workspace_bytes, hipStre
 typedef struct {
     int32_t tile_m, tile_n, tile_k;   /* output tile and reduction step        */
     int32_t mfma_m, mfma_n, mfma_k;   /* MFMA instruction shape               */
-    int64_t grid;                     /* workgroups launched                  */
+    int64_t grid;                     /* workgroups launched (persistent)     */
     int64_t chunk_max;                /* wgrad det: longest token chunk; 0 otherwise */
     int64_t unit;                     /* wgrad non-det: token units; 0 otherwise */
     int64_t max_partials;             /* wgrad det: partial slots reserved     */
@@ -188,8 +188,9 @@ drgg_status drgg_wgrad_chunking(int64_t T, int64_t chunk_max, int64_t *chunk_len
  * Test knobs (process-wide; not thread-safe; 0 restores the default):
  *   DRGG_KNOB_TILE        force the output tile of fwd/dgrad/det-wgrad:
  *                         1 = 256x256, 2 = 128x128, 3 = 256x128, 4 = 128x256
- *   DRGG_KNOB_GRID        force the workgroup count of the non-deterministic
- *                         weight gradient (stream-K) to this value
+ *   DRGG_KNOB_GRID        force the workgroup count of the persistent kernels
+ *                         (every program; for the non-deterministic weight
+ *                         gradient it also sets the stream-K partition)
  *   DRGG_KNOB_REVERSE     1 = walk the work items in reverse order
  *   DRGG_KNOB_TIMING      1 = record a HIP event on the stream before every
  *                         kernel launch of a call and after its last launch
