@@ -297,7 +297,7 @@ drgg_status drgg_plan(drgg_op op, int32_t E, int64_t M, int64_t N, int64_t K, dr
     std::memset(out, 0, sizeof *out);
     out->tile_m = p.ts.bm;
     out->tile_n = p.ts.bn;
-    out->tile_k = kTileK;
+    out->tile_k = kStageK;
     out->mfma_m = kMfmaM;
     out->mfma_n = kMfmaN;
     out->mfma_k = kMfmaK;

@@ -37,6 +37,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 #include "internal.hpp"
 #include "plan.hpp"
 
@@ -48,7 +50,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;       // fold / zero / router kernels
-constexpr int kGemmThreads = 512;   // grouped-GEMM kernels: 8 waves
+constexpr int kGemmWaves = 4;       // grouped-GEMM kernels: one wave per SIMD
+constexpr int kGemmThreads = 64 * kGemmWaves;
 
 // ---------------------------------------------------------------------------
 // small helpers
@@ -215,80 +218,169 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
 }
 constexpr uint32_t kOOB = 0xFFFFFFF0u;
 
-// LDS layouts of one 64-wide reduction step ("stage"):
-//   K-major:  ROWS rows of 64 reduction values (128 B = 8 chunks of 16 B);
-//             chunk c of row r sits at c ^ swzK(r).  The MFMA operand reads
-//             (16 lanes = 16 consecutive rows, one chunk) then hit 16
-//             distinct 16-byte bank groups.
-//   MN-major: 64 rows (reduction index) of ROWS output indices
-//             (ROWS*2 B = CPR chunks); chunk c of row r sits at
-//             c ^ swzMN(r).  The XOR is even, so the two chunks a group of
-//             four lanes reads stay adjacent, and the 16 row segments of one
-//             transposed read spread over all banks in two passes.
-__device__ __forceinline__ int swzK(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+// ---------------------------------------------------------------------------
+// main-loop pipeline
+//
+// The reduction runs in stages of kStageK = 32 values.  Each operand has
+// kStages = 4 LDS buffers; stage s lives in buffer s % 4.  A step computes
+// one stage in two MFMA sub-steps of 16 and is cut in half by the one
+// workgroup barrier of the step:
+//
+//   sub-step 0   MFMAs of sub-step 0 (fragments already in registers),
+//                LDS reads of the sub-step 1 fragments
+//   barrier      after this wave's loads of stage s+1 have landed and its
+//                LDS reads of stage s have returned
+//   sub-step 1   MFMAs of sub-step 1, LDS reads of the next stage's sub-step
+//                0 fragments, and the global loads of stage s+4 into the
+//                buffer stage s has just freed
+//
+// so a load has three steps between its issue and its first use, and the
+// MFMA pipe is fed from registers while the barrier and the next stage's
+// first reads resolve.  Global loads go straight from HBM to LDS (16-byte
+// buffer loads with an LDS destination), and the MFMAs, LDS reads and
+// global loads of a sub-step are interleaved one by one.
+//
+// The stage stream runs through consecutive tiles of a workgroup without a
+// break: the loads of the last three steps of a tile fetch the first stages
+// of the next tile.  Every tile runs a multiple of four steps (padding steps
+// compute nothing) so that each tile starts in buffer 0 and every buffer
+// index is a compile-time constant; the eight buffers are distinct
+// __shared__ arrays, so the compiler sees that a read of one buffer does not
+// alias the loads in flight into another and never waits for those.
+
+constexpr int kSubSteps = kStageK / kMfmaK;   // 2
+static_assert(kSubSteps == 2, "the step schedule assumes two MFMA sub-steps per stage");
+
+// s_waitcnt with vmcnt(N) and lgkmcnt(0) (expcnt left free).  GFX9 encoding:
+// vmcnt in bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm() {
+    static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// Wait until at most n of this wave's vector memory operations are pending
+// (n is one of 0, C, 2C, 3C) and all its LDS operations have returned.
+// Buffer loads return in issue order, so "at most n pending" means every
+// load issued before the last n has landed; stores in between only make the
+// wait stricter.
+template <int C>
+__device__ __forceinline__ void wait_loads(int n) {
+    if (n >= 3 * C) wait_vm_lgkm<3 * C>();
+    else if (n >= 2 * C) wait_vm_lgkm<2 * C>();
+    else if (n >= C) wait_vm_lgkm<C>();
+    else wait_vm_lgkm<0>();
+}
+
+// Workgroup barrier without a memory fence: the waits above are the only
+// synchronisation the pipeline needs, and a fence would drain every load in
+// flight.  The "memory" clobber keeps the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void barrier_nofence() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Scheduling groups (masks of __builtin_amdgcn_sched_group_barrier).
+constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100;
+
+// Interleave NM MFMAs with NR LDS reads and NL global loads of the same
+// region: after MFMA t come the reads and loads whose share falls on t.
+template <int NM, int NR, int NL, int T>
+__device__ __forceinline__ void sched_slot() {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    constexpr int r = NR * (T + 1) / NM - NR * T / NM;
+    constexpr int l = NL * (T + 1) / NM - NL * T / NM;
+    if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, r, 0);
+    if constexpr (l > 0) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, l, 0);
+}
+template <int NM, int NR, int NL, int... T>
+__device__ __forceinline__ void sched_interleave_impl(std::integer_sequence<int, T...>) {
+    (sched_slot<NM, NR, NL, T>(), ...);
+}
+template <int NM, int NR, int NL>
+__device__ __forceinline__ void sched_interleave() {
+    sched_interleave_impl<NM, NR, NL>(std::make_integer_sequence<int, NM>{});
+}
+
+// LDS layouts of one stage:
+//   K-major:  ROWS rows of 32 reduction values (64 B = 4 chunks of 16 B);
+//             chunk c of row r sits at c ^ swzK(r).  An MFMA operand read
+//             (16 lanes = 16 consecutive rows, one chunk) then covers all
+//             16 bank groups of 256 bytes.
+//   MN-major: 32 rows (reduction index) of ROWS output indices (ROWS*2 B =
+//             CPR chunks); chunk c of row r sits at c ^ swzMN(r).  The XOR is
+//             even, so the two chunks a group of four lanes reads stay
+//             adjacent, and the 16 row segments of one transposed read spread
+//             over all banks in two passes.
+__device__ __forceinline__ int swzK(int row) { return (row >> 2) & 3; }
 template <int CPR>
 __device__ __forceinline__ int swzMN(int row) {
     return (2 * ((row & 3) + 4 * ((row >> 3) & 1))) & (CPR - 2);
 }
 
-// Loads one stage of an operand straight from HBM into LDS with 16-byte
-// buffer loads (no registers in between).  A stage is ROWS*128 bytes =
-// ROWS/8 wave instructions of 1 KB; each of the 8 waves issues ROWS/64 of
-// them.  Lane l of instruction g writes LDS bytes [g*1024 + 16*l, +16); the
-// swizzle is applied by choosing which global chunk the lane fetches.
+// Loads one stage of an operand from HBM into LDS with 16-byte buffer loads
+// (no registers in between).  A stage is ROWS*64 bytes = ROWS/16 wave
+// instructions of 1 KB; each of the 4 waves issues ROWS/64 of them.  Lane l
+// of instruction g writes LDS bytes [g*1024 + 16*l, +16); the swizzle is
+// applied by choosing which global chunk the lane fetches.
 template <int ROWS, bool KMAJ>
-struct LdsLoader {
-    static constexpr int kPerWave = ROWS / 64;
-    static constexpr int kRowBytes = KMAJ ? 128 : ROWS * 2;
+struct StageLoader {
+    static constexpr int kPerWave = ROWS * kStageK * 2 / 1024 / kGemmWaves;
+    static constexpr int kRowBytes = KMAJ ? kStageK * 2 : ROWS * 2;
     static constexpr int kCPR = kRowBytes / 16;
     static_assert(ROWS % 64 == 0, "tile rows must be a multiple of 64");
-    uint32_t off[kPerWave];   // byte offset of this lane's 16 bytes from the step base (kOOB if masked)
-    int64_t step_bytes;       // byte distance between consecutive steps
+    uint32_t off[kPerWave];   // byte offset of this lane's 16 bytes from the stage base (kOOB if masked)
+    int32_t kp[kPerWave];     // reduction position of those 16 bytes within the stage
+    int64_t step_bytes;       // byte distance between consecutive stages
     const char* base;
     int32_t klen;
 
+    // this lane's (row, physical chunk) in the stage layout for instruction i
+    __device__ __forceinline__ static void slot(int i, int lane, int& row, int& phys) {
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const int b = (wave * kPerWave + i) * 1024 + lane * 16;
+        row = b / kRowBytes;
+        phys = (b % kRowBytes) / 16;
+    }
+
     __device__ __forceinline__ void init(const Operand& op) {
-        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        // opaque lane index: keeps the lane-dependent offset arithmetic here
+        // instead of hoisted (and held in registers) across the tile loop
+        int lane = threadIdx.x & 63;
+        asm volatile("" : "+v"(lane));
         base = reinterpret_cast<const char*>(op.base);
         klen = op.klen;
-        step_bytes = KMAJ ? 128 : 64 * op.ld * 2;
+        step_bytes = KMAJ ? kStageK * 2 : (int64_t)kStageK * op.ld * 2;
 #pragma unroll
         for (int i = 0; i < kPerWave; ++i) {
-            const int b = (wave * kPerWave + i) * 1024 + lane * 16;
-            const int row = b / kRowBytes, phys = (b % kRowBytes) / 16;
+            int row, phys;
+            slot(i, lane, row, phys);
             if constexpr (KMAJ) {
                 const int logical = phys ^ swzK(row);
                 off[i] = row < op.nvalid ? (uint32_t)(row * op.ld * 2 + logical * 16) : kOOB;
+                kp[i] = logical * 8;
             } else {
-                const int logical = phys ^ swzMN<kCPR>(row);
-                const int col = logical * 8;
+                const int col = (phys ^ swzMN<kCPR>(row)) * 8;
                 off[i] = col < op.nvalid ? (uint32_t)(row * op.ld * 2 + col * 2) : kOOB;
+                kp[i] = row;
             }
         }
     }
 
-    // reduction position, within a step, of the 16 bytes instruction i loads
-    __device__ __forceinline__ int kpos(int i) const {
-        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-        const int b = (wave * kPerWave + i) * 1024 + lane * 16;
-        const int row = b / kRowBytes, phys = (b % kRowBytes) / 16;
-        if constexpr (KMAJ) return (phys ^ swzK(row)) * 8;
-        else return row;
-    }
-
-    // Issue the loads of reduction step kt into `stage`.  With TAIL, positions
-    // at or past klen are masked.
-    template <bool TAIL>
-    __device__ __forceinline__ void issue(lds_t* stage, int kt) const {
-        const int wave = threadIdx.x >> 6;
-        const __amdgpu_buffer_rsrc_t r = make_rsrc(base + kt * step_bytes);
-        const int rem = klen - kt * 64;
+    // Issue the loads of stage L into `buf`; reduction positions at or past
+    // klen read as zero, and so does the whole stage when !valid (or when L
+    // lies past the last stage): such a load accesses no memory.
+    __device__ __forceinline__ void issue(lds_t* buf, int L, bool valid) const {
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(base + L * step_bytes);
+        const int rem = valid ? klen - L * kStageK : 0;
 #pragma unroll
         for (int i = 0; i < kPerWave; ++i) {
-            uint32_t o = off[i];
-            if constexpr (TAIL) o = kpos(i) < rem ? o : kOOB;
+            const uint32_t o = kp[i] < rem ? off[i] : kOOB;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                r, (lds_void_t*)(stage + (wave * kPerWave + i) * 1024), 16, o, 0, 0, 0);
+                r, (lds_void_t*)(buf + (wave * kPerWave + i) * 1024), 16, o, 0, 0, 0);
         }
     }
 };
@@ -296,12 +388,11 @@ struct LdsLoader {
 // MFMA operand fragment: lane l gets the 8 reduction values 16*s + 8*(l/32)
 // .. +7 of tile row rb + (l & 31).
 template <int ROWS, bool KMAJ>
-__device__ __forceinline__ bf16x8 read_frag(const lds_t* stage, int rb, int s) {
-    const int l = threadIdx.x & 63;
+__device__ __forceinline__ bf16x8 read_frag(const lds_t* buf, int rb, int s, int l) {
     if constexpr (KMAJ) {
         const int row = rb + (l & 31), c = 2 * s + (l >> 5);
         return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
-            stage + row * 128 + ((c ^ swzK(row)) << 4));
+            buf + row * (kStageK * 2) + ((c ^ swzK(row)) << 4));
     } else {
         // ds_read_b64_tr_b16: in a group of 16 lanes, lane 4j+q addresses
         // 4 values of row kbase+j at column col0+4q; lane i receives column
@@ -310,98 +401,16 @@ __device__ __forceinline__ bf16x8 read_frag(const lds_t* stage, int rb, int s) {
         const int g = l >> 4, j = (l >> 2) & 3, q = l & 3;
         const int col = rb + 16 * (g & 1) + 4 * q;
         const int chunk = col >> 3, within = (col & 7) * 2;
-        const int k0 = 16 * s + 8 * (g >> 1) + j;
-        const int r0 = k0, r1 = k0 + 4;
+        const int r0 = 16 * s + 8 * (g >> 1) + j, r1 = r0 + 4;
         typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
         v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_v4i16*)(stage + r0 * ROWS * 2 + ((chunk ^ swzMN<CPR>(r0)) << 4) + within));
+            (lds_v4i16*)(buf + r0 * ROWS * 2 + ((chunk ^ swzMN<CPR>(r0)) << 4) + within));
         v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_v4i16*)(stage + r1 * ROWS * 2 + ((chunk ^ swzMN<CPR>(r1)) << 4) + within));
+            (lds_v4i16*)(buf + r1 * ROWS * 2 + ((chunk ^ swzMN<CPR>(r1)) << 4) + within));
         v8i16 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         return __builtin_bit_cast(bf16x8, v);
     }
 }
-
-// One BMxBN output tile on 8 waves: the waves form a 2x4 grid, each owning a
-// (BM/2)x(BN/4) block of 32x32 MFMA tiles whose accumulators stay in
-// registers.  Two LDS stages alternate: after the barrier that ends step
-// kt-1, the loads of step kt+1 go out into the free stage while the MFMAs
-// consume step kt.
-template <int BM, int BN, bool AK, bool BK>
-struct TileMma {
-    static constexpr int WM = BM / 2, WN = BN / 4;
-    static constexpr int kBI = WM / 32, kBJ = WN / 32;
-    static constexpr int kStageA = BM * 128, kStageB = BN * 128;
-    static constexpr int kLdsBytes = 2 * (kStageA + kStageB);
-    static_assert(kBI >= 1 && kBJ >= 1, "tile too small for the 2x4 wave grid");
-    f32x16 acc[kBI][kBJ];
-
-    __device__ __forceinline__ void zero() {
-#pragma unroll
-        for (int i = 0; i < kBI; ++i)
-#pragma unroll
-            for (int j = 0; j < kBJ; ++j)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    }
-
-    __device__ __forceinline__ void compute(const lds_t* sA, const lds_t* sB) {
-        const int wave = threadIdx.x >> 6;
-        const int ra = (wave >> 2) * WM, rb = (wave & 3) * WN;
-        bf16x8 a[2][kBI], b[2][kBJ];
-#pragma unroll
-        for (int i = 0; i < kBI; ++i) a[0][i] = read_frag<BM, AK>(sA, ra + 32 * i, 0);
-#pragma unroll
-        for (int j = 0; j < kBJ; ++j) b[0][j] = read_frag<BN, BK>(sB, rb + 32 * j, 0);
-        // The scheduling fences keep this order: the operand reads of step
-        // s+1 are issued before the MFMAs of step s, so their LDS latency
-        // hides behind those MFMAs instead of stalling each MFMA pair.
-#pragma unroll
-        for (int s = 0; s < kTileK / kMfmaK; ++s) {
-            const int cur = s & 1;
-            if (s + 1 < kTileK / kMfmaK) {
-#pragma unroll
-                for (int i = 0; i < kBI; ++i) a[cur ^ 1][i] = read_frag<BM, AK>(sA, ra + 32 * i, s + 1);
-#pragma unroll
-                for (int j = 0; j < kBJ; ++j) b[cur ^ 1][j] = read_frag<BN, BK>(sB, rb + 32 * j, s + 1);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int i = 0; i < kBI; ++i)
-#pragma unroll
-                for (int j = 0; j < kBJ; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][i], b[cur][j], acc[i][j], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-
-    // Visit every accumulator element: f(row, col, value) with (row, col)
-    // inside the tile.  For a fixed register, lanes 0..31 hold 32 consecutive
-    // columns of one row, so stores from here are 64- or 128-byte runs.
-    template <class F>
-    __device__ __forceinline__ void for_each(F f) const {
-        int lane = threadIdx.x & 63;
-        // The (row, col) of each register does not depend on the tile; an
-        // opaque copy of the lane index keeps the compiler from hoisting all
-        // of them out of the persistent tile loop, where they would occupy
-        // registers for its whole length.
-        asm volatile("" : "+v"(lane));
-        const int wave = threadIdx.x >> 6;
-        const int ra = (wave >> 2) * WM, rb = (wave & 3) * WN;
-#pragma unroll
-        for (int i = 0; i < kBI; ++i)
-#pragma unroll
-            for (int j = 0; j < kBJ; ++j) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    f(ra + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3), rb + 32 * j + (lane & 31),
-                      acc[i][j][r]);
-                // one block at a time: keeps the store addresses of the
-                // other blocks from occupying registers
-                __builtin_amdgcn_sched_barrier(0);
-            }
-    }
-};
 
 // One tile of work for the persistent driver: the two operand views and the
 // kernel's own output coordinates.
@@ -412,72 +421,255 @@ struct TileInfo {
     int32_t e, aux, aux2;  // expert and kernel-specific tags
 };
 
-// Persistent tile loop.  `more()` tells whether this workgroup has another
-// tile and `next(t)` decodes it; `finish(t, mma)` writes a finished tile from
-// the accumulators.  Reduction steps of consecutive tiles form one stream
-// over the two LDS stages: during the last step of a tile the first step of
-// the next tile is already loading, so neither the pipeline fill nor the
-// epilogue of a tile is exposed.  The next tile is decoded only at that last
-// step, so its description does not occupy registers during the loop.  Must
-// be called by all threads.
-template <int BM, int BN, bool AK, bool BK, class More, class Next, class Finish>
-__device__ __forceinline__ void run_tiles(lds_t* lds, More more, Next next, Finish finish) {
-    using Mma = TileMma<BM, BN, AK, BK>;
-    Mma mma;
-    LdsLoader<BM, AK> la;
-    LdsLoader<BN, BK> lb;
-    lds_t* const sA0 = lds;
-    lds_t* const sB0 = lds + 2 * Mma::kStageA;
-    if (!more()) return;
-    TileInfo cur;
-    next(cur);
-    la.init(cur.A);
-    lb.init(cur.B);
-    int stage = 0;
-    if (cur.A.klen >= kTileK) {
-        la.template issue<false>(sA0, 0);
-        lb.template issue<false>(sB0, 0);
-    } else {
-        la.template issue<true>(sA0, 0);
-        lb.template issue<true>(sB0, 0);
+// The LDS buffers of a kernel: kStages per operand, each a distinct
+// __shared__ array (see above).
+struct Stages {
+    lds_t* a[kStages];
+    lds_t* b[kStages];
+};
+
+#define DRGG_STAGES(BM, BN, name)                                                              \
+    __shared__ __attribute__((aligned(1024))) char name##_a0[(BM) * kStageK * 2];              \
+    __shared__ __attribute__((aligned(1024))) char name##_a1[(BM) * kStageK * 2];              \
+    __shared__ __attribute__((aligned(1024))) char name##_a2[(BM) * kStageK * 2];              \
+    __shared__ __attribute__((aligned(1024))) char name##_a3[(BM) * kStageK * 2];              \
+    __shared__ __attribute__((aligned(1024))) char name##_b0[(BN) * kStageK * 2];              \
+    __shared__ __attribute__((aligned(1024))) char name##_b1[(BN) * kStageK * 2];              \
+    __shared__ __attribute__((aligned(1024))) char name##_b2[(BN) * kStageK * 2];              \
+    __shared__ __attribute__((aligned(1024))) char name##_b3[(BN) * kStageK * 2];              \
+    const Stages name{{(lds_t*)name##_a0, (lds_t*)name##_a1, (lds_t*)name##_a2, (lds_t*)name##_a3}, \
+                      {(lds_t*)name##_b0, (lds_t*)name##_b1, (lds_t*)name##_b2, (lds_t*)name##_b3}}
+
+// The accumulators and operand fragments of one BMxBN tile on 4 waves (one
+// per SIMD): the waves form a 2x2 grid, each owning a (BM/2)x(BN/2) block of
+// 32x32 MFMA tiles whose FP32 accumulators stay in registers (AGPRs for the
+// 256x256 tile).  The MFMA takes the B-side fragment as its first operand,
+// so that the accumulator of lane l holds tile row l%32 and, in registers
+// 4q..4q+3, four consecutive tile columns 8q + 4*(l/32) .. +3: a lane's
+// outputs leave as 8- or 16-byte stores.
+template <int BM, int BN, bool AK, bool BK>
+struct TileMma {
+    static constexpr int WM = BM / 2, WN = BN / 2;
+    static constexpr int kBI = WM / 32, kBJ = WN / 32;
+    static_assert(kBI >= 1 && kBJ >= 1, "tile too small for the 2x2 wave grid");
+    // LDS reads per sub-step: one per 32-row block (K-major), two (MN-major)
+    static constexpr int kReads = kBI * (AK ? 1 : 2) + kBJ * (BK ? 1 : 2);
+    static constexpr int kMfmas = kBI * kBJ;
+    f32x16 acc[kBI][kBJ];
+    bf16x8 fa[2][kBI], fb[2][kBJ];   // fragments of sub-step 0 and 1
+
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int i = 0; i < kBI; ++i)
+#pragma unroll
+            for (int j = 0; j < kBJ; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
     }
-    for (;;) {
-        const int nk = (cur.A.klen + kTileK - 1) / kTileK;   // >= 1
-        const int nfull = cur.A.klen / kTileK;
-        const bool has_next = more();
-        TileInfo nxt;
-        mma.zero();
-        for (int kt = 0; kt < nk; ++kt) {
-            __builtin_amdgcn_s_waitcnt(0);   // this lane's loads of step kt have landed
-            __syncthreads();                 // everyone's; and the other stage is free
-            lds_t* const nA = sA0 + (stage ^ 1) * Mma::kStageA;
-            lds_t* const nB = sB0 + (stage ^ 1) * Mma::kStageB;
-            if (kt + 1 < nfull) {
-                la.template issue<false>(nA, kt + 1);
-                lb.template issue<false>(nB, kt + 1);
-            } else if (kt + 1 < nk) {
-                la.template issue<true>(nA, kt + 1);
-                lb.template issue<true>(nB, kt + 1);
-            } else if (has_next) {
-                next(nxt);
-                la.init(nxt.A);
-                lb.init(nxt.B);
-                if (nxt.A.klen >= kTileK) {
-                    la.template issue<false>(nA, 0);
-                    lb.template issue<false>(nB, 0);
+
+    // fragments of sub-step s of the stage in (sA, sB) into set F
+    template <int F>
+    __device__ __forceinline__ void read(const lds_t* sA, const lds_t* sB, int s) {
+        const int l = threadIdx.x & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const int ra = (wave >> 1) * WM, rb = (wave & 1) * WN;
+        // in the order the MFMAs consume them
+        fa[F][0] = read_frag<BM, AK>(sA, ra, s, l);
+#pragma unroll
+        for (int j = 0; j < kBJ; ++j) fb[F][j] = read_frag<BN, BK>(sB, rb + 32 * j, s, l);
+#pragma unroll
+        for (int i = 1; i < kBI; ++i) fa[F][i] = read_frag<BM, AK>(sA, ra + 32 * i, s, l);
+    }
+
+    template <int F>
+    __device__ __forceinline__ void mfma() {
+#pragma unroll
+        for (int i = 0; i < kBI; ++i)
+#pragma unroll
+            for (int j = 0; j < kBJ; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[F][j], fa[F][i], acc[i][j], 0, 0, 0);
+    }
+};
+
+// Write a finished tile: out[row * ld + col] = tile[row][col] rounded once to
+// the output type, for row < rows and col < cols (cols a multiple of 4).
+// Each lane stores its four consecutive columns as one 8- or 16-byte buffer
+// store; lanes outside the valid region get an out-of-range offset, and
+// their stores are dropped by the hardware range check, so the epilogue has
+// no branches.  Each 32-row block gets its own descriptor, which keeps the
+// per-lane offsets below 2^31 for ld <= 2^22.
+template <bool OUT_BF16, class Mma>
+__device__ __forceinline__ void store_tile(const Mma& mma, void* out, int64_t ld, int rows, int cols) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    constexpr int ES = OUT_BF16 ? 2 : 4;
+    // opaque lane index: the offsets do not depend on the tile and would
+    // otherwise be hoisted out of the tile loop and held in registers
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int ra = (wave >> 1) * Mma::WM, rb = (wave & 1) * Mma::WN;
+    const int r = lane & 31;
+#pragma unroll
+    for (int i = 0; i < Mma::kBI; ++i) {
+        const int r0 = ra + 32 * i;
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(reinterpret_cast<char*>(out) + (int64_t)r0 * ld * ES);
+        const bool rok = r0 + r < rows;
+#pragma unroll
+        for (int j = 0; j < Mma::kBJ; ++j) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int c = rb + 32 * j + 8 * q + 4 * (lane >> 5);
+                const uint32_t o = rok && c < cols ? (uint32_t)((r * ld + c) * ES) : kOOB;
+                const f32x16& a = mma.acc[i][j];
+                if constexpr (OUT_BF16) {
+                    const bf16x2 lo = __builtin_convertvector((f32x2{a[4 * q], a[4 * q + 1]}), bf16x2);
+                    const bf16x2 hi = __builtin_convertvector((f32x2{a[4 * q + 2], a[4 * q + 3]}), bf16x2);
+                    const u32x2 d = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+                    __builtin_amdgcn_raw_buffer_store_b64(d, rs, o, 0, 0);
                 } else {
-                    la.template issue<true>(nA, 0);
-                    lb.template issue<true>(nB, 0);
+                    const u32x4 d = {__float_as_uint(a[4 * q]), __float_as_uint(a[4 * q + 1]),
+                                     __float_as_uint(a[4 * q + 2]), __float_as_uint(a[4 * q + 3])};
+                    __builtin_amdgcn_raw_buffer_store_b128(d, rs, o, 0, 0);
                 }
             }
-            mma.compute(sA0 + stage * Mma::kStageA, sB0 + stage * Mma::kStageB);
-            stage ^= 1;
+            __builtin_amdgcn_sched_barrier(0);
         }
-        finish(cur, mma);
-        if (!has_next) break;
-        cur = nxt;
     }
 }
+
+// Add a finished tile into an FP32 tile buffer: ts[row * ld + col] +=
+// tile[row][col] for row < rows, col < cols, with device-coherent atomic
+// adds (performed in L2).  Masked lanes use an out-of-range offset, as in
+// store_tile.
+template <class Mma>
+__device__ __forceinline__ void atomic_add_tile(const Mma& mma, float* ts, int ld, int rows, int cols) {
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int ra = (wave >> 1) * Mma::WM, rb = (wave & 1) * Mma::WN;
+    const int r = ra + (lane & 31);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(ts);
+#pragma unroll
+    for (int i = 0; i < Mma::kBI; ++i) {
+        const bool rok = r + 32 * i < rows;
+#pragma unroll
+        for (int j = 0; j < Mma::kBJ; ++j) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int c = rb + 32 * j + 8 * q + 4 * (lane >> 5);
+                const uint32_t o = rok && c < cols ? (uint32_t)(((r + 32 * i) * ld + c) * 4) : kOOB;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(mma.acc[i][j][4 * q + e], rs,
+                                                                     o == kOOB ? kOOB : o + 4 * e, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+// Persistent tile loop over the stage pipeline.  `more()` tells whether this
+// workgroup has another tile and `next(t)` decodes it; `finish(t, mma)`
+// writes a finished tile from the accumulators.  Every step has the same
+// shape: each one issues one stage of loads and runs both MFMA sub-steps.
+// Stages past the end of a tile (the padding up to a multiple of four, or
+// past the last tile) are "loaded" with every lane masked, which writes
+// zeros to LDS without touching memory, so the MFMAs of a padding step add
+// zeros and no branch is taken around the accumulators.  The next tile is
+// decoded at the start of step nk4-4, whose loads fetch its first stage.
+// Must be called by all threads.
+template <int BM, int BN, bool AK, bool BK>
+struct TileRunner {
+    using Mma = TileMma<BM, BN, AK, BK>;
+    using LA = StageLoader<BM, AK>;
+    using LB = StageLoader<BN, BK>;
+    static constexpr int C = LA::kPerWave + LB::kPerWave;   // loads per wave per stage
+    Mma mma;
+    LA la;
+    LB lb;
+    Stages st;
+    TileInfo cur, nxt;
+    int nk, nk4, nk_nxt;
+    bool has_next;
+
+    static __device__ __forceinline__ int stages_of(const TileInfo& t) {
+        return (t.A.klen + kStageK - 1) / kStageK;
+    }
+
+    // Step kt of the current tile; ST = kt % 4 is its buffer.
+    template <int ST, class Next>
+    __device__ __forceinline__ void step(int kt, Next& next) {
+        constexpr int NX = (ST + 1) % kStages;
+        if (kt + kStages == nk4 && has_next) {
+            next(nxt);
+            nk_nxt = stages_of(nxt);
+            la.init(nxt.A);
+            lb.init(nxt.B);
+        }
+        // the stage this step loads: kt+4 of this tile, or of the next tile
+        // once past nk4 (the loaders then point at the next tile)
+        const int L = kt + kStages;
+        const int Ls = L < nk4 ? L : L - nk4;
+        const bool valid = L < nk4 || has_next;
+        __builtin_amdgcn_sched_barrier(0);
+        // sub-step 0: its MFMAs; the sub-step 1 fragments
+        mma.template read<1>(st.a[ST], st.b[ST], 1);
+        mma.template mfma<0>();
+        sched_interleave<Mma::kMfmas, Mma::kReads, 0>();
+        __builtin_amdgcn_sched_barrier(0);
+        // stage kt+1 has landed for every wave (the loads of kt+2 and kt+3
+        // may still be in flight), and every wave is done reading stage kt
+        wait_vm_lgkm<2 * C>();
+        barrier_nofence();
+        // sub-step 1: its MFMAs; stage kt+4 into the freed buffer; the
+        // sub-step 0 fragments of stage kt+1
+        la.issue(st.a[ST], Ls, valid);
+        lb.issue(st.b[ST], Ls, valid);
+        mma.template read<0>(st.a[NX], st.b[NX], 0);
+        mma.template mfma<1>();
+        sched_interleave<Mma::kMfmas, Mma::kReads, C>();
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    template <class More, class Next, class Finish>
+    __device__ __forceinline__ void run(More more, Next next, Finish finish) {
+        if (!more()) return;
+        next(cur);
+        nk = stages_of(cur);
+        nk4 = (nk + kStages - 1) & ~(kStages - 1);
+        la.init(cur.A);
+        lb.init(cur.B);
+        // prologue: the first four stages (zeros past nk), then stage 0
+#pragma unroll
+        for (int X = 0; X < kStages; ++X) {
+            la.issue(st.a[X], X, true);
+            lb.issue(st.b[X], X, true);
+        }
+        wait_vm_lgkm<3 * C>();
+        barrier_nofence();
+        mma.template read<0>(st.a[0], st.b[0], 0);
+        for (;;) {
+            has_next = more();
+            nk_nxt = 0;
+            mma.zero();
+            for (int kt = 0; kt < nk4; kt += kStages) {
+                step<0>(kt, next);
+                step<1>(kt + 1, next);
+                step<2>(kt + 2, next);
+                step<3>(kt + 3, next);
+            }
+            finish(cur, mma);
+            if (!has_next) break;
+            cur = nxt;
+            nk = nk_nxt;
+            nk4 = (nk + kStages - 1) & ~(kStages - 1);
+        }
+        // the masked loads past the last tile are still in flight
+        __builtin_amdgcn_s_waitcnt(0);
+    }
+};
 
 template <bool OUT_BF16>
 __device__ __forceinline__ void store1(void* out, int64_t idx, float v) {
@@ -508,7 +700,7 @@ __device__ __forceinline__ void store4(void* out, int64_t idx, f32x4 v) {
 
 template <int OP, int BM, int BN, bool OUT_BF16>
 __global__ __launch_bounds__(kGemmThreads) void gg_fwd_dgrad_kernel(GemmArgs a) {
-    __shared__ __attribute__((aligned(1024))) char lds[TileMma<BM, BN, true, OP == 0>::kLdsBytes];
+    DRGG_STAGES(BM, BN, stg);
     __shared__ Sched sch;
     // output columns: N (forward) or K (data gradient)
     const int64_t ncols = OP == 0 ? a.N : a.K;
@@ -544,11 +736,13 @@ __global__ __launch_bounds__(kGemmThreads) void gg_fwd_dgrad_kernel(GemmArgs a) 
     };
     void* out = a.out;
     auto finish = [&](const TileInfo& t, const TileMma<BM, BN, true, OP == 0>& mma) {
-        mma.for_each([&](int r, int c, float v) {
-            if (r < t.rows && c < t.cols) store1<OUT_BF16>(out, (t.o0 + r) * ncols + t.o1 + c, v);
-        });
+        void* base = OUT_BF16 ? (void*)(reinterpret_cast<uint16_t*>(out) + t.o0 * ncols + t.o1)
+                              : (void*)(reinterpret_cast<float*>(out) + t.o0 * ncols + t.o1);
+        store_tile<OUT_BF16>(mma, base, ncols, t.rows, t.cols);
     };
-    run_tiles<BM, BN, true, OP == 0>((lds_t*)lds, more, next, finish);
+    TileRunner<BM, BN, true, OP == 0> runner;
+    runner.st = stg;
+    runner.run(more, next, finish);
 }
 
 // ---------------------------------------------------------------------------
@@ -556,7 +750,7 @@ __global__ __launch_bounds__(kGemmThreads) void gg_fwd_dgrad_kernel(GemmArgs a) 
 
 template <int BM, int BN, bool OUT_BF16>
 __global__ __launch_bounds__(kGemmThreads) void gg_wgrad_det_kernel(GemmArgs a) {
-    __shared__ __attribute__((aligned(1024))) char lds[TileMma<BM, BN, false, false>::kLdsBytes];
+    DRGG_STAGES(BM, BN, stg);
     __shared__ Sched sch;
     __shared__ int32_t slot_base[kMaxExperts + 1];
     const int32_t tn = (int32_t)((a.N + BM - 1) / BM), tk = (int32_t)((a.K + BN - 1) / BN);
@@ -604,20 +798,20 @@ __global__ __launch_bounds__(kGemmThreads) void gg_wgrad_det_kernel(GemmArgs a) 
         w += G;
     };
     auto finish = [&](const TileInfo& t, const TileMma<BM, BN, false, false>& mma) {
-        if (t.aux < 0) {
-            void* out = a.out;
-            const int64_t base = (int64_t)t.e * a.N * a.K + t.o0 * a.K + t.o1;
-            mma.for_each([&](int r, int c, float v) {
-                if (r < t.rows && c < t.cols) store1<OUT_BF16>(out, base + r * a.K + c, v);
-            });
-        } else {
+        const int64_t ld = a.K;
+        if (t.aux < 0) {   // one chunk: round and store the output directly
+            const int64_t off = (int64_t)t.e * a.N * a.K + t.o0 * a.K + t.o1;
+            void* base = OUT_BF16 ? (void*)(reinterpret_cast<uint16_t*>(a.out) + off)
+                                  : (void*)(reinterpret_cast<float*>(a.out) + off);
+            store_tile<OUT_BF16>(mma, base, ld, t.rows, t.cols);
+        } else {           // a chunk partial of an expert cut into several chunks
             float* dst = a.partial + (int64_t)t.aux * a.N * a.K + t.o0 * a.K + t.o1;
-            mma.for_each([&](int r, int c, float v) {
-                if (r < t.rows && c < t.cols) dst[r * a.K + c] = v;
-            });
+            store_tile<false>(mma, dst, ld, t.rows, t.cols);
         }
     };
-    run_tiles<BM, BN, false, false>((lds_t*)lds, more, next, finish);
+    TileRunner<BM, BN, false, false> runner;
+    runner.st = stg;
+    runner.run(more, next, finish);
 }
 
 // Fold the partials of every expert cut into more than one chunk, in chunk
@@ -691,7 +885,7 @@ __global__ __launch_bounds__(kThreads) void gg_wgrad_fold_kernel(GemmArgs a) {
 
 template <int BM, int BN, bool OUT_BF16>
 __global__ __launch_bounds__(kGemmThreads) void gg_wgrad_streamk_kernel(GemmArgs a) {
-    __shared__ __attribute__((aligned(1024))) char lds[TileMma<BM, BN, false, false>::kLdsBytes];
+    DRGG_STAGES(BM, BN, stg);
     __shared__ Sched sch;
     __shared__ int32_t s_last;
     const int32_t tn = (int32_t)((a.N + BM - 1) / BM), tk = (int32_t)((a.K + BN - 1) / BN);
@@ -741,17 +935,14 @@ __global__ __launch_bounds__(kGemmThreads) void gg_wgrad_streamk_kernel(GemmArgs
         const int64_t base = (int64_t)t.e * a.N * a.K + t.o0 * a.K + t.o1;
         void* out = a.out;
         if (t.aux < 0) {   // the whole tile in this workgroup: store directly
-            mma.for_each([&](int r, int c, float v) {
-                if (r < t.rows && c < t.cols) store1<OUT_BF16>(out, base + r * a.K + c, v);
-            });
+            void* ob = OUT_BF16 ? (void*)(reinterpret_cast<uint16_t*>(out) + base)
+                                : (void*)(reinterpret_cast<float*>(out) + base);
+            store_tile<OUT_BF16>(mma, ob, a.K, t.rows, t.cols);
             return;
         }
         const int64_t slot = (int64_t)t.e * P + t.aux;
         float* ts = a.tilesum + slot * (BM * BN);
-        mma.for_each([&](int r, int c, float v) {
-            if (r < t.rows && c < t.cols)
-                __hip_atomic_fetch_add(ts + r * BN + c, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        });
+        atomic_add_tile(mma, ts, BN, t.rows, t.cols);
         __threadfence();
         __syncthreads();
         if (threadIdx.x == 0) {
@@ -779,7 +970,9 @@ __global__ __launch_bounds__(kGemmThreads) void gg_wgrad_streamk_kernel(GemmArgs
         }
         __syncthreads();
     };
-    run_tiles<BM, BN, false, false>((lds_t*)lds, more, next, finish);
+    TileRunner<BM, BN, false, false> runner;
+    runner.st = stg;
+    runner.run(more, next, finish);
     // experts without tokens: dW[e] = +0, shared out over the grid
     const int64_t nk = a.N * a.K;
     for (int e = 0; e < a.E; ++e) {

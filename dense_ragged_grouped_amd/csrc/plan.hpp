@@ -9,12 +9,20 @@
 
 namespace drgg {
 
-// Reduction step of every main loop and the MFMA shape every program uses:
-// v_mfma_f32_32x32x16_bf16 (32x32 output block, 16 reduction values per
-// instruction).  One fixed instruction and step per program keeps each output
-// element's accumulation order independent of the tile shape.
-constexpr int kTileK = 64;
+// The MFMA shape every program uses: v_mfma_f32_32x32x16_bf16 (32x32 output
+// block, 16 reduction values per instruction).  Each output element is
+// accumulated by one chain of these instructions in reduction order, so its
+// value does not depend on the tile shape or the pipeline depth.
 constexpr int kMfmaM = 32, kMfmaN = 32, kMfmaK = 16;
+
+// Grouped-GEMM main loop: LDS stages of kStageK reduction values, kStages
+// buffers per operand.
+constexpr int kStageK = 32;
+constexpr int kStages = 4;
+
+// Token alignment of the deterministic weight gradient's chunks (and the
+// reduction step of the router kernel).
+constexpr int kTileK = 64;
 
 // Token unit of the non-deterministic (stream-K) weight gradient: the K range
 // of a split tile is handed out in 512-token units (flashinfer PR #8258,
@@ -92,10 +100,10 @@ inline int64_t wgrad_max_partials(int64_t M, int64_t chunk_max) {
 }
 
 // Workgroups of a persistent grouped-GEMM kernel that fit on one CU (LDS:
-// two stages of (BM + BN) x 64 BF16 plus about 11 KB of schedule tables, out
-// of 160 KB).
+// kStages stages of (BM + BN) x kStageK BF16 plus at most 14 KB of schedule
+// tables, out of 160 KB; each workgroup has 4 waves).
 inline int64_t wgs_per_cu(TileShape t) {
-    const int64_t lds = 2 * (int64_t)(t.bm + t.bn) * 128 + 11 * 1024;
+    const int64_t lds = (int64_t)kStages * (t.bm + t.bn) * kStageK * 2 + 14 * 1024;
     const int64_t n = (160 * 1024) / lds;
     return n < 1 ? 1 : n;
 }
