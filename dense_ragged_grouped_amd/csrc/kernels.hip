@@ -259,19 +259,6 @@ __device__ __forceinline__ void wait_vm_lgkm() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
 }
 
-// Wait until at most n of this wave's vector memory operations are pending
-// (n is one of 0, C, 2C, 3C) and all its LDS operations have returned.
-// Buffer loads return in issue order, so "at most n pending" means every
-// load issued before the last n has landed; stores in between only make the
-// wait stricter.
-template <int C>
-__device__ __forceinline__ void wait_loads(int n) {
-    if (n >= 3 * C) wait_vm_lgkm<3 * C>();
-    else if (n >= 2 * C) wait_vm_lgkm<2 * C>();
-    else if (n >= C) wait_vm_lgkm<C>();
-    else wait_vm_lgkm<0>();
-}
-
 // Workgroup barrier without a memory fence: the waits above are the only
 // synchronisation the pipeline needs, and a fence would drain every load in
 // flight.  The "memory" clobber keeps the compiler from moving memory
@@ -304,59 +291,65 @@ __device__ __forceinline__ void sched_interleave() {
     sched_interleave_impl<NM, NR, NL>(std::make_integer_sequence<int, NM>{});
 }
 
-// LDS layouts of one stage:
-//   K-major:  ROWS rows of 32 reduction values (64 B = 4 chunks of 16 B);
-//             chunk c of row r sits at c ^ swzK(r).  An MFMA operand read
-//             (16 lanes = 16 consecutive rows, one chunk) then covers all
-//             16 bank groups of 256 bytes.
-//   MN-major: 32 rows (reduction index) of ROWS output indices (ROWS*2 B =
-//             CPR chunks); chunk c of row r sits at c ^ swzMN(r).  The XOR is
-//             even, so the two chunks a group of four lanes reads stay
-//             adjacent, and the 16 row segments of one transposed read spread
-//             over all banks in two passes.
-__device__ __forceinline__ int swzK(int row) { return (row >> 2) & 3; }
+// LDS layouts:
+//   K-major operands (reduction index contiguous in memory) are staged in
+//   pairs of stages: a pair buffer holds ROWS rows of 64 reduction values
+//   (128 B = 8 chunks of 16 B), stage 2p in the first four chunks of each
+//   row and stage 2p+1 in the last four.  Loading a pair moves whole 128-byte
+//   lines (a 32-value stage alone would be half a line per row, twice the
+//   memory requests and address translations per byte).  Chunk c of row r
+//   sits at c ^ swzK(r), which puts the 16 rows an MFMA operand read covers
+//   per pass (one chunk each) on 16 distinct 16-byte bank groups, and any 8
+//   consecutive rows on 8.
+//   MN-major operands: one buffer per stage, 32 rows (reduction index) of
+//   ROWS output indices (ROWS*2 B = CPR chunks), already whole lines in
+//   memory; chunk c of row r sits at c ^ swzMN(r).  A transposed read has
+//   each group of 32 lanes read 4 rows at the same 4 chunks (c0 .. c0+3, c0
+//   a multiple of 4), each group of 16 lanes 2 of those chunks.  The XOR
+//   values 0, 10, 12, 6 for r % 4 = 0..3 send the 4 rows to 4 different
+//   64-byte bank groups of a 256-byte window (bits 2-3 of the chunk index
+//   all differ) and, for the 16-lane halves, to 4 different 32-byte groups of
+//   a 128-byte window (bits 1-2 all differ): no bank conflicts with either
+//   32 or 64 banks.
+__device__ __forceinline__ int swzK(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 template <int CPR>
 __device__ __forceinline__ int swzMN(int row) {
-    return (2 * ((row & 3) + 4 * ((row >> 3) & 1))) & (CPR - 2);
+    return ((0x6CA0 >> (4 * (row & 3))) & 15) & (CPR - 1);
 }
 
-// Loads one stage of an operand from HBM into LDS with 16-byte buffer loads
-// (no registers in between).  A stage is ROWS*64 bytes = ROWS/16 wave
-// instructions of 1 KB; each of the 4 waves issues ROWS/64 of them.  Lane l
-// of instruction g writes LDS bytes [g*1024 + 16*l, +16); the swizzle is
-// applied by choosing which global chunk the lane fetches.
+// Loads stages of an operand from HBM into LDS with 16-byte buffer loads (no
+// registers in between): a K-major operand two stages (one pair buffer) at a
+// time, an MN-major operand one stage at a time.  Either way one load is
+// ROWS*64*SPAN bytes = ROWS*SPAN/16 wave instructions of 1 KB, of which each
+// of the 4 waves issues a quarter.  Lane l of instruction g writes LDS bytes
+// [g*1024 + 16*l, +16); the swizzle is applied by choosing which global
+// chunk the lane fetches.
 template <int ROWS, bool KMAJ>
 struct StageLoader {
-    static constexpr int kPerWave = ROWS * kStageK * 2 / 1024 / kGemmWaves;
-    static constexpr int kRowBytes = KMAJ ? kStageK * 2 : ROWS * 2;
+    static constexpr int kSpan = KMAJ ? 2 : 1;   // stages per load
+    static constexpr int kPerWave = ROWS * kStageK * 2 * kSpan / 1024 / kGemmWaves;
+    static constexpr int kRowBytes = KMAJ ? 2 * kStageK * 2 : ROWS * 2;
     static constexpr int kCPR = kRowBytes / 16;
     static_assert(ROWS % 64 == 0, "tile rows must be a multiple of 64");
-    uint32_t off[kPerWave];   // byte offset of this lane's 16 bytes from the stage base (kOOB if masked)
-    int32_t kp[kPerWave];     // reduction position of those 16 bytes within the stage
+    uint32_t off[kPerWave];   // byte offset of this lane's 16 bytes from the load base (kOOB if masked)
+    int32_t kp[kPerWave];     // reduction position of those 16 bytes from the first stage loaded
     int64_t step_bytes;       // byte distance between consecutive stages
     const char* base;
     int32_t klen;
-
-    // this lane's (row, physical chunk) in the stage layout for instruction i
-    __device__ __forceinline__ static void slot(int i, int lane, int& row, int& phys) {
-        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-        const int b = (wave * kPerWave + i) * 1024 + lane * 16;
-        row = b / kRowBytes;
-        phys = (b % kRowBytes) / 16;
-    }
 
     __device__ __forceinline__ void init(const Operand& op) {
         // opaque lane index: keeps the lane-dependent offset arithmetic here
         // instead of hoisted (and held in registers) across the tile loop
         int lane = threadIdx.x & 63;
         asm volatile("" : "+v"(lane));
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         base = reinterpret_cast<const char*>(op.base);
         klen = op.klen;
         step_bytes = KMAJ ? kStageK * 2 : (int64_t)kStageK * op.ld * 2;
 #pragma unroll
         for (int i = 0; i < kPerWave; ++i) {
-            int row, phys;
-            slot(i, lane, row, phys);
+            const int b = (wave * kPerWave + i) * 1024 + lane * 16;
+            const int row = b / kRowBytes, phys = (b % kRowBytes) / 16;
             if constexpr (KMAJ) {
                 const int logical = phys ^ swzK(row);
                 off[i] = row < op.nvalid ? (uint32_t)(row * op.ld * 2 + logical * 16) : kOOB;
@@ -369,9 +362,10 @@ struct StageLoader {
         }
     }
 
-    // Issue the loads of stage L into `buf`; reduction positions at or past
-    // klen read as zero, and so does the whole stage when !valid (or when L
-    // lies past the last stage): such a load accesses no memory.
+    // Issue the load of stage L (stages L, L+1 for a K-major operand) into
+    // `buf`; reduction positions at or past klen read as zero, and so does
+    // everything when !valid (or when L lies past the last stage): such a
+    // load accesses no memory.
     __device__ __forceinline__ void issue(lds_t* buf, int L, bool valid) const {
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         const __amdgpu_buffer_rsrc_t r = make_rsrc(base + L * step_bytes);
@@ -386,13 +380,14 @@ struct StageLoader {
 };
 
 // MFMA operand fragment: lane l gets the 8 reduction values 16*s + 8*(l/32)
-// .. +7 of tile row rb + (l & 31).
+// .. +7 of tile row rb + (l & 31) from the stage in `buf` (for a K-major pair
+// buffer, the stage in half h).
 template <int ROWS, bool KMAJ>
-__device__ __forceinline__ bf16x8 read_frag(const lds_t* buf, int rb, int s, int l) {
+__device__ __forceinline__ bf16x8 read_frag(const lds_t* buf, int h, int rb, int s, int l) {
     if constexpr (KMAJ) {
-        const int row = rb + (l & 31), c = 2 * s + (l >> 5);
+        const int row = rb + (l & 31), c = 4 * h + 2 * s + (l >> 5);
         return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
-            buf + row * (kStageK * 2) + ((c ^ swzK(row)) << 4));
+            buf + row * (4 * kStageK) + ((c ^ swzK(row)) << 4));
     } else {
         // ds_read_b64_tr_b16: in a group of 16 lanes, lane 4j+q addresses
         // 4 values of row kbase+j at column col0+4q; lane i receives column
@@ -421,24 +416,29 @@ struct TileInfo {
     int32_t e, aux, aux2;  // expert and kernel-specific tags
 };
 
-// The LDS buffers of a kernel: kStages per operand, each a distinct
-// __shared__ array (see above).
+// The LDS buffers of a kernel, indexed by stage % 4: for a K-major operand
+// entries 2p and 2p+1 name the same pair buffer p, for an MN-major operand
+// each entry is its own buffer.  Every buffer is a distinct __shared__ array
+// (see above).
 struct Stages {
     lds_t* a[kStages];
     lds_t* b[kStages];
 };
 
-#define DRGG_STAGES(BM, BN, name)                                                              \
-    __shared__ __attribute__((aligned(1024))) char name##_a0[(BM) * kStageK * 2];              \
-    __shared__ __attribute__((aligned(1024))) char name##_a1[(BM) * kStageK * 2];              \
-    __shared__ __attribute__((aligned(1024))) char name##_a2[(BM) * kStageK * 2];              \
-    __shared__ __attribute__((aligned(1024))) char name##_a3[(BM) * kStageK * 2];              \
-    __shared__ __attribute__((aligned(1024))) char name##_b0[(BN) * kStageK * 2];              \
-    __shared__ __attribute__((aligned(1024))) char name##_b1[(BN) * kStageK * 2];              \
-    __shared__ __attribute__((aligned(1024))) char name##_b2[(BN) * kStageK * 2];              \
-    __shared__ __attribute__((aligned(1024))) char name##_b3[(BN) * kStageK * 2];              \
-    const Stages name{{(lds_t*)name##_a0, (lds_t*)name##_a1, (lds_t*)name##_a2, (lds_t*)name##_a3}, \
-                      {(lds_t*)name##_b0, (lds_t*)name##_b1, (lds_t*)name##_b2, (lds_t*)name##_b3}}
+#define DRGG_STAGE_BUFS(ROWS, KMAJ, name)                                                        \
+    __shared__ __attribute__((aligned(256))) char name##0[(KMAJ ? 2 : 1) * (ROWS) * kStageK * 2]; \
+    __shared__ __attribute__((aligned(256))) char name##1[(KMAJ ? 2 : 1) * (ROWS) * kStageK * 2]; \
+    __shared__ __attribute__((aligned(256))) char name##2[(KMAJ ? 0 : 1) * (ROWS) * kStageK * 2 + 16]; \
+    __shared__ __attribute__((aligned(256))) char name##3[(KMAJ ? 0 : 1) * (ROWS) * kStageK * 2 + 16]
+
+#define DRGG_STAGE_PTRS(KMAJ, name)                                                              \
+    KMAJ ? (lds_t*)name##0 : (lds_t*)name##0, KMAJ ? (lds_t*)name##0 : (lds_t*)name##1,          \
+    KMAJ ? (lds_t*)name##1 : (lds_t*)name##2, KMAJ ? (lds_t*)name##1 : (lds_t*)name##3
+
+#define DRGG_STAGES(BM, BN, AK, BK, name)                                                        \
+    DRGG_STAGE_BUFS(BM, AK, name##_a);                                                           \
+    DRGG_STAGE_BUFS(BN, BK, name##_b);                                                           \
+    const Stages name{{DRGG_STAGE_PTRS(AK, name##_a)}, {DRGG_STAGE_PTRS(BK, name##_b)}}
 
 // The accumulators and operand fragments of one BMxBN tile on 4 waves (one
 // per SIMD): the waves form a 2x2 grid, each owning a (BM/2)x(BN/2) block of
@@ -467,18 +467,18 @@ struct TileMma {
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
     }
 
-    // fragments of sub-step s of the stage in (sA, sB) into set F
-    template <int F>
-    __device__ __forceinline__ void read(const lds_t* sA, const lds_t* sB, int s) {
+    // fragments of sub-step s of stage ST (its buffers in st) into set F
+    template <int F, int ST>
+    __device__ __forceinline__ void read(const Stages& st, int s) {
         const int l = threadIdx.x & 63;
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         const int ra = (wave >> 1) * WM, rb = (wave & 1) * WN;
         // in the order the MFMAs consume them
-        fa[F][0] = read_frag<BM, AK>(sA, ra, s, l);
+        fa[F][0] = read_frag<BM, AK>(st.a[ST], ST & 1, ra, s, l);
 #pragma unroll
-        for (int j = 0; j < kBJ; ++j) fb[F][j] = read_frag<BN, BK>(sB, rb + 32 * j, s, l);
+        for (int j = 0; j < kBJ; ++j) fb[F][j] = read_frag<BN, BK>(st.b[ST], ST & 1, rb + 32 * j, s, l);
 #pragma unroll
-        for (int i = 1; i < kBI; ++i) fa[F][i] = read_frag<BM, AK>(sA, ra + 32 * i, s, l);
+        for (int i = 1; i < kBI; ++i) fa[F][i] = read_frag<BM, AK>(st.a[ST], ST & 1, ra + 32 * i, s, l);
     }
 
     template <int F>
@@ -570,22 +570,53 @@ __device__ __forceinline__ void atomic_add_tile(const Mma& mma, float* ts, int l
     }
 }
 
+// Issue schedule of the stage loads (steps t of the global step sequence;
+// the prologue acts as steps -4 .. -1).  A K-major operand loads stages t+3
+// and t+4 at odd steps (into the pair buffer whose two stages t-1 and t were
+// read by then), an MN-major operand stage t+4 at every step; within a step
+// A goes before B.  The pipeline waits, at the barrier of step s, until
+// stage s+1 of both operands has landed: with buffer loads returning in
+// issue order, that is "at most N pending", N the number of loads issued
+// after the last one of stage s+1.
+template <bool AK, bool BK, int CA, int CB>
+struct IssuePlan {
+    static constexpr int loads_at(int t, int op) {
+        const bool k = op == 0 ? AK : BK;
+        const int c = op == 0 ? CA : CB;
+        return k ? ((t & 1) ? c : 0) : c;
+    }
+    static constexpr int issue_step(bool k, int X) { return k ? ((X & 1) ? X - 4 : X - 3) : X - 4; }
+    // loads issued after those of stage X, up to and including step `upto`
+    static constexpr int after(int X, int upto) {
+        const int ta = issue_step(AK, X), tb = issue_step(BK, X);
+        const int last = 2 * ta > 2 * tb + 1 ? 2 * ta : 2 * tb + 1;
+        int n = 0;
+        for (int t = (ta < tb ? ta : tb); t <= upto; ++t)
+            for (int op = 0; op < 2; ++op)
+                if (2 * t + op > last) n += loads_at(t, op);
+        return n;
+    }
+    static constexpr int at_barrier(int s) { return after(s + 1, s - 1); }   // wait at step s
+    static constexpr int prologue = after(0, -1);                              // wait for stage 0
+};
+
 // Persistent tile loop over the stage pipeline.  `more()` tells whether this
 // workgroup has another tile and `next(t)` decodes it; `finish(t, mma)`
 // writes a finished tile from the accumulators.  Every step has the same
-// shape: each one issues one stage of loads and runs both MFMA sub-steps.
-// Stages past the end of a tile (the padding up to a multiple of four, or
-// past the last tile) are "loaded" with every lane masked, which writes
-// zeros to LDS without touching memory, so the MFMAs of a padding step add
-// zeros and no branch is taken around the accumulators.  The next tile is
-// decoded at the start of step nk4-4, whose loads fetch its first stage.
-// Must be called by all threads.
+// shape (up to the parity that decides whether a K-major pair is loaded):
+// it runs both MFMA sub-steps and issues its loads.  Stages past the end of a
+// tile (the padding up to a multiple of four, or past the last tile) are
+// "loaded" with every lane masked, which writes zeros to LDS without
+// touching memory, so the MFMAs of a padding step add zeros and no branch is
+// taken around the accumulators.  The next tile is decoded at the start of
+// step nk4-4, whose loads fetch its first stage.  Must be called by all
+// threads.
 template <int BM, int BN, bool AK, bool BK>
 struct TileRunner {
     using Mma = TileMma<BM, BN, AK, BK>;
     using LA = StageLoader<BM, AK>;
     using LB = StageLoader<BN, BK>;
-    static constexpr int C = LA::kPerWave + LB::kPerWave;   // loads per wave per stage
+    using Plan = IssuePlan<AK, BK, LA::kPerWave, LB::kPerWave>;
     Mma mma;
     LA la;
     LB lb;
@@ -598,38 +629,46 @@ struct TileRunner {
         return (t.A.klen + kStageK - 1) / kStageK;
     }
 
-    // Step kt of the current tile; ST = kt % 4 is its buffer.
+    // The loads of step t (t % 4 == ST) for operand loader `ld`: stage t+4,
+    // or for a K-major operand at odd t the pair t+3, t+4, of this tile or,
+    // past nk4, of the next one (the loaders then point at the next tile).
+    template <int ST, bool K, class Ld>
+    __device__ __forceinline__ void issue(Ld& ld, lds_t* const* bufs, int kt) {
+        if constexpr (!K || (ST & 1)) {
+            const int L = kt + (K ? 3 : 4);
+            const int Ls = L < nk4 ? L : L - nk4;
+            ld.issue(bufs[(ST + (K ? 3 : 4)) % kStages], Ls, L < nk4 || has_next);
+        }
+    }
+
+    // Step kt of the current tile; ST = kt % 4.
     template <int ST, class Next>
     __device__ __forceinline__ void step(int kt, Next& next) {
         constexpr int NX = (ST + 1) % kStages;
+        constexpr int NL = (AK && !(ST & 1) ? 0 : LA::kPerWave) + (BK && !(ST & 1) ? 0 : LB::kPerWave);
         if (kt + kStages == nk4 && has_next) {
             next(nxt);
             nk_nxt = stages_of(nxt);
             la.init(nxt.A);
             lb.init(nxt.B);
         }
-        // the stage this step loads: kt+4 of this tile, or of the next tile
-        // once past nk4 (the loaders then point at the next tile)
-        const int L = kt + kStages;
-        const int Ls = L < nk4 ? L : L - nk4;
-        const bool valid = L < nk4 || has_next;
         __builtin_amdgcn_sched_barrier(0);
         // sub-step 0: its MFMAs; the sub-step 1 fragments
-        mma.template read<1>(st.a[ST], st.b[ST], 1);
+        mma.template read<1, ST>(st, 1);
         mma.template mfma<0>();
         sched_interleave<Mma::kMfmas, Mma::kReads, 0>();
         __builtin_amdgcn_sched_barrier(0);
-        // stage kt+1 has landed for every wave (the loads of kt+2 and kt+3
-        // may still be in flight), and every wave is done reading stage kt
-        wait_vm_lgkm<2 * C>();
+        // stage kt+1 has landed for every wave, and every wave is done
+        // reading stage kt
+        wait_vm_lgkm<Plan::at_barrier(4 + ST)>();
         barrier_nofence();
-        // sub-step 1: its MFMAs; stage kt+4 into the freed buffer; the
+        // sub-step 1: its MFMAs; the loads into the buffers just freed; the
         // sub-step 0 fragments of stage kt+1
-        la.issue(st.a[ST], Ls, valid);
-        lb.issue(st.b[ST], Ls, valid);
-        mma.template read<0>(st.a[NX], st.b[NX], 0);
+        issue<ST, AK>(la, st.a, kt);
+        issue<ST, BK>(lb, st.b, kt);
+        mma.template read<0, NX>(st, 0);
         mma.template mfma<1>();
-        sched_interleave<Mma::kMfmas, Mma::kReads, C>();
+        sched_interleave<Mma::kMfmas, Mma::kReads, NL>();
         __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -639,17 +678,24 @@ struct TileRunner {
         next(cur);
         nk = stages_of(cur);
         nk4 = (nk + kStages - 1) & ~(kStages - 1);
+        has_next = false;
         la.init(cur.A);
         lb.init(cur.B);
-        // prologue: the first four stages (zeros past nk), then stage 0
+        // prologue: stages 0..3 (zeros past nk) in the order of steps -4..-1
 #pragma unroll
-        for (int X = 0; X < kStages; ++X) {
-            la.issue(st.a[X], X, true);
-            lb.issue(st.b[X], X, true);
+        for (int t = -4; t < 0; ++t) {
+#pragma unroll
+            for (int op = 0; op < 2; ++op) {
+                const bool k = op == 0 ? AK : BK;
+                if (k && !(t & 1)) continue;
+                const int L = t + (k ? 3 : 4);
+                if (op == 0) la.issue(st.a[L], L, true);
+                else lb.issue(st.b[L], L, true);
+            }
         }
-        wait_vm_lgkm<3 * C>();
+        wait_vm_lgkm<Plan::prologue>();
         barrier_nofence();
-        mma.template read<0>(st.a[0], st.b[0], 0);
+        mma.template read<0, 0>(st, 0);
         for (;;) {
             has_next = more();
             nk_nxt = 0;
@@ -700,7 +746,7 @@ __device__ __forceinline__ void store4(void* out, int64_t idx, f32x4 v) {
 
 template <int OP, int BM, int BN, bool OUT_BF16>
 __global__ __launch_bounds__(kGemmThreads) void gg_fwd_dgrad_kernel(GemmArgs a) {
-    DRGG_STAGES(BM, BN, stg);
+    DRGG_STAGES(BM, BN, true, OP == 0, stg);
     __shared__ Sched sch;
     // output columns: N (forward) or K (data gradient)
     const int64_t ncols = OP == 0 ? a.N : a.K;
@@ -750,7 +796,7 @@ __global__ __launch_bounds__(kGemmThreads) void gg_fwd_dgrad_kernel(GemmArgs a) 
 
 template <int BM, int BN, bool OUT_BF16>
 __global__ __launch_bounds__(kGemmThreads) void gg_wgrad_det_kernel(GemmArgs a) {
-    DRGG_STAGES(BM, BN, stg);
+    DRGG_STAGES(BM, BN, false, false, stg);
     __shared__ Sched sch;
     __shared__ int32_t slot_base[kMaxExperts + 1];
     const int32_t tn = (int32_t)((a.N + BM - 1) / BM), tk = (int32_t)((a.K + BN - 1) / BN);
@@ -885,7 +931,7 @@ __global__ __launch_bounds__(kThreads) void gg_wgrad_fold_kernel(GemmArgs a) {
 
 template <int BM, int BN, bool OUT_BF16>
 __global__ __launch_bounds__(kGemmThreads) void gg_wgrad_streamk_kernel(GemmArgs a) {
-    DRGG_STAGES(BM, BN, stg);
+    DRGG_STAGES(BM, BN, false, false, stg);
     __shared__ Sched sch;
     __shared__ int32_t s_last;
     const int32_t tn = (int32_t)((a.N + BM - 1) / BM), tk = (int32_t)((a.K + BN - 1) / BN);
