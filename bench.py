@@ -98,15 +98,15 @@ def gate_up_step(torch, drgg, prob):
 
 def cpu_baseline(prob):
     """The oracle as it stands, on a bounded sample of the gate_up workload:
-    forward rows 0..4095 (all N), data-gradient rows 0..2047 (all K), weight
-    gradient of expert 0 for output rows n = 0..63 (all K, 16384 tokens)."""
+    forward rows 0..16383 (all N), data-gradient rows 0..4095 (all K), weight
+    gradient of expert 0 for output rows n = 0..255 (all K, 16384 tokens)."""
     import oracle
     N, K = prob.N, prob.K
     T0 = int(prob.offs[1] - prob.offs[0])
     jobs = [
-        ("fwd", lambda: oracle.fwd(prob.X, prob.W, prob.offs, np.arange(4096 * N)), 2.0 * 4096 * N * K),
-        ("dgrad", lambda: oracle.dgrad(prob.G, prob.W, prob.offs, np.arange(2048 * K)), 2.0 * 2048 * K * N),
-        ("wgrad", lambda: oracle.wgrad(prob.X, prob.G, prob.offs, np.arange(64 * K)), 2.0 * 64 * K * T0),
+        ("fwd", lambda: oracle.fwd(prob.X, prob.W, prob.offs, np.arange(16384 * N)), 2.0 * 16384 * N * K),
+        ("dgrad", lambda: oracle.dgrad(prob.G, prob.W, prob.offs, np.arange(4096 * K)), 2.0 * 4096 * K * N),
+        ("wgrad", lambda: oracle.wgrad(prob.X, prob.G, prob.offs, np.arange(256 * K)), 2.0 * 256 * K * T0),
     ]
     flops = secs = 0.0
     for name, fn, f in jobs:
@@ -117,8 +117,8 @@ def cpu_baseline(prob):
         flops += f
         secs += dt
     return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(), "kind": "oracle",
-            "sample": "fwd rows 0-4095 x all 1536 cols, dgrad rows 0-2047 x all 2048 cols, "
-                      "wgrad expert 0 rows n 0-63 x all 2048 cols over its 16384 tokens "
+            "sample": "fwd rows 0-16383 x all 1536 cols, dgrad rows 0-4095 x all 2048 cols, "
+                      "wgrad expert 0 rows n 0-255 x all 2048 cols over its 16384 tokens "
                       f"({flops / 1e9:.1f} GFLOP in {secs:.1f} s, binary64 accumulation)"}
 
 
@@ -128,14 +128,25 @@ PROFILE_KEYS = {"gg_fwd_kernel": "gg_fwd_dgrad_kernel<0,", "gg_dgrad_kernel": "g
                 "gg_wgrad_det_kernel": "gg_wgrad_det_kernel<", "gg_wgrad_fold_kernel": "gg_wgrad_fold_kernel<"}
 
 
+def kernel_source_digest(path=KERNEL_SRC):
+    """Digest of the kernel source with comments and whitespace removed: it
+    changes when the code does, not when a comment does."""
+    import hashlib
+    import re
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    text = re.sub(r"\s+", "", text)
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
+
+
 def measured_traffic(kernel):
     """HBM-side bytes per launch of `kernel` from the committed rocprofv3
     counter summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy's
-    readings), or None when the kernel source changed since it was taken."""
-    import hashlib
+    readings), or None when the kernel code changed since it was taken."""
     try:
         text = open(PROFILE).read()
-        sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+        sha = kernel_source_digest()
     except OSError:
         return None
     if f"`{sha}`" not in text:

@@ -7,33 +7,27 @@
 //   weight gradient  dW[e,n,k] = sum_{t of e} G[t,n] X[t,k]
 // with FP32 accumulation on v_mfma_f32_32x32x16_bf16 and one rounding.
 //
-// One workgroup = 4 waves (256 lanes) computes one BMxBN output tile; the
-// waves form a 2x2 grid, each wave a (BM/2)x(BN/2) block of 32x32 MFMA tiles
-// whose FP32 accumulators stay in registers for the whole reduction.
+// One workgroup = 4 waves (256 lanes, one per SIMD) computes one BMxBN output
+// tile at a time and walks a list of tiles (persistent); the waves form a 2x2
+// grid, each wave a (BM/2)x(BN/2) block of 32x32 MFMA tiles whose FP32
+// accumulators stay in registers for the whole reduction.
 //
-// Operand staging.  The reduction runs in steps of 64.  For each step the
-// workgroup loads an A tile (BM x 64) and a B tile (BN x 64) from HBM with
-// 16-byte loads into registers, and writes them to LDS in one layout for all
-// programs: "K-major" rows of 64 reduction values (128 bytes), whose eight
-// 16-byte chunks are XOR-swizzled by the row index so that the MFMA operand
-// reads (32 rows, one chunk) and the tile writes hit distinct banks.  Two
-// LDS buffers alternate: while the MFMAs consume one step, the next step's
-// global loads are in flight and land in the other buffer.
-//   * K-major operands (reduction index contiguous in memory: X and W in the
-//     forward, G in the data gradient) are copied chunk for chunk.
-//   * MN-major operands (reduction index strided: W in the data gradient, G
-//     and X in the weight gradient, whose reduction runs over tokens) are
-//     loaded as 8x8 blocks -- eight rows of 8 consecutive output indices --
-//     and transposed in registers (32 byte permutes) before the LDS write, so
-//     the LDS tile is K-major again and the inner loop is the same MFMA code
-//     for every program.
+// Operand staging.  The reduction runs in stages of 32 values through four
+// LDS stage slots per operand, filled straight from HBM by 16-byte buffer
+// loads with an LDS destination (no registers in between), three steps
+// ahead of their use.  Operands whose reduction index is contiguous in
+// memory ("K-major": X and W in the forward, G in the data gradient) are
+// loaded two stages at a time as whole 128-byte rows; operands whose
+// reduction index is strided ("MN-major": W in the data gradient, G and X in
+// the weight gradient, reduced over tokens) one 32-row stage at a time and
+// read back transposed by ds_read_b64_tr_b16.  Both layouts are XOR-swizzled
+// so that the MFMA operand reads are free of bank conflicts.
 //
 // Ragged groups.  Every workgroup reads the group offsets, clamps them into
 // [0, M] and builds the per-expert prefix of work items in LDS; a work index
-// is then mapped to (expert, tile, chunk) by binary search.  Out-of-range
-// rows are never loaded from outside the buffers: row indices are clamped to
-// the last valid row and reduction positions outside the range are replaced
-// by zeros after the load.
+// is then mapped to (expert, tile, chunk) by binary search.  Rows, columns
+// and reduction positions outside an operand's valid range are never read:
+// their loads carry an out-of-range offset and write zeros to LDS.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
