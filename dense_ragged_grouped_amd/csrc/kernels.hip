@@ -533,31 +533,96 @@ __device__ __forceinline__ void store_tile(const Mma& mma, void* out, int64_t ld
     }
 }
 
-// Add a finished tile into an FP32 tile buffer: ts[row * ld + col] +=
-// tile[row][col] for row < rows, col < cols, with device-coherent atomic
-// adds (performed in L2).  Masked lanes use an out-of-range offset, as in
-// store_tile.
+// A split tile's FP32 sum lives in the workspace in the accumulators' own
+// order: element (wave w, block (i, j), register r, lane l) at
+// ((((w * kBI + i) * kBJ + j) * 16 + r) * 64 + l), so each atomic or load
+// instruction covers 64 consecutive floats (two cache lines).  Positions
+// outside the tile's valid rows and columns hold zeros (their operands were
+// zero-filled) and need no masking.
 template <class Mma>
-__device__ __forceinline__ void atomic_add_tile(const Mma& mma, float* ts, int ld, int rows, int cols) {
+__device__ __forceinline__ uint32_t tile_sum_offset(int wave, int i, int j, int r, int lane) {
+    return (uint32_t)(((((wave * Mma::kBI + i) * Mma::kBJ + j) * 16 + r) * 64 + lane) * 4);
+}
+
+// Add a finished tile into its FP32 tile sum with device-coherent atomic
+// adds (performed in L2).
+template <class Mma>
+__device__ __forceinline__ void atomic_add_tile(const Mma& mma, float* ts) {
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(ts);
+#pragma unroll
+    for (int i = 0; i < Mma::kBI; ++i)
+#pragma unroll
+        for (int j = 0; j < Mma::kBJ; ++j) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(mma.acc[i][j][r], rs,
+                                                                 tile_sum_offset<Mma>(wave, i, j, r, lane), 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+}
+
+// The last piece of a split tile: out[row * ld + col] = the tile sum (+ this
+// piece's own partial when ADD_OWN), rounded once, for row < rows and
+// col < cols; the tile sum is cleared back to zero for the next call.  The
+// caller has made the other pieces' atomic adds visible.
+template <bool OUT_BF16, bool ADD_OWN, class Mma>
+__device__ __forceinline__ void drain_tile_sum(const Mma& mma, float* ts, void* out, int64_t ld, int rows,
+                                               int cols) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    constexpr int ES = OUT_BF16 ? 2 : 4;
     int lane = threadIdx.x & 63;
     asm volatile("" : "+v"(lane));
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int ra = (wave >> 1) * Mma::WM, rb = (wave & 1) * Mma::WN;
-    const int r = ra + (lane & 31);
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(ts);
+    const int r = lane & 31;
+    const __amdgpu_buffer_rsrc_t rsum = make_rsrc(ts);
 #pragma unroll
     for (int i = 0; i < Mma::kBI; ++i) {
-        const bool rok = r + 32 * i < rows;
+        const int r0 = ra + 32 * i;
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(reinterpret_cast<char*>(out) + (int64_t)r0 * ld * ES);
+        const bool rok = r0 + r < rows;
 #pragma unroll
         for (int j = 0; j < Mma::kBJ; ++j) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int c = rb + 32 * j + 8 * q + 4 * (lane >> 5);
-                const uint32_t o = rok && c < cols ? (uint32_t)(((r + 32 * i) * ld + c) * 4) : kOOB;
+                const uint32_t o = rok && c < cols ? (uint32_t)((r * ld + c) * ES) : kOOB;
+                f32x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                        rsum, tile_sum_offset<Mma>(wave, i, j, 4 * q + e, lane), 0, 0));
+                    if constexpr (ADD_OWN) {
+                        float own = mma.acc[i][j][4 * q + e];
+                        // With a BF16 output the compiler otherwise copies
+                        // every accumulator out of the AGPRs up front, which
+                        // needs more VGPRs than there are: read each one here.
+                        if constexpr (OUT_BF16)
+                            asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(own) : "a"(mma.acc[i][j][4 * q + e]));
+                        v[e] += own;
+                    }
+                }
+                if constexpr (OUT_BF16) {
+                    const bf16x2 lo = __builtin_convertvector((f32x2{v[0], v[1]}), bf16x2);
+                    const bf16x2 hi = __builtin_convertvector((f32x2{v[2], v[3]}), bf16x2);
+                    const u32x2 d = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+                    __builtin_amdgcn_raw_buffer_store_b64(d, rs, o, 0, 0);
+                } else {
+                    const u32x4 d = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                                     __float_as_uint(v[3])};
+                    __builtin_amdgcn_raw_buffer_store_b128(d, rs, o, 0, 0);
+                }
+                // issued after the store above, whose data needed the loads:
+                // the clear cannot overtake the read
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(mma.acc[i][j][4 * q + e], rs,
-                                                                     o == kOOB ? kOOB : o + 4 * e, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b32(0u, rsum, tile_sum_offset<Mma>(wave, i, j, 4 * q + e, lane),
+                                                          0, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -934,7 +999,9 @@ __global__ __launch_bounds__(kGemmThreads) void gg_wgrad_streamk_kernel(GemmArgs
         return P * (int32_t)((T + kStreamKUnit - 1) / kStreamKUnit);
     });
     const int64_t U = uni(sch.prefix[a.E]);
-    const int64_t b = blockIdx.x;
+    // range index of this workgroup: consecutive ranges (adjacent tiles,
+    // sharing operand slabs) go to the same XCD
+    const int64_t b = xcd_remap(blockIdx.x, gridDim.x);
     // Workgroup b of G takes units [b*U/G, (b+1)*U/G).  With G <= U every
     // range is non-empty, so the workgroups touching a tile are exactly
     // owner(first unit) .. owner(last unit).
@@ -982,29 +1049,35 @@ __global__ __launch_bounds__(kGemmThreads) void gg_wgrad_streamk_kernel(GemmArgs
         }
         const int64_t slot = (int64_t)t.e * P + t.aux;
         float* ts = a.tilesum + slot * (BM * BN);
-        atomic_add_tile(mma, ts, BN, t.rows, t.cols);
-        __threadfence();
+        const uint32_t parts = (uint32_t)t.aux2;
+        void* ob = OUT_BF16 ? (void*)(reinterpret_cast<uint16_t*>(out) + base)
+                            : (void*)(reinterpret_cast<float*>(out) + base);
+        // If every other piece of this tile has already added its partial and
+        // taken its ticket, this piece is the last one: it adds its own
+        // partial from registers and skips the atomic adds (mode 2).
+        // Otherwise it adds into the tile sum, takes a ticket, and is the last
+        // one (mode 1) if the ticket says so.
+        if (threadIdx.x == 0)
+            s_last = __hip_atomic_load(a.tickets + slot, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) + 1 == parts
+                         ? 2 : 0;
         __syncthreads();
-        if (threadIdx.x == 0) {
-            const uint32_t old = __hip_atomic_fetch_add(a.tickets + slot, 1u, __ATOMIC_ACQ_REL,
-                                                        __HIP_MEMORY_SCOPE_AGENT);
-            s_last = (old + 1 == (uint32_t)t.aux2);
-        }
-        __syncthreads();
-        if (s_last) {   // last arrival: read and clear the sum, write the tile
+        int mode = s_last;
+        if (mode == 0) {
+            atomic_add_tile(mma, ts);
             __threadfence();
-            for (int i = threadIdx.x * 4; i < BM * BN; i += kGemmThreads * 4) {
-                const int r = i / BN, c = i % BN;
-                if (r < t.rows && c < t.cols) {
-                    f32x4 v;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        v[q] = __hip_atomic_load(ts + i + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        __hip_atomic_store(ts + i + q, 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    }
-                    store4<OUT_BF16>(out, base + r * a.K + c, v);
-                }
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                const uint32_t old = __hip_atomic_fetch_add(a.tickets + slot, 1u, __ATOMIC_ACQ_REL,
+                                                            __HIP_MEMORY_SCOPE_AGENT);
+                s_last = old + 1 == parts ? 1 : 0;
             }
+            __syncthreads();
+            mode = s_last;
+        }
+        if (mode != 0) {   // last piece: write the tile from the sum and clear it
+            __threadfence();
+            if (mode == 2) drain_tile_sum<OUT_BF16, true>(mma, ts, ob, a.K, t.rows, t.cols);
+            else drain_tile_sum<OUT_BF16, false>(mma, ts, ob, a.K, t.rows, t.cols);
             if (threadIdx.x == 0)
                 __hip_atomic_store(a.tickets + slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
