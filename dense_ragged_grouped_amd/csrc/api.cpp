@@ -242,6 +242,7 @@ drgg_status grouped_gemm_wgrad(const void* X, const void* G, const int32_t* grou
     }
     const int64_t P = ceil_div(N, p.ts.bm) * ceil_div(K, p.ts.bn);
     const int64_t sums = round_up(P * E * p.ts.bm * p.ts.bn * 4, 256);
+    a.chunk_max = wgrad_chunk_max(E, M, N, K);   // chunks in whole 512-token units on the device
     a.tilesum = static_cast<float*>(workspace);
     a.tickets = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + sums);
     return launch_status(launch_wgrad_streamk(p.tile, a, p.grid, bf16, stream));

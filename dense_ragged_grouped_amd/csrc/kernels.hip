@@ -985,8 +985,20 @@ __global__ __launch_bounds__(kThreads) void gg_wgrad_fold_kernel(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// non-deterministic weight gradient: stream-K over 512-token units with an
-// atomic FP32 tile sum and a last-arrival ticket for split tiles
+// non-deterministic weight gradient: the deterministic kernel's chunk-major
+// items, with token chunks of whole 512-token units; the partials of an
+// expert cut into several chunks are added into an FP32 tile sum by atomics,
+// and a per-tile ticket picks the last arrival, which writes the tile
+
+// the deterministic chunk length rounded up to whole 512-token units
+__device__ __forceinline__ int32_t unit_chunk_len(int32_t T, int64_t chunk_max) {
+    const int32_t l = chunk_len_dev(T, chunk_max);
+    return (int32_t)(((l + kStreamKUnit - 1) / kStreamKUnit) * kStreamKUnit);
+}
+__device__ __forceinline__ int32_t unit_chunks(int32_t T, int64_t chunk_max) {
+    const int32_t l = unit_chunk_len(T, chunk_max);
+    return l ? (T + l - 1) / l : 0;
+}
 
 template <int BM, int BN, bool OUT_BF16>
 __global__ __launch_bounds__(kGemmThreads) void gg_wgrad_streamk_kernel(GemmArgs a) {
@@ -995,48 +1007,36 @@ __global__ __launch_bounds__(kGemmThreads) void gg_wgrad_streamk_kernel(GemmArgs
     __shared__ int32_t s_last;
     const int32_t tn = (int32_t)((a.N + BM - 1) / BM), tk = (int32_t)((a.K + BN - 1) / BN);
     const int32_t P = tn * tk;
-    build_schedule(sch, a.offs, a.E, a.M, [=](int, int32_t T) {
-        return P * (int32_t)((T + kStreamKUnit - 1) / kStreamKUnit);
-    });
-    const int64_t U = uni(sch.prefix[a.E]);
-    // range index of this workgroup: consecutive ranges (adjacent tiles,
-    // sharing operand slabs) go to the same XCD
-    const int64_t b = xcd_remap(blockIdx.x, gridDim.x);
-    // Workgroup b of G takes units [b*U/G, (b+1)*U/G).  With G <= U every
-    // range is non-empty, so the workgroups touching a tile are exactly
-    // owner(first unit) .. owner(last unit).
-    const int64_t G = U < (int64_t)gridDim.x ? U : (int64_t)gridDim.x;
-    const int64_t u_end = b < G ? (b + 1) * U / G : 0;
-    int64_t u = b < G ? b * U / G : 0;
-    // the workgroup whose unit range holds unit v
-    auto owner = [&](int64_t v) { return ((v + 1) * G - 1) / U; };
-    // segments: the part of one tile's unit range inside this workgroup's range
-    auto more = [&]() { return u < u_end; };
+    const int64_t cmax = a.chunk_max;
+    build_schedule(sch, a.offs, a.E, a.M, [=](int, int32_t T) { return P * unit_chunks(T, cmax); });
+    const int64_t total = uni(sch.prefix[a.E]);
+    const int64_t G = gridDim.x;
+    const int64_t b = blockIdx.x;
+    int64_t w = xcd_remap(blockIdx.x, G);
+    if (a.reverse) w = G - 1 - w;
+    auto more = [&]() { return w < total; };
     auto next = [&](TileInfo& t) {
-        const int e = uni(find_expert(sch, a.E, (int32_t)u));
-        const int32_t oe = uni(sch.offs[e]), oe1 = uni(sch.offs[e + 1]), pe = uni(sch.prefix[e]);
+        const int e = uni(find_expert(sch, a.E, (int32_t)w));
+        const int32_t oe = uni(sch.offs[e]), oe1 = uni(sch.offs[e + 1]);
         const int32_t T = oe1 - oe;
-        const int32_t Ue = (int32_t)((T + kStreamKUnit - 1) / kStreamKUnit);
-        const int32_t local = (int32_t)(u - pe);
-        const int32_t tile = local / Ue, unit = local % Ue;
-        const int64_t tile_u0 = pe + (int64_t)tile * Ue;
-        const int64_t seg_end = min(u_end, tile_u0 + Ue);
-        const int32_t unit_hi = (int32_t)(seg_end - tile_u0);
+        const int32_t clen = unit_chunk_len(T, cmax);
+        const int32_t nch = (T + clen - 1) / clen;
+        const int32_t local = (int32_t)w - uni(sch.prefix[e]);
+        const int32_t chunk = local / P, tile = local % P;   // chunk-major: tiles of a chunk adjacent
         const int32_t ti = tile / tk, tj = tile % tk;
         const int64_t n0 = (int64_t)ti * BM, k0 = (int64_t)tj * BN;
-        const int64_t tb = oe + (int64_t)unit * kStreamKUnit;
-        const int64_t te = min<int64_t>(oe + (int64_t)unit_hi * kStreamKUnit, oe1);
+        const int64_t tb = oe + (int64_t)chunk * clen;
+        const int32_t len = (int32_t)min<int64_t>(clen, oe1 - tb);
         t.o0 = n0;
         t.o1 = k0;
         t.rows = (int32_t)min<int64_t>(BM, a.N - n0);
         t.cols = (int32_t)min<int64_t>(BN, a.K - k0);
         t.e = e;
-        const bool whole = unit == 0 && unit_hi == Ue;
-        t.aux = whole ? -1 : tile;
-        t.aux2 = whole ? 1 : (int32_t)(owner(tile_u0 + Ue - 1) - owner(tile_u0) + 1);
-        t.A = Operand{a.A + tb * a.N + n0, a.N, t.rows, (int32_t)(te - tb)};
-        t.B = Operand{a.B + tb * a.K + k0, a.K, t.cols, (int32_t)(te - tb)};
-        u = seg_end;
+        t.aux = nch == 1 ? -1 : tile;   // -1: the whole tile in this item, store directly
+        t.aux2 = nch;                   // pieces of a split tile
+        t.A = Operand{a.A + tb * a.N + n0, a.N, t.rows, len};
+        t.B = Operand{a.B + tb * a.K + k0, a.K, t.cols, len};
+        w += G;
     };
     auto finish = [&](const TileInfo& t, const TileMma<BM, BN, false, false>& mma) {
         const int64_t base = (int64_t)t.e * a.N * a.K + t.o0 * a.K + t.o1;
