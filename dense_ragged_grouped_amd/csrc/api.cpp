@@ -252,12 +252,14 @@ drgg_status router_gemm_fp32_bf16x3(const float* X, const float* Wr, int64_t M, 
                                     float* out, hipStream_t stream) {
     if (!X || !Wr || !out) return DRGG_EINVAL;
     if (M < 0 || N < 1 || K < 8 || M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return DRGG_ESHAPE;
-    if (K % 8 != 0) return DRGG_EALIGN;
+    if (K % 8 != 0 || N % 4 != 0) return DRGG_EALIGN;
     if (!aligned16(X) || !aligned16(Wr) || !aligned16(out)) return DRGG_EALIGN;
     int64_t t;
     if (!mul_ok(M, K, &t) || !mul_ok(t, 4, &t) || !mul_ok(M, N, &t) || !mul_ok(t, 4, &t) ||
         !mul_ok(N, K, &t) || !mul_ok(t, 4, &t))
         return DRGG_EOVERFLOW;
+    // per-lane byte offsets within a 128-row tile stay below 2^31
+    if (K > (int64_t(1) << 22)) return DRGG_ESHAPE;
     if (M == 0) return DRGG_OK;
     return launch_status(launch_router(X, Wr, out, M, N, K, stream));
 }

@@ -31,6 +31,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
 #include <utility>
 
 #include "internal.hpp"
@@ -60,25 +61,6 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
     return __uint_as_float((uint32_t)h << 16);
-}
-
-// 16-byte chunk swizzle of an LDS row (8 chunks of 8 BF16 per 128-byte row).
-__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
-
-__device__ __forceinline__ int lds_off(int row, int chunk) {
-    return row * kTileK + ((chunk ^ swz(row)) << 3);
-}
-
-__device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
-    return *reinterpret_cast<const u32x4*>(p);
-}
-
-__device__ __forceinline__ void st_lds16(uint16_t* s, int off, u32x4 v) {
-    *reinterpret_cast<u32x4*>(s + off) = v;
-}
-
-__device__ __forceinline__ bf16x8 ld_lds_frag(const uint16_t* s, int off) {
-    return *reinterpret_cast<const bf16x8*>(s + off);
 }
 
 // ---------------------------------------------------------------------------
@@ -1108,6 +1090,13 @@ __global__ __launch_bounds__(kGemmThreads) void gg_wgrad_streamk_kernel(GemmArgs
 // "FP32 router GEMM (256 experts, BF16x3 emulation)").
 //   out[m,n] = sum_k X[m,k] Wr[n,k];  v = hi + lo, hi = bf16(v), lo = bf16(v - hi)
 //   per 16-step: acc += hi_x hi_w, then hi_x lo_w, then lo_x hi_w.
+//
+// One workgroup per 128x128 output tile, 4 waves in a 2x2 grid (64x64 each),
+// with the grouped GEMM's step schedule.  The FP32 operands go straight from
+// HBM into four 32-value LDS stages per operand (rows of 128 bytes, chunk c of
+// row r at c ^ swzK(r), conflict-free for the operand reads); each MFMA
+// operand fragment is read as 8 FP32 values and split into its BF16 hi and
+// lo parts in registers (v - hi is exact in FP32).
 
 constexpr int kRouterBM = 128, kRouterBN = 128;
 
@@ -1118,124 +1107,236 @@ struct RouterArgs {
     int64_t M, N, K;
 };
 
-struct RouterLoader {
-    // 128 rows x 64 floats = 1024 chunks of 8 floats; 4 chunks per thread
-    f32x4 r[8];
-    __device__ __forceinline__ void load(const float* base, int64_t ld, int32_t nvalid, int32_t klen,
-                                         int kstep) {
+// Loads one 32-value stage of ROWS FP32 rows (128 bytes each) into LDS.
+template <int ROWS>
+struct F32StageLoader {
+    static constexpr int kPerWave = ROWS * 128 / 1024 / kGemmWaves;
+    uint32_t off[kPerWave];   // byte offset of this lane's 16 bytes from the stage base (kOOB if masked)
+    int32_t kp[kPerWave];     // reduction position of those 16 bytes within the stage
+    const char* base;
+    int32_t klen;
+
+    __device__ __forceinline__ void init(const float* b, int64_t ld, int32_t nvalid, int32_t kl) {
+        const int lane = threadIdx.x & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        base = reinterpret_cast<const char*>(b);
+        klen = kl;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int v = j * kThreads + threadIdx.x;
-            const int row = v >> 3, ch = v & 7;
-            const int kk = kstep * kTileK + ch * 8;
-            const bool ok = kk < klen;
-            const int rr = row < nvalid ? row : nvalid - 1;
-            const float* p = base + (int64_t)rr * ld + (ok ? kk : 0);
-            f32x4 x0 = *reinterpret_cast<const f32x4*>(p);
-            f32x4 x1 = *reinterpret_cast<const f32x4*>(p + 4);
-            r[2 * j] = ok ? x0 : f32x4{0.f, 0.f, 0.f, 0.f};
-            r[2 * j + 1] = ok ? x1 : f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < kPerWave; ++i) {
+            const int bb = (wave * kPerWave + i) * 1024 + lane * 16;
+            const int row = bb / 128, logical = ((bb % 128) / 16) ^ swzK(row);
+            off[i] = row < nvalid ? (uint32_t)(row * ld * 4 + logical * 16) : kOOB;
+            kp[i] = logical * 4;
         }
     }
-    __device__ __forceinline__ void store(uint16_t* shi, uint16_t* slo) const {
+
+    // stage L into `buf`; positions at or past klen read as zero
+    __device__ __forceinline__ void issue(lds_t* buf, int L) const {
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(base + (int64_t)L * 128);
+        const int rem = klen - L * 32;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int v = j * kThreads + threadIdx.x;
-            u32x4 h, l;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float x0 = r[2 * j + (q >> 1)][(q & 1) * 2];
-                const float x1 = r[2 * j + (q >> 1)][(q & 1) * 2 + 1];
-                const uint16_t h0 = f32_to_bf16(x0), h1 = f32_to_bf16(x1);
-                const uint16_t l0 = f32_to_bf16(x0 - bf16_to_f32(h0));
-                const uint16_t l1 = f32_to_bf16(x1 - bf16_to_f32(h1));
-                h[q] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-                l[q] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-            }
-            const int off = lds_off(v >> 3, v & 7);
-            st_lds16(shi, off, h);
-            st_lds16(slo, off, l);
+        for (int i = 0; i < kPerWave; ++i) {
+            const uint32_t o = kp[i] < rem ? off[i] : kOOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                r, (lds_void_t*)(buf + (wave * kPerWave + i) * 1024), 16, o, 0, 0, 0);
         }
     }
 };
 
-__global__ __launch_bounds__(kThreads, 1) void router_bf16x3_kernel(RouterArgs a) {
-    constexpr int BM = kRouterBM, BN = kRouterBN, TS = BM * kTileK;
-    __shared__ __attribute__((aligned(16))) uint16_t sAh[2 * TS], sAl[2 * TS], sBh[2 * TS], sBl[2 * TS];
+// Lane l's 8 FP32 values 16*s + 8*(l/32) .. +7 of tile row rb + (l & 31).
+struct Raw8 {
+    f32x4 x0, x1;
+};
+__device__ __forceinline__ Raw8 read_raw(const lds_t* buf, int rb, int s, int l) {
+    typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+    const int row = rb + (l & 31), c0 = 4 * s + 2 * (l >> 5);
+    Raw8 r;
+    r.x0 = *reinterpret_cast<const lds_f32x4*>(buf + row * 128 + ((c0 ^ swzK(row)) << 4));
+    r.x1 = *reinterpret_cast<const lds_f32x4*>(buf + row * 128 + (((c0 + 1) ^ swzK(row)) << 4));
+    return r;
+}
+
+// Split 8 FP32 values into BF16 hi = bf16(v) and lo = bf16(v - hi), both
+// rounded to nearest even (v - hi is exact in FP32).
+__device__ __forceinline__ void split8(const Raw8& r, bf16x8& hi, bf16x8& lo) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const float x[8] = {r.x0[0], r.x0[1], r.x0[2], r.x0[3], r.x1[0], r.x1[1], r.x1[2], r.x1[3]};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const bf16x2 h = __builtin_convertvector((f32x2{x[2 * p], x[2 * p + 1]}), bf16x2);
+        const bf16x2 d = __builtin_convertvector((f32x2{x[2 * p] - (float)h[0], x[2 * p + 1] - (float)h[1]}), bf16x2);
+        hi[2 * p] = h[0];
+        hi[2 * p + 1] = h[1];
+        lo[2 * p] = d[0];
+        lo[2 * p + 1] = d[1];
+    }
+}
+
+constexpr int kSchedValu = 0x002;
+
+// Router sub-step schedule: the NR LDS reads, the NV vector instructions
+// that split the fragments read in the previous sub-step, and the NL global
+// loads are spread evenly over the NM MFMAs.
+template <int NM, int NR, int NL, int NV, int T>
+__device__ __forceinline__ void router_slot() {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    constexpr int r = NR * (T + 1) / NM - NR * T / NM;
+    constexpr int v = NV * (T + 1) / NM - NV * T / NM;
+    constexpr int l = NL * (T + 1) / NM - NL * T / NM;
+    if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, r, 0);
+    if constexpr (l > 0) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, l, 0);
+    if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(kSchedValu, v, 0);
+}
+template <int NM, int NR, int NL, int NV, int... T>
+__device__ __forceinline__ void router_sched_impl(std::integer_sequence<int, T...>) {
+    (router_slot<NM, NR, NL, NV, T>(), ...);
+}
+template <int NM, int NR, int NL, int NV>
+__device__ __forceinline__ void router_sched() {
+    router_sched_impl<NM, NR, NL, NV>(std::make_integer_sequence<int, NM>{});
+}
+
+template <int BM, int BN>
+struct RouterMma {
+    static constexpr int WM = BM / 2, WN = BN / 2;
+    static constexpr int kBI = WM / 32, kBJ = WN / 32;
+    static constexpr int kReads = 2 * (kBI + kBJ);
+    static constexpr int kMfmas = 3 * kBI * kBJ;
+    static constexpr int kSplitValu = 24 * (kBI + kBJ);   // about 24 per 8-value fragment
+    f32x16 acc[kBI][kBJ];
+    bf16x8 ah[2][kBI], al[2][kBI], bh[2][kBJ], bl[2][kBJ];   // split fragments of sub-step 0 and 1
+    Raw8 ra[kBI], rbv[kBJ];                                    // raw fragments waiting to be split
+
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int i = 0; i < kBI; ++i)
+#pragma unroll
+            for (int j = 0; j < kBJ; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    }
+
+    // raw fragments of sub-step s of the stage in (sA, sB)
+    __device__ __forceinline__ void read(const lds_t* sA, const lds_t* sB, int s) {
+        const int l = threadIdx.x & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const int oa = (wave >> 1) * WM, ob = (wave & 1) * WN;
+#pragma unroll
+        for (int i = 0; i < kBI; ++i) ra[i] = read_raw(sA, oa + 32 * i, s, l);
+#pragma unroll
+        for (int j = 0; j < kBJ; ++j) rbv[j] = read_raw(sB, ob + 32 * j, s, l);
+    }
+
+    // split the raw fragments into set F
+    template <int F>
+    __device__ __forceinline__ void split() {
+#pragma unroll
+        for (int i = 0; i < kBI; ++i) split8(ra[i], ah[F][i], al[F][i]);
+#pragma unroll
+        for (int j = 0; j < kBJ; ++j) split8(rbv[j], bh[F][j], bl[F][j]);
+    }
+
+    // the three products of one 16-step, each over all blocks before the
+    // next, so that dependent MFMAs on one accumulator are kBI*kBJ apart
+    template <int F>
+    __device__ __forceinline__ void mfma() {
+#pragma unroll
+        for (int i = 0; i < kBI; ++i)
+#pragma unroll
+            for (int j = 0; j < kBJ; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bh[F][j], ah[F][i], acc[i][j], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < kBI; ++i)
+#pragma unroll
+            for (int j = 0; j < kBJ; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bl[F][j], ah[F][i], acc[i][j], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < kBI; ++i)
+#pragma unroll
+            for (int j = 0; j < kBJ; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bh[F][j], al[F][i], acc[i][j], 0, 0, 0);
+    }
+};
+
+// kRouterStages LDS stages per operand: with no other LDS in this kernel, five
+// (all 160 KB) fit, one more stage of loads in flight than the grouped GEMM.
+constexpr int kRouterStages = 5;
+
+__global__ __launch_bounds__(kGemmThreads) void router_bf16x3_kernel(RouterArgs a) {
+    constexpr int BM = kRouterBM, BN = kRouterBN, S = kRouterStages;
+    static_assert(S == 5, "the stage buffers below are written out for five stages");
+    __shared__ __attribute__((aligned(256))) char sa0[BM * 128], sa1[BM * 128], sa2[BM * 128], sa3[BM * 128],
+        sa4[BM * 128];
+    __shared__ __attribute__((aligned(256))) char sb0[BN * 128], sb1[BN * 128], sb2[BN * 128], sb3[BN * 128],
+        sb4[BN * 128];
+    lds_t* const sa[S] = {(lds_t*)sa0, (lds_t*)sa1, (lds_t*)sa2, (lds_t*)sa3, (lds_t*)sa4};
+    lds_t* const sb[S] = {(lds_t*)sb0, (lds_t*)sb1, (lds_t*)sb2, (lds_t*)sb3, (lds_t*)sb4};
+    using Mma = RouterMma<BM, BN>;
+    using LA = F32StageLoader<BM>;
+    using LB = F32StageLoader<BN>;
+    constexpr int C = LA::kPerWave + LB::kPerWave;   // loads per wave per stage
+
     const int64_t ntn = (a.N + BN - 1) / BN;
     const int64_t w = xcd_remap(blockIdx.x, gridDim.x);
-    const int64_t mt = w / ntn, nt = w % ntn;
-    const int64_t m0 = mt * BM, n0 = nt * BN;
+    const int64_t m0 = (w / ntn) * BM, n0 = (w % ntn) * BN;
     const int32_t rows = (int32_t)min<int64_t>(BM, a.M - m0);
     const int32_t cols = (int32_t)min<int64_t>(BN, a.N - n0);
-    const int32_t klen = (int32_t)a.K;
-    const float* Xb = a.X + m0 * a.K;
-    const float* Wb = a.Wr + n0 * a.K;
-
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    f32x16 acc[2][2];
+    LA la;
+    LB lb;
+    la.init(a.X + m0 * a.K, a.K, rows, (int32_t)a.K);
+    lb.init(a.Wr + n0 * a.K, a.K, cols, (int32_t)a.K);
+    const int nk = (int)((a.K + 31) / 32);
+    const int nkS = ((nk + S - 1) / S) * S;
+    Mma mma;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-    const int nk = (klen + kTileK - 1) / kTileK;
-    RouterLoader la, lb;
-    la.load(Xb, a.K, rows, klen, 0);
-    lb.load(Wb, a.K, cols, klen, 0);
-    la.store(sAh, sAl);
-    lb.store(sBh, sBl);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        const bool more = kt + 1 < nk;
-        if (more) {
-            la.load(Xb, a.K, rows, klen, kt + 1);
-            lb.load(Wb, a.K, cols, klen, kt + 1);
-        }
-        const uint16_t *ah = sAh + cur * TS, *al = sAl + cur * TS;
-        const uint16_t *bh = sBh + cur * TS, *bl = sBl + cur * TS;
-#pragma unroll
-        for (int ks = 0; ks < kTileK / kMfmaK; ++ks) {
-            const int ch = ks * 2 + (lane >> 5);
-            bf16x8 xh[2], xl[2], wh[2], wl[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int ra = wm * 64 + i * 32 + (lane & 31);
-                const int rb = wn * 64 + i * 32 + (lane & 31);
-                xh[i] = ld_lds_frag(ah, lds_off(ra, ch));
-                xl[i] = ld_lds_frag(al, lds_off(ra, ch));
-                wh[i] = ld_lds_frag(bh, lds_off(rb, ch));
-                wl[i] = ld_lds_frag(bl, lds_off(rb, ch));
-            }
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xh[i], wh[j], acc[i][j], 0, 0, 0);
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xh[i], wl[j], acc[i][j], 0, 0, 0);
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xl[i], wh[j], acc[i][j], 0, 0, 0);
-                }
-        }
-        if (more) {
-            la.store(sAh + (cur ^ 1) * TS, sAl + (cur ^ 1) * TS);
-            lb.store(sBh + (cur ^ 1) * TS, sBl + (cur ^ 1) * TS);
-        }
-        __syncthreads();
+    for (int X = 0; X < S; ++X) {
+        la.issue(sa[X], X);
+        lb.issue(sb[X], X);
     }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                const int col = wn * 64 + j * 32 + (lane & 31);
-                if (row < rows && col < cols) a.out[(m0 + row) * a.N + n0 + col] = acc[i][j][r];
-            }
+    // stages 0 and 1 have landed; the fragments of stage 0 are read (and
+    // those of sub-step 0 split) ahead of step 0
+    wait_vm_lgkm<(S - 2) * C>();
+    barrier_nofence();
+    mma.read(sa[0], sb[0], 0);
+    mma.template split<0>();
+    mma.read(sa[0], sb[0], 1);
+    mma.zero();
+    // Step kt of stage slot ST, software-pipelined over the two sub-steps:
+    //   region 0: MFMAs of (kt, 0); split of the raw (kt, 1); read raw (kt+1, 0)
+    //   barrier:  stage kt+2 has landed for every wave (the loads of kt+3 ..
+    //             kt+S-1 may still be in flight); stage kt was read in full
+    //             during step kt-1, so its slot takes the loads of stage kt+S
+    //   region 1: MFMAs of (kt, 1); split of the raw (kt+1, 0); read raw (kt+1, 1)
+    // Stages past nk load zeros, which add nothing.
+    auto step = [&](auto st_tag, int kt) {
+        constexpr int ST = decltype(st_tag)::value, NX = (ST + 1) % S;
+        __builtin_amdgcn_sched_barrier(0);
+        mma.template mfma<0>();
+        mma.template split<1>();
+        mma.read(sa[NX], sb[NX], 0);
+        router_sched<Mma::kMfmas, Mma::kReads, 0, Mma::kSplitValu>();
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm_lgkm<(S - 3) * C>();
+        barrier_nofence();
+        la.issue(sa[ST], kt + S);
+        lb.issue(sb[ST], kt + S);
+        mma.template mfma<1>();
+        mma.template split<0>();
+        mma.read(sa[NX], sb[NX], 1);
+        router_sched<Mma::kMfmas, Mma::kReads, C, Mma::kSplitValu>();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int kt = 0; kt < nkS; kt += S) {
+        step(std::integral_constant<int, 0>{}, kt);
+        step(std::integral_constant<int, 1>{}, kt + 1);
+        step(std::integral_constant<int, 2>{}, kt + 2);
+        step(std::integral_constant<int, 3>{}, kt + 3);
+        step(std::integral_constant<int, 4>{}, kt + 4);
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // the masked loads past the end
+    store_tile<false>(mma, a.out + m0 * a.N + n0, a.N, rows, cols);
 }
 
 // ---------------------------------------------------------------------------
@@ -1318,7 +1419,7 @@ hipError_t launch_router(const float* X, const float* Wr, float* out, int64_t M,
     RouterArgs a{X, Wr, out, M, N, K};
     const int64_t tiles = ((M + kRouterBM - 1) / kRouterBM) * ((N + kRouterBN - 1) / kRouterBN);
     timing_mark("router_bf16x3_kernel", s);
-    hipLaunchKernelGGL(router_bf16x3_kernel, dim3((unsigned)tiles), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(router_bf16x3_kernel, dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, a);
     timing_end(s);
     return hipGetLastError();
 }

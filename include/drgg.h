@@ -140,8 +140,9 @@ drgg_status grouped_gemm_wgrad(const void *X, const void *G, const int32_t *grou
  * BF16x3 emulation)"): each FP32 operand value v is split into
  * hi = bf16(v), lo = bf16(v - hi) (round to nearest even) and every product
  * is taken as hi*hi + hi*lo + lo*hi with FP32 accumulation.
- * X [M,K] FP32, Wr [N,K] FP32, out [M,N] FP32.  K must be a multiple of 8.
- * Deterministic (one fixed order).
+ * X [M,K] FP32, Wr [N,K] FP32, out [M,N] FP32.  K must be a multiple of 8
+ * and at most 2^22 (DRGG_ESHAPE otherwise), N a multiple of 4
+ * (DRGG_EALIGN otherwise).  Deterministic (one fixed order).
  */
 drgg_status router_gemm_fp32_bf16x3(const float *X, const float *Wr, int64_t M, int64_t N,
                                     int64_t K, float *out, hipStream_t stream);

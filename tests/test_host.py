@@ -96,6 +96,8 @@ def test_router_argument_checks(drgg):
     assert r(A16, A16, -1, 16, 16, A16, None) == 2
     assert r(A16, A16, 16, 16, 12, A16, None) == 3
     assert r(A16, A16, 16, 16, 16, A16 + 4, None) == 3
+    assert r(A16, A16, 16, 10, 16, A16, None) == 3          # N must be a multiple of 4
+    assert r(A16, A16, 16, 16, 2 ** 22 + 8, A16, None) == 2
     assert r(A16, A16, 2 ** 31 - 1, 16, 2 ** 31 - 8, A16, None) == 4
 
 
