@@ -245,7 +245,7 @@ drgg_status grouped_gemm_wgrad(const void* X, const void* G, const int32_t* grou
     a.chunk_max = wgrad_chunk_max(E, M, N, K);   // chunks in whole 512-token units on the device
     a.tilesum = static_cast<float*>(workspace);
     a.tickets = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + sums);
-    return launch_status(launch_wgrad_streamk(p.tile, a, p.grid, bf16, stream));
+    return launch_status(launch_wgrad_atomic(p.tile, a, p.grid, bf16, stream));
 }
 
 drgg_status router_gemm_fp32_bf16x3(const float* X, const float* Wr, int64_t M, int64_t N, int64_t K,

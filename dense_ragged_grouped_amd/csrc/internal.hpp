@@ -27,7 +27,7 @@ struct GemmArgs {
 
 hipError_t launch_fwd_dgrad(int op, int tile, const GemmArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_wgrad_det(int tile, const GemmArgs& a, bool bf16, hipStream_t s);
-hipError_t launch_wgrad_streamk(int tile, const GemmArgs& a, int64_t grid_n, bool bf16, hipStream_t s);
+hipError_t launch_wgrad_atomic(int tile, const GemmArgs& a, int64_t grid_n, bool bf16, hipStream_t s);
 hipError_t launch_router(const float* X, const float* Wr, float* out, int64_t M, int64_t N, int64_t K,
                          hipStream_t s);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);

@@ -425,7 +425,12 @@ struct Stages {
 // outputs leave as 8- or 16-byte stores.
 template <int BM, int BN, bool AK, bool BK>
 struct TileMma {
-    static constexpr int WM = BM / 2, WN = BN / 2;
+    // wave grid: kWGM waves along the tile rows, kWGN along its columns
+    static constexpr int kWGM = (kGemmWaves == 8 && BM >= 256) ? 4 : 2;
+    static constexpr int kWGN = kGemmWaves / kWGM;
+    static constexpr int WM = BM / kWGM, WN = BN / kWGN;
+    __device__ static __forceinline__ int wave_row(int wave) { return (wave / kWGN) * WM; }
+    __device__ static __forceinline__ int wave_col(int wave) { return (wave % kWGN) * WN; }
     static constexpr int kBI = WM / 32, kBJ = WN / 32;
     static_assert(kBI >= 1 && kBJ >= 1, "tile too small for the 2x2 wave grid");
     // LDS reads per sub-step: one per 32-row block (K-major), two (MN-major)
@@ -448,7 +453,7 @@ struct TileMma {
     __device__ __forceinline__ void read(const Stages& st, int s) {
         const int l = threadIdx.x & 63;
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-        const int ra = (wave >> 1) * WM, rb = (wave & 1) * WN;
+        const int ra = wave_row(wave), rb = wave_col(wave);
         // in the order the MFMAs consume them
         fa[F][0] = read_frag<BM, AK>(st.a[ST], ST & 1, ra, s, l);
 #pragma unroll
@@ -485,7 +490,7 @@ __device__ __forceinline__ void store_tile(const Mma& mma, void* out, int64_t ld
     int lane = threadIdx.x & 63;
     asm volatile("" : "+v"(lane));
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int ra = (wave >> 1) * Mma::WM, rb = (wave & 1) * Mma::WN;
+    const int ra = Mma::wave_row(wave), rb = Mma::wave_col(wave);
     const int r = lane & 31;
 #pragma unroll
     for (int i = 0; i < Mma::kBI; ++i) {
@@ -560,7 +565,7 @@ __device__ __forceinline__ void drain_tile_sum(const Mma& mma, float* ts, void* 
     int lane = threadIdx.x & 63;
     asm volatile("" : "+v"(lane));
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int ra = (wave >> 1) * Mma::WM, rb = (wave & 1) * Mma::WN;
+    const int ra = Mma::wave_row(wave), rb = Mma::wave_col(wave);
     const int r = lane & 31;
     const __amdgpu_buffer_rsrc_t rsum = make_rsrc(ts);
 #pragma unroll
@@ -983,7 +988,7 @@ __device__ __forceinline__ int32_t unit_chunks(int32_t T, int64_t chunk_max) {
 }
 
 template <int BM, int BN, bool OUT_BF16>
-__global__ __launch_bounds__(kGemmThreads) void gg_wgrad_streamk_kernel(GemmArgs a) {
+__global__ __launch_bounds__(kGemmThreads) void gg_wgrad_atomic_kernel(GemmArgs a) {
     DRGG_STAGES(BM, BN, false, false, stg);
     __shared__ Sched sch;
     __shared__ int32_t s_last;
@@ -1200,7 +1205,11 @@ __device__ __forceinline__ void router_sched() {
 
 template <int BM, int BN>
 struct RouterMma {
-    static constexpr int WM = BM / 2, WN = BN / 2;
+    static constexpr int kWGM = (kGemmWaves == 8 && BM >= 256) ? 4 : 2;
+    static constexpr int kWGN = kGemmWaves / kWGM;
+    static constexpr int WM = BM / kWGM, WN = BN / kWGN;
+    __device__ static __forceinline__ int wave_row(int wave) { return (wave / kWGN) * WM; }
+    __device__ static __forceinline__ int wave_col(int wave) { return (wave % kWGN) * WN; }
     static constexpr int kBI = WM / 32, kBJ = WN / 32;
     static constexpr int kReads = 2 * (kBI + kBJ);
     static constexpr int kMfmas = 3 * kBI * kBJ;
@@ -1222,7 +1231,7 @@ struct RouterMma {
     __device__ __forceinline__ void read(const lds_t* sA, const lds_t* sB, int s) {
         const int l = threadIdx.x & 63;
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-        const int oa = (wave >> 1) * WM, ob = (wave & 1) * WN;
+        const int oa = wave_row(wave), ob = wave_col(wave);
 #pragma unroll
         for (int i = 0; i < kBI; ++i) ra[i] = read_raw(sA, oa + 32 * i, s, l);
 #pragma unroll
@@ -1395,22 +1404,22 @@ hipError_t launch_wgrad_det(int tile, const GemmArgs& a, bool bf16, hipStream_t 
 }
 
 template <int BM, int BN>
-static hipError_t launch_wgrad_streamk_t(const GemmArgs& a, int64_t grid_n, bool bf16, hipStream_t s) {
+static hipError_t launch_wgrad_atomic_t(const GemmArgs& a, int64_t grid_n, bool bf16, hipStream_t s) {
     dim3 grid((unsigned)grid_n), block(kGemmThreads);
-    timing_mark("gg_wgrad_streamk_kernel", s);
-    if (bf16) hipLaunchKernelGGL((gg_wgrad_streamk_kernel<BM, BN, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((gg_wgrad_streamk_kernel<BM, BN, false>), grid, block, 0, s, a);
+    timing_mark("gg_wgrad_atomic_kernel", s);
+    if (bf16) hipLaunchKernelGGL((gg_wgrad_atomic_kernel<BM, BN, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((gg_wgrad_atomic_kernel<BM, BN, false>), grid, block, 0, s, a);
     timing_end(s);
     return hipGetLastError();
 }
 
-hipError_t launch_wgrad_streamk(int tile, const GemmArgs& a, int64_t grid_n, bool bf16, hipStream_t s) {
+hipError_t launch_wgrad_atomic(int tile, const GemmArgs& a, int64_t grid_n, bool bf16, hipStream_t s) {
     switch (tile) {
-        case kTile128x128: return launch_wgrad_streamk_t<128, 128>(a, grid_n, bf16, s);
-        case kTile256x128: return launch_wgrad_streamk_t<256, 128>(a, grid_n, bf16, s);
-        case kTile128x256: return launch_wgrad_streamk_t<128, 256>(a, grid_n, bf16, s);
-        case kTile64x256: return launch_wgrad_streamk_t<64, 256>(a, grid_n, bf16, s);
-        default: return launch_wgrad_streamk_t<256, 256>(a, grid_n, bf16, s);
+        case kTile128x128: return launch_wgrad_atomic_t<128, 128>(a, grid_n, bf16, s);
+        case kTile256x128: return launch_wgrad_atomic_t<256, 128>(a, grid_n, bf16, s);
+        case kTile128x256: return launch_wgrad_atomic_t<128, 256>(a, grid_n, bf16, s);
+        case kTile64x256: return launch_wgrad_atomic_t<64, 256>(a, grid_n, bf16, s);
+        default: return launch_wgrad_atomic_t<256, 256>(a, grid_n, bf16, s);
     }
 }
 

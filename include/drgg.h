@@ -31,13 +31,16 @@
  *                       (never on the device), writes one FP32 partial per
  *                       chunk and folds the partials in chunk order before a
  *                       single rounding.
- *   deterministic == 0  the weight gradient splits the token range of tiles
- *                       across workgroups in 512-token units (stream-K); the
- *                       pieces of a split tile add their FP32 partials into
- *                       an FP32 tile sum with atomic adds, a per-tile ticket
+ *   deterministic == 0  the weight gradient cuts an expert's token range into
+ *                       chunks of whole 512-token units (the deterministic
+ *                       chunk lengths rounded up); the pieces of a tile cut
+ *                       into several chunks add their FP32 partials into an
+ *                       FP32 tile sum with atomic adds, and a per-tile ticket
  *                       picks the last arrival, which reads and clears the sum
- *                       and writes the output tile.  The summation order of a
- *                       split tile can differ from run to run.  Forward and
+ *                       and writes the output tile (a piece that finds every
+ *                       other piece already done adds its own partial in
+ *                       registers instead).  The summation order of a split
+ *                       tile can differ from run to run.  Forward and
  *                       data gradient have no split and are identical in both
  *                       modes (PR #8363, Summary: the dense non-deterministic
  *                       forward and input gradient are the deterministic
@@ -190,8 +193,7 @@ drgg_status drgg_wgrad_chunking(int64_t T, int64_t chunk_max, int64_t *chunk_len
  *   DRGG_KNOB_TILE        force the output tile of fwd/dgrad/det-wgrad:
  *                         1 = 256x256, 2 = 128x128, 3 = 256x128, 4 = 128x256
  *   DRGG_KNOB_GRID        force the workgroup count of the persistent kernels
- *                         (every program; for the non-deterministic weight
- *                         gradient it also sets the stream-K partition)
+ *                         (every program)
  *   DRGG_KNOB_REVERSE     1 = walk the work items in reverse order
  *   DRGG_KNOB_TIMING      1 = record a HIP event on the stream before every
  *                         kernel launch of a call and after its last launch
