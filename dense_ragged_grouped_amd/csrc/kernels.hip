@@ -45,8 +45,12 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;       // fold / zero / router kernels
-constexpr int kGemmWaves = 4;       // grouped-GEMM kernels: one wave per SIMD
+// Grouped-GEMM kernels run 4 waves (one per SIMD) or, for the 256x256
+// forward and data-gradient tiles, 8 (two per SIMD, each on half the
+// accumulators): a second wave per SIMD covers the stalls of the first.
+constexpr int kGemmWaves = 4;
 constexpr int kGemmThreads = 64 * kGemmWaves;
+constexpr int kMaxGemmThreads = 512;
 
 // ---------------------------------------------------------------------------
 // small helpers
@@ -69,7 +73,7 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
 struct Sched {
     int32_t offs[kMaxExperts + 1];    // clamped, non-decreasing offsets
     int32_t prefix[kMaxExperts + 1];  // exclusive prefix of work per expert
-    int32_t scan[kGemmThreads];
+    int32_t scan[kMaxGemmThreads];
 };
 
 // Fills s.offs[0..E] with the offsets clamped into [0, M] (and made
@@ -78,22 +82,22 @@ struct Sched {
 template <class WorkFn>
 __device__ void build_schedule(Sched& s, const int32_t* __restrict__ offs, int E, int64_t M,
                                WorkFn work) {
-    const int tid = threadIdx.x;
-    for (int e = tid; e <= E; e += kGemmThreads) {
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    for (int e = tid; e <= E; e += nthr) {
         int64_t v = offs[e];
         v = v < 0 ? 0 : (v > M ? M : v);
         s.offs[e] = (int32_t)v;
     }
     __syncthreads();
     // make non-decreasing (a running max); E <= 1024, one pass per thread chunk
-    const int per = (E + kGemmThreads) / kGemmThreads;   // covers indices 0..E
+    const int per = (E + nthr) / nthr;   // covers indices 0..E
     const int lo = tid * per;
     const int hi = min(lo + per, E + 1);
     int32_t run = 0;
     for (int i = lo; i < hi; ++i) run = max(run, s.offs[i]);
     s.scan[tid] = run;
     __syncthreads();
-    for (int d = 1; d < kGemmThreads; d <<= 1) {
+    for (int d = 1; d < nthr; d <<= 1) {
         int32_t v = tid >= d ? s.scan[tid - d] : 0;
         __syncthreads();
         s.scan[tid] = max(s.scan[tid], v);
@@ -111,7 +115,7 @@ __device__ void build_schedule(Sched& s, const int32_t* __restrict__ offs, int E
     for (int e = lo; e < hi && e < E; ++e) local += work(e, s.offs[e + 1] - s.offs[e]);
     s.scan[tid] = local;
     __syncthreads();
-    for (int d = 1; d < kGemmThreads; d <<= 1) {
+    for (int d = 1; d < nthr; d <<= 1) {
         int32_t v = tid >= d ? s.scan[tid - d] : 0;
         __syncthreads();
         s.scan[tid] += v;
@@ -249,11 +253,15 @@ __device__ __forceinline__ void barrier_nofence() {
 constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100;
 
 // Interleave NM MFMAs with NR LDS reads and NL global loads of the same
-// region: after MFMA t come the reads and loads whose share falls on t.
+// region: the reads spread over the first half of the MFMAs (they feed the
+// next sub-step), the loads over all of them.  Used when both operands are
+// K-major; with transposed (MN-major) reads the compiler's own order is
+// faster, as measured.
 template <int NM, int NR, int NL, int T>
 __device__ __forceinline__ void sched_slot() {
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-    constexpr int r = NR * (T + 1) / NM - NR * T / NM;
+    constexpr int H = NM / 2;   // the reads go out during the first half
+    constexpr int r = T < H ? NR * (T + 1) / H - NR * T / H : 0;
     constexpr int l = NL * (T + 1) / NM - NL * T / NM;
     if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, r, 0);
     if constexpr (l > 0) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, l, 0);
@@ -300,10 +308,11 @@ __device__ __forceinline__ int swzMN(int row) {
 // of the 4 waves issues a quarter.  Lane l of instruction g writes LDS bytes
 // [g*1024 + 16*l, +16); the swizzle is applied by choosing which global
 // chunk the lane fetches.
-template <int ROWS, bool KMAJ>
+template <int ROWS, bool KMAJ, int WAVES>
 struct StageLoader {
     static constexpr int kSpan = KMAJ ? 2 : 1;   // stages per load
-    static constexpr int kPerWave = ROWS * kStageK * 2 * kSpan / 1024 / kGemmWaves;
+    static constexpr int kPerWave = ROWS * kStageK * 2 * kSpan / 1024 / WAVES;
+    static_assert(kPerWave >= 1, "every wave issues at least one load per stage");
     static constexpr int kRowBytes = KMAJ ? 2 * kStageK * 2 : ROWS * 2;
     static constexpr int kCPR = kRowBytes / 16;
     static_assert(ROWS % 64 == 0, "tile rows must be a multiple of 64");
@@ -423,11 +432,11 @@ struct Stages {
 // so that the accumulator of lane l holds tile row l%32 and, in registers
 // 4q..4q+3, four consecutive tile columns 8q + 4*(l/32) .. +3: a lane's
 // outputs leave as 8- or 16-byte stores.
-template <int BM, int BN, bool AK, bool BK>
+template <int BM, int BN, bool AK, bool BK, int WAVES = kGemmWaves>
 struct TileMma {
     // wave grid: kWGM waves along the tile rows, kWGN along its columns
-    static constexpr int kWGM = (kGemmWaves == 8 && BM >= 256) ? 4 : 2;
-    static constexpr int kWGN = kGemmWaves / kWGM;
+    static constexpr int kWGM = (WAVES == 8 && BM >= 256) ? 4 : 2;
+    static constexpr int kWGN = WAVES / kWGM;
     static constexpr int WM = BM / kWGM, WN = BN / kWGN;
     __device__ static __forceinline__ int wave_row(int wave) { return (wave / kWGN) * WM; }
     __device__ static __forceinline__ int wave_col(int wave) { return (wave % kWGN) * WN; }
@@ -657,11 +666,11 @@ struct IssuePlan {
 // taken around the accumulators.  The next tile is decoded at the start of
 // step nk4-4, whose loads fetch its first stage.  Must be called by all
 // threads.
-template <int BM, int BN, bool AK, bool BK>
+template <int BM, int BN, bool AK, bool BK, int WAVES = kGemmWaves>
 struct TileRunner {
-    using Mma = TileMma<BM, BN, AK, BK>;
-    using LA = StageLoader<BM, AK>;
-    using LB = StageLoader<BN, BK>;
+    using Mma = TileMma<BM, BN, AK, BK, WAVES>;
+    using LA = StageLoader<BM, AK, WAVES>;
+    using LB = StageLoader<BN, BK, WAVES>;
     using Plan = IssuePlan<AK, BK, LA::kPerWave, LB::kPerWave>;
     Mma mma;
     LA la;
@@ -702,7 +711,7 @@ struct TileRunner {
         // sub-step 0: its MFMAs; the sub-step 1 fragments
         mma.template read<1, ST>(st, 1);
         mma.template mfma<0>();
-        sched_interleave<Mma::kMfmas, Mma::kReads, 0>();
+        if constexpr (AK && BK) sched_interleave<Mma::kMfmas, Mma::kReads, 0>();
         __builtin_amdgcn_sched_barrier(0);
         // stage kt+1 has landed for every wave, and every wave is done
         // reading stage kt
@@ -714,7 +723,7 @@ struct TileRunner {
         issue<ST, BK>(lb, st.b, kt);
         mma.template read<0, NX>(st, 0);
         mma.template mfma<1>();
-        sched_interleave<Mma::kMfmas, Mma::kReads, NL>();
+        if constexpr (AK && BK) sched_interleave<Mma::kMfmas, Mma::kReads, NL>();
         __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -790,8 +799,8 @@ __device__ __forceinline__ void store4(void* out, int64_t idx, f32x4 v) {
 // time the 32 workgroups of one XCD work on 32 consecutive output tiles (the
 // tiles of a few 256-row panels), which share operand slabs in that XCD's L2.
 
-template <int OP, int BM, int BN, bool OUT_BF16>
-__global__ __launch_bounds__(kGemmThreads) void gg_fwd_dgrad_kernel(GemmArgs a) {
+template <int OP, int BM, int BN, bool OUT_BF16, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void gg_fwd_dgrad_kernel(GemmArgs a) {
     DRGG_STAGES(BM, BN, true, OP == 0, stg);
     __shared__ Sched sch;
     // output columns: N (forward) or K (data gradient)
@@ -827,12 +836,12 @@ __global__ __launch_bounds__(kGemmThreads) void gg_fwd_dgrad_kernel(GemmArgs a) 
         w += G;
     };
     void* out = a.out;
-    auto finish = [&](const TileInfo& t, const TileMma<BM, BN, true, OP == 0>& mma) {
+    auto finish = [&](const TileInfo& t, const TileMma<BM, BN, true, OP == 0, WAVES>& mma) {
         void* base = OUT_BF16 ? (void*)(reinterpret_cast<uint16_t*>(out) + t.o0 * ncols + t.o1)
                               : (void*)(reinterpret_cast<float*>(out) + t.o0 * ncols + t.o1);
         store_tile<OUT_BF16>(mma, base, ncols, t.rows, t.cols);
     };
-    TileRunner<BM, BN, true, OP == 0> runner;
+    TileRunner<BM, BN, true, OP == 0, WAVES> runner;
     runner.st = stg;
     runner.run(more, next, finish);
 }
@@ -1353,10 +1362,12 @@ __global__ __launch_bounds__(kGemmThreads) void router_bf16x3_kernel(RouterArgs 
 
 template <int OP, int BM, int BN>
 static hipError_t launch_fwd_dgrad_t(const GemmArgs& a, bool bf16, hipStream_t s) {
-    dim3 grid((unsigned)a.items_max), block(kGemmThreads);
+    // two waves per SIMD for the 256x256 tile, one otherwise
+    constexpr int WAVES = (BM == 256 && BN == 256) ? 8 : 4;
+    dim3 grid((unsigned)a.items_max), block(64 * WAVES);
     timing_mark(OP == 0 ? "gg_fwd_kernel" : "gg_dgrad_kernel", s);
-    if (bf16) hipLaunchKernelGGL((gg_fwd_dgrad_kernel<OP, BM, BN, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((gg_fwd_dgrad_kernel<OP, BM, BN, false>), grid, block, 0, s, a);
+    if (bf16) hipLaunchKernelGGL((gg_fwd_dgrad_kernel<OP, BM, BN, true, WAVES>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((gg_fwd_dgrad_kernel<OP, BM, BN, false, WAVES>), grid, block, 0, s, a);
     timing_end(s);
     return hipGetLastError();
 }
