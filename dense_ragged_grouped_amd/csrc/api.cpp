@@ -90,7 +90,8 @@ drgg_status make_plan(drgg_op op, int32_t E, int64_t M, int64_t N, int64_t K, in
     // persistent grid: as many workgroups as fit on the device at once, never
     // more than there are work items (a bound that holds for any offsets)
     const int64_t g_knob = g_knob_grid.load();
-    const int64_t resident = (int64_t)cu_count * wgs_per_cu(p->ts);
+    const bool fd = op == DRGG_OP_FWD || op == DRGG_OP_DGRAD;
+    const int64_t resident = (int64_t)cu_count * wgs_per_cu(p->ts, fd, !fd && det);
     auto grid_for = [&](int64_t items_max) {
         int64_t g = g_knob > 0 ? g_knob : (resident < items_max ? resident : items_max);
         return g < 1 ? (int64_t)1 : g;

@@ -426,9 +426,9 @@ struct Stages {
     const Stages name{{DRGG_STAGE_PTRS(AK, name##_a)}, {DRGG_STAGE_PTRS(BK, name##_b)}}
 
 // The accumulators and operand fragments of one BMxBN tile on 4 waves (one
-// per SIMD): the waves form a 2x2 grid, each owning a (BM/2)x(BN/2) block of
-// 32x32 MFMA tiles whose FP32 accumulators stay in registers (AGPRs for the
-// 256x256 tile).  The MFMA takes the B-side fragment as its first operand,
+// per SIMD, a 2x2 wave grid) or 8 waves (two per SIMD, a 4x2 grid for
+// 256-row tiles): each wave owns a block of 32x32 MFMA tiles whose FP32
+// accumulators stay in registers.  The MFMA takes the B-side fragment as its first operand,
 // so that the accumulator of lane l holds tile row l%32 and, in registers
 // 4q..4q+3, four consecutive tile columns 8q + 4*(l/32) .. +3: a lane's
 // outputs leave as 8- or 16-byte stores.
@@ -471,13 +471,16 @@ struct TileMma {
         for (int i = 1; i < kBI; ++i) fa[F][i] = read_frag<BM, AK>(st.a[ST], ST & 1, ra + 32 * i, s, l);
     }
 
-    template <int F>
+    // FIRST: the tile's first products, accumulated onto zero (this is what
+    // clears the accumulators between tiles)
+    template <int F, bool FIRST = false>
     __device__ __forceinline__ void mfma() {
 #pragma unroll
         for (int i = 0; i < kBI; ++i)
 #pragma unroll
             for (int j = 0; j < kBJ; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[F][j], fa[F][i], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[F][j], fa[F][i], FIRST ? f32x16{} : acc[i][j],
+                                                                    0, 0, 0);
     }
 };
 
@@ -525,6 +528,99 @@ __device__ __forceinline__ void store_tile(const Mma& mma, void* out, int64_t ld
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+// Write a finished tile like store_tile, but so that every global store
+// instruction writes whole 128-byte lines (R = ep_rows of the tile, from
+// plan.hpp, which sizes the LDS for it).  In the accumulator layout a
+// lane owns one row of each 32x32 block, so a direct store touches 32 rows
+// (32 lines, 16 or 32 bytes each) per instruction; written back-to-back by
+// every workgroup at a tile boundary, those partial lines cost more than the
+// rest of the epilogue.  Here each wave moves its blocks through its own
+// R x 128-byte LDS scratch `scr`: a 128-byte row segment (64 BF16 or 32 FP32
+// columns, i.e. two or one 32-column blocks) of R rows at a time, written by
+// the lanes that own those rows and read back as 16-byte chunks, eight lanes
+// per row, then stored with 16-byte buffer stores (R/8 rows of whole lines
+// per instruction).  Chunk c of scratch row rr sits at 16 * (c ^ (rr & 7)), so
+// the read-back is free of bank conflicts.  Masking as in store_tile; cols
+// must be a multiple of 8 (BF16) or 4 (FP32).  The scratch is private to the
+// wave, so a wave-level sync between the phases is all it needs.
+// Lanes of one wave exchanging data through LDS: the fences order each
+// lane's accesses before and after this point for the compiler (no
+// instruction is emitted; the wave's DS instructions execute in order).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <bool OUT_BF16, int R, class Mma>
+__device__ __forceinline__ void store_tile_lines(const Mma& mma, lds_t* scr, void* out, int64_t ld, int rows,
+                                                 int cols) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    constexpr int ES = OUT_BF16 ? 2 : 4;
+    constexpr int SEG = 128 / ES;   // columns per 128-byte segment
+    constexpr int BPS = SEG / 32;   // 32-column blocks per segment
+    constexpr int CPL = R / 8;      // read-back chunks per lane and round
+    static_assert(R == 8 || R == 16, "rounds of 8 or 16 rows");
+    static_assert(Mma::kBJ % BPS == 0, "whole segments per wave");
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int ra = Mma::wave_row(wave), rb = Mma::wave_col(wave);
+    lds_t* sw = scr + wave * (R * 128);
+    const int r = lane & 31, h = lane >> 5;
+    const int rr = r % R;   // this lane's scratch row in the round that owns it
+    const int sx = rr & 7;
+#pragma unroll
+    for (int i = 0; i < Mma::kBI; ++i) {
+        const int r0 = ra + 32 * i;
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(reinterpret_cast<char*>(out) + (int64_t)r0 * ld * ES);
+#pragma unroll
+        for (int g = 0; g < Mma::kBJ / BPS; ++g) {
+            const int c0 = rb + g * SEG;
+#pragma unroll
+            for (int s = 0; s < 32 / R; ++s) {
+                if (r / R == s) {
+#pragma unroll
+                    for (int b = 0; b < BPS; ++b) {
+                        const f32x16& a = mma.acc[i][g * BPS + b];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            if constexpr (OUT_BF16) {
+                                // columns 32b + 8q + 4h .. +3: chunk 4b + q, its half h
+                                const bf16x2 lo = __builtin_convertvector((f32x2{a[4 * q], a[4 * q + 1]}), bf16x2);
+                                const bf16x2 hi = __builtin_convertvector((f32x2{a[4 * q + 2], a[4 * q + 3]}), bf16x2);
+                                *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(
+                                    sw + rr * 128 + (((4 * b + q) ^ sx) << 4) + 8 * h) =
+                                    u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+                            } else {
+                                // columns 8q + 4h .. +3: chunk 2q + h
+                                *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
+                                    sw + rr * 128 + (((2 * q + h) ^ sx) << 4)) =
+                                    u32x4{__float_as_uint(a[4 * q]), __float_as_uint(a[4 * q + 1]),
+                                          __float_as_uint(a[4 * q + 2]), __float_as_uint(a[4 * q + 3])};
+                            }
+                        }
+                    }
+                }
+                wave_lds_sync();   // the round's rows are in the scratch
+#pragma unroll
+                for (int k = 0; k < CPL; ++k) {
+                    const int idx = lane + 64 * k, row = idx >> 3, c = idx & 7;
+                    const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+                        sw + row * 128 + ((c ^ (row & 7)) << 4));
+                    const int rowb = s * R + row;            // row within the 32-row block
+                    const int col = c0 + c * (16 / ES);
+                    const uint32_t o = r0 + rowb < rows && col < cols ? (uint32_t)((rowb * ld + col) * ES) : kOOB;
+                    __builtin_amdgcn_raw_buffer_store_b128(v, rs, o, 0, 0);
+                }
+                wave_lds_sync();   // read back before the next round overwrites it
+            }
         }
     }
 }
@@ -680,8 +776,20 @@ struct TileRunner {
     int nk, nk4, nk_nxt;
     bool has_next;
 
+    // The first step group of a tile accumulates onto zero instead of
+    // clearing the accumulators first.  Only with 8 waves, whose accumulators
+    // live in VGPRs: with 4 waves they sit in AGPRs, and the extra copy of
+    // the group makes the compiler move them out and spill.
+    static constexpr bool kPeel = WAVES == 8;
+
     static __device__ __forceinline__ int stages_of(const TileInfo& t) {
         return (t.A.klen + kStageK - 1) / kStageK;
+    }
+    // steps run for a tile of n stages: whole groups of kStages (the stages
+    // past n load zeros), at least the peeled group
+    static __device__ __forceinline__ int round4(int n) {
+        const int r = (n + kStages - 1) & ~(kStages - 1);
+        return kPeel && r < kStages ? kStages : r;
     }
 
     // The loads of step t (t % 4 == ST) for operand loader `ld`: stage t+4,
@@ -696,8 +804,8 @@ struct TileRunner {
         }
     }
 
-    // Step kt of the current tile; ST = kt % 4.
-    template <int ST, class Next>
+    // Step kt of the current tile; ST = kt % 4; FIRST for step 0.
+    template <int ST, bool FIRST = false, class Next>
     __device__ __forceinline__ void step(int kt, Next& next) {
         constexpr int NX = (ST + 1) % kStages;
         constexpr int NL = (AK && !(ST & 1) ? 0 : LA::kPerWave) + (BK && !(ST & 1) ? 0 : LB::kPerWave);
@@ -710,7 +818,7 @@ struct TileRunner {
         __builtin_amdgcn_sched_barrier(0);
         // sub-step 0: its MFMAs; the sub-step 1 fragments
         mma.template read<1, ST>(st, 1);
-        mma.template mfma<0>();
+        mma.template mfma<0, FIRST>();
         if constexpr (AK && BK) sched_interleave<Mma::kMfmas, Mma::kReads, 0>();
         __builtin_amdgcn_sched_barrier(0);
         // stage kt+1 has landed for every wave, and every wave is done
@@ -732,7 +840,7 @@ struct TileRunner {
         if (!more()) return;
         next(cur);
         nk = stages_of(cur);
-        nk4 = (nk + kStages - 1) & ~(kStages - 1);
+        nk4 = round4(nk);
         has_next = false;
         la.init(cur.A);
         lb.init(cur.B);
@@ -754,8 +862,17 @@ struct TileRunner {
         for (;;) {
             has_next = more();
             nk_nxt = 0;
-            mma.zero();
-            for (int kt = 0; kt < nk4; kt += kStages) {
+            int kt0 = 0;
+            if constexpr (kPeel) {
+                step<0, true>(0, next);
+                step<1>(1, next);
+                step<2>(2, next);
+                step<3>(3, next);
+                kt0 = kStages;
+            } else {
+                mma.zero();
+            }
+            for (int kt = kt0; kt < nk4; kt += kStages) {
                 step<0>(kt, next);
                 step<1>(kt + 1, next);
                 step<2>(kt + 2, next);
@@ -765,7 +882,7 @@ struct TileRunner {
             if (!has_next) break;
             cur = nxt;
             nk = nk_nxt;
-            nk4 = (nk + kStages - 1) & ~(kStages - 1);
+            nk4 = round4(nk);
         }
         // the masked loads past the last tile are still in flight
         __builtin_amdgcn_s_waitcnt(0);
@@ -803,6 +920,7 @@ template <int OP, int BM, int BN, bool OUT_BF16, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void gg_fwd_dgrad_kernel(GemmArgs a) {
     DRGG_STAGES(BM, BN, true, OP == 0, stg);
     __shared__ Sched sch;
+    __shared__ __attribute__((aligned(16))) char ep[WAVES * ep_rows(BM, BN) * 128];
     // output columns: N (forward) or K (data gradient)
     const int64_t ncols = OP == 0 ? a.N : a.K;
     const int32_t ntn = (int32_t)((ncols + BN - 1) / BN);
@@ -839,7 +957,7 @@ __global__ __launch_bounds__(64 * WAVES) void gg_fwd_dgrad_kernel(GemmArgs a) {
     auto finish = [&](const TileInfo& t, const TileMma<BM, BN, true, OP == 0, WAVES>& mma) {
         void* base = OUT_BF16 ? (void*)(reinterpret_cast<uint16_t*>(out) + t.o0 * ncols + t.o1)
                               : (void*)(reinterpret_cast<float*>(out) + t.o0 * ncols + t.o1);
-        store_tile<OUT_BF16>(mma, base, ncols, t.rows, t.cols);
+        store_tile_lines<OUT_BF16, ep_rows(BM, BN)>(mma, (lds_t*)ep, base, ncols, t.rows, t.cols);
     };
     TileRunner<BM, BN, true, OP == 0, WAVES> runner;
     runner.st = stg;

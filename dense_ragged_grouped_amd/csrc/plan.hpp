@@ -99,11 +99,20 @@ inline int64_t wgrad_max_partials(int64_t M, int64_t chunk_max) {
     return M <= 0 ? 0 : (2 * M) / chunk_max + 1;
 }
 
-// Workgroups of a persistent grouped-GEMM kernel that fit on one CU (LDS:
-// kStages stages of (BM + BN) x kStageK BF16 plus at most 14 KB of schedule
-// tables, out of 160 KB; each workgroup has 4 waves).
-inline int64_t wgs_per_cu(TileShape t) {
-    const int64_t lds = (int64_t)kStages * (t.bm + t.bn) * kStageK * 2 + 14 * 1024;
+// Rows per round of the staged epilogue of the forward and data-gradient
+// kernels (kernels.hip): its LDS scratch is that many 128-byte rows per
+// wave.  Tiles below 256x128 share a CU and get the smaller scratch.
+constexpr int ep_rows(int bm, int bn) { return bm * bn >= 256 * 128 ? 16 : 8; }
+// Workgroups of a persistent grouped-GEMM kernel that fit on one CU's 160 KB
+// of LDS: kStages stages of (BM + BN) x kStageK BF16, the schedule tables
+// (10 KB; the deterministic weight gradient adds 4 KB of partial-slot
+// bases), the forward/data-gradient epilogue scratch, and 1 KB for
+// alignment.  Workgroups have 4 waves, except the 8 of the 256x256 forward
+// and data-gradient kernels.
+inline int64_t wgs_per_cu(TileShape t, bool fwd_dgrad, bool det_wgrad) {
+    const int64_t waves = fwd_dgrad && t.bm == 256 && t.bn == 256 ? 8 : 4;
+    const int64_t lds = (int64_t)kStages * (t.bm + t.bn) * kStageK * 2 + 10248 + (det_wgrad ? 4100 : 0) +
+                        (fwd_dgrad ? waves * ep_rows(t.bm, t.bn) * 128 : 0) + 1024;
     const int64_t n = (160 * 1024) / lds;
     return n < 1 ? 1 : n;
 }
