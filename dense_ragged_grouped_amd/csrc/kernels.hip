@@ -197,6 +197,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFF0, 0x00020000);
 }
 constexpr uint32_t kOOB = 0xFFFFFFF0u;
+// Cache-policy operand of a buffer store: the non-temporal (nt) hint, for
+// output that this kernel never reads back, so that it is evicted before the
+// operand panels that the workgroups of an XCD share through L2.
+constexpr int kCpolNT = 2;
 
 // ---------------------------------------------------------------------------
 // main-loop pipeline
@@ -532,21 +536,6 @@ __device__ __forceinline__ void store_tile(const Mma& mma, void* out, int64_t ld
     }
 }
 
-// Write a finished tile like store_tile, but so that every global store
-// instruction writes whole 128-byte lines (R = ep_rows of the tile, from
-// plan.hpp, which sizes the LDS for it).  In the accumulator layout a
-// lane owns one row of each 32x32 block, so a direct store touches 32 rows
-// (32 lines, 16 or 32 bytes each) per instruction; written back-to-back by
-// every workgroup at a tile boundary, those partial lines cost more than the
-// rest of the epilogue.  Here each wave moves its blocks through its own
-// R x 128-byte LDS scratch `scr`: a 128-byte row segment (64 BF16 or 32 FP32
-// columns, i.e. two or one 32-column blocks) of R rows at a time, written by
-// the lanes that own those rows and read back as 16-byte chunks, eight lanes
-// per row, then stored with 16-byte buffer stores (R/8 rows of whole lines
-// per instruction).  Chunk c of scratch row rr sits at 16 * (c ^ (rr & 7)), so
-// the read-back is free of bank conflicts.  Masking as in store_tile; cols
-// must be a multiple of 8 (BF16) or 4 (FP32).  The scratch is private to the
-// wave, so a wave-level sync between the phases is all it needs.
 // Lanes of one wave exchanging data through LDS: the fences order each
 // lane's accesses before and after this point for the compiler (no
 // instruction is emitted; the wave's DS instructions execute in order).
@@ -556,6 +545,22 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Write a finished tile like store_tile, but so that every global store
+// instruction writes whole 128-byte lines (R = ep_rows of the tile, from
+// plan.hpp, which sizes the LDS for it), with the non-temporal hint.  In the
+// accumulator layout a lane owns one row of each 32x32 block, so a direct
+// store touches 32 rows (32 lines, 16 or 32 bytes each) per instruction;
+// written back-to-back by every workgroup at a tile boundary, those partial
+// lines cost more than the rest of the epilogue.  Here each wave moves its
+// blocks through its own R x 128-byte LDS scratch `scr`: a 128-byte row
+// segment (64 BF16 or 32 FP32 columns, i.e. two or one 32-column blocks) of R
+// rows at a time, written by the lanes that own those rows and read back as
+// 16-byte chunks, eight lanes per row, then stored with 16-byte buffer stores
+// (R/8 rows of whole lines per instruction).  Chunk c of scratch row rr sits
+// at 16 * (c ^ (rr & 7)), so the read-back is free of bank conflicts.  Masking
+// as in store_tile; cols must be a multiple of 8 (BF16) or 4 (FP32).  The
+// scratch is private to the wave, so a wave-level sync between the phases is
+// all it needs.
 template <bool OUT_BF16, int R, class Mma>
 __device__ __forceinline__ void store_tile_lines(const Mma& mma, lds_t* scr, void* out, int64_t ld, int rows,
                                                  int cols) {
@@ -617,7 +622,7 @@ __device__ __forceinline__ void store_tile_lines(const Mma& mma, lds_t* scr, voi
                     const int rowb = s * R + row;            // row within the 32-row block
                     const int col = c0 + c * (16 / ES);
                     const uint32_t o = r0 + rowb < rows && col < cols ? (uint32_t)((rowb * ld + col) * ES) : kOOB;
-                    __builtin_amdgcn_raw_buffer_store_b128(v, rs, o, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b128(v, rs, o, 0, kCpolNT);
                 }
                 wave_lds_sync();   // read back before the next round overwrites it
             }
@@ -792,12 +797,32 @@ struct TileRunner {
         return kPeel && r < kStages ? kStages : r;
     }
 
+    // With 8 waves the workgroup barrier is passed at odd steps only: the
+    // two waves of a SIMD stop issuing MFMAs at a barrier, and with two of
+    // them per SIMD that stall is the larger cost.  Every load is then issued
+    // at an odd step t (stages t+3 and t+4, into the buffers of stages t-1
+    // and t, which every wave has finished reading at that barrier), and the
+    // barrier waits for all loads in flight: those of stages t+1 and t+2,
+    // issued at the previous barrier, which steps t and t+1 read.
+    static constexpr bool kBar2 = WAVES == 8;
+
     // The loads of step t (t % 4 == ST) for operand loader `ld`: stage t+4,
-    // or for a K-major operand at odd t the pair t+3, t+4, of this tile or,
-    // past nk4, of the next one (the loaders then point at the next tile).
+    // or for a K-major operand at odd t the pair t+3, t+4 (with kBar2, an
+    // MN-major operand also loads stages t+3 and t+4 at odd t), of this tile
+    // or, past nk4, of the next one (the loaders then point at the next
+    // tile).
     template <int ST, bool K, class Ld>
     __device__ __forceinline__ void issue(Ld& ld, lds_t* const* bufs, int kt) {
-        if constexpr (!K || (ST & 1)) {
+        if constexpr (kBar2 && !K) {
+            if constexpr (ST & 1) {
+#pragma unroll
+                for (int d = 3; d <= 4; ++d) {
+                    const int L = kt + d;
+                    const int Ls = L < nk4 ? L : L - nk4;
+                    ld.issue(bufs[(ST + d) % kStages], Ls, L < nk4 || has_next);
+                }
+            }
+        } else if constexpr (!K || (ST & 1)) {
             const int L = kt + (K ? 3 : 4);
             const int Ls = L < nk4 ? L : L - nk4;
             ld.issue(bufs[(ST + (K ? 3 : 4)) % kStages], Ls, L < nk4 || has_next);
@@ -808,7 +833,9 @@ struct TileRunner {
     template <int ST, bool FIRST = false, class Next>
     __device__ __forceinline__ void step(int kt, Next& next) {
         constexpr int NX = (ST + 1) % kStages;
-        constexpr int NL = (AK && !(ST & 1) ? 0 : LA::kPerWave) + (BK && !(ST & 1) ? 0 : LB::kPerWave);
+        // loads issued in this step (the schedule hints place them)
+        constexpr int NL = kBar2 ? ((ST & 1) ? (AK ? 1 : 2) * LA::kPerWave + (BK ? 1 : 2) * LB::kPerWave : 0)
+                                 : (AK && !(ST & 1) ? 0 : LA::kPerWave) + (BK && !(ST & 1) ? 0 : LB::kPerWave);
         if (kt + kStages == nk4 && has_next) {
             next(nxt);
             nk_nxt = stages_of(nxt);
@@ -823,8 +850,10 @@ struct TileRunner {
         __builtin_amdgcn_sched_barrier(0);
         // stage kt+1 has landed for every wave, and every wave is done
         // reading stage kt
-        wait_vm_lgkm<Plan::at_barrier(4 + ST)>();
-        barrier_nofence();
+        if constexpr (!kBar2 || (ST & 1)) {
+            wait_vm_lgkm<kBar2 ? 0 : Plan::at_barrier(4 + ST)>();
+            barrier_nofence();
+        }
         // sub-step 1: its MFMAs; the loads into the buffers just freed; the
         // sub-step 0 fragments of stage kt+1
         issue<ST, AK>(la, st.a, kt);
@@ -856,7 +885,8 @@ struct TileRunner {
                 else lb.issue(st.b[L], L, true);
             }
         }
-        wait_vm_lgkm<Plan::prologue>();
+        // stage 0 landed (and with kBar2 stage 1 too, which step 0 reads)
+        wait_vm_lgkm<kBar2 ? Plan::after(1, -1) : Plan::prologue>();
         barrier_nofence();
         mma.template read<0, 0>(st, 0);
         for (;;) {
