@@ -169,8 +169,10 @@ def other_workloads(torch, drgg, synth, reps):
         X, G = to_dev_bf16(torch, p.X), to_dev_bf16(torch, p.G)
         offs = torch.from_numpy(p.offs).cuda()
         dW = torch.empty((1, p.N, p.K), dtype=torch.float32, device="cuda")
-        ws = drgg.Workspace()
         for det in (True, False):
+            # one workspace per variant: a deterministic call leaves partials
+            # where the non-deterministic program needs zeroed tile sums
+            ws = drgg.Workspace()
             fn = lambda: drgg.grouped_gemm_wgrad(X, G, offs, out_dtype=torch.float32, deterministic=det,
                                                  out=dW, workspace=ws)
             fn()

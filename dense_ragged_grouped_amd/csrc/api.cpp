@@ -76,6 +76,7 @@ struct Plan {
     size_t ws_bytes;
 };
 
+// ws layout, det weight gradient: [partial slots: max_partials*N*K fp32][fold table: E int32x4]
 // ws layout, non-det weight gradient: [tile sums: E*P*BM*BN fp32][tickets: E*P u32]
 drgg_status make_plan(drgg_op op, int32_t E, int64_t M, int64_t N, int64_t K, int det, int cu_count,
                       Plan* p) {
@@ -109,7 +110,8 @@ drgg_status make_plan(drgg_op op, int32_t E, int64_t M, int64_t N, int64_t K, in
         p->grid = grid_for(P * (M / p->chunk_max + E));
         int64_t b;
         if (!mul_ok(p->max_partials, N * K, &b) || !mul_ok(b, 4, &b)) return DRGG_EOVERFLOW;
-        p->ws_bytes = (size_t)b;
+        // followed by the per-expert fold table: E x {T_e, chunks_e, slot base, 0} int32
+        p->ws_bytes = b > 0 ? (size_t)(b + round_up((int64_t)E * 16, 256)) : 0;
     } else {
         p->grid = g_knob > 0 ? g_knob : resident;
         int64_t sums, tk;
@@ -237,6 +239,7 @@ drgg_status grouped_gemm_wgrad(const void* X, const void* G, const int32_t* grou
     const bool bf16 = out_dtype == DRGG_BF16;
     if (deterministic) {
         a.partial = static_cast<float*>(workspace);
+        a.fold_info = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + p.max_partials * N * K * 4);
         a.chunk_max = p.chunk_max;
         a.items_max = M > 0 ? p.grid : 0;
         return launch_status(launch_wgrad_det(p.tile, a, bf16, stream));

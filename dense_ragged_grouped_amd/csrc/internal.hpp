@@ -16,6 +16,7 @@ struct GemmArgs {
     const int32_t* offs;   // group offsets [E+1], device
     void* out;             // Y / dX / dW
     float* partial;        // det wgrad: chunk partial slots [slot][N][K]
+    int32_t* fold_info;    // det wgrad: [E][4] = T_e, chunks_e, first slot, 0 (chunk kernel -> fold)
     float* tilesum;        // non-det wgrad: FP32 tile sums [E*P][BM*BN]
     uint32_t* tickets;     // non-det wgrad: [E*P]
     int64_t M, N, K;

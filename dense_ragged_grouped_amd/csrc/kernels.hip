@@ -70,6 +70,12 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
 // ---------------------------------------------------------------------------
 // ragged work decode
 
+// LDS pointers keep their address space in the type, so that every access
+// compiles to ds_* instructions (a generic pointer would become a flat access
+// that also waits for outstanding global loads).
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) char lds_t;
+
 struct Sched {
     int32_t offs[kMaxExperts + 1];    // clamped, non-decreasing offsets
     int32_t prefix[kMaxExperts + 1];  // exclusive prefix of work per expert
@@ -129,6 +135,87 @@ __device__ void build_schedule(Sched& s, const int32_t* __restrict__ offs, int E
     __syncthreads();
 }
 
+// Weight-gradient work order: longest token chunks first.  Items of one
+// expert all cost about the same (a tile over one chunk of its tokens), so
+// the experts are put in decreasing order of chunk length (ties: expert
+// index) and, for the persistent walk below, the rounds alternate direction
+// ("snake"): the longest items of round r and the shortest of round r+1 land
+// on the same workgroup.  On the Zipf-routed E=32 workload that balances the
+// workgroups to 96 % of the mean load, against 81 % in expert order.  After
+// this, s.prefix[p] is the exclusive prefix of work in the new order and
+// expert_at(s, p) the expert at position p (stored as 16-bit values over
+// s.scan, which build_schedule no longer needs).  `scr` is 8 KB of LDS
+// that is free until the first stage load; `clen(T)` is an expert's chunk
+// length and `work(T)` its item count.  Must be called by all threads after
+// build_schedule; ends with a barrier.
+static_assert(kMaxExperts <= 2 * kMaxGemmThreads && kMaxExperts <= 32767, "16-bit expert order in Sched::scan");
+__device__ __forceinline__ int expert_at(const Sched& s, int p) {
+    return reinterpret_cast<const int16_t*>(s.scan)[p];
+}
+template <class LenFn, class WorkFn>
+__device__ void order_longest_first(Sched& s, lds_t* scr, int E, LenFn clen, WorkFn work) {
+    static_assert(kMaxExperts <= 4 * kGemmThreads, "at most four experts per thread");
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    auto* key = reinterpret_cast<__attribute__((address_space(3))) int32_t*>(scr);
+    auto* wk = key + kMaxExperts;
+    for (int e = tid; e < E; e += nthr) {
+        const int32_t T = s.offs[e + 1] - s.offs[e];
+        key[e] = clen(T);
+        wk[e] = work(T);
+    }
+    __syncthreads();
+    // rank of expert e: experts with a longer chunk, or as long and a lower
+    // index, go first; each thread ranks its (up to four) experts in one
+    // pass over the keys
+    int32_t k4[4], r4[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int e = tid + u * nthr;
+        k4[u] = e < E ? key[e] : 0;
+        r4[u] = 0;
+    }
+    for (int f = 0; f < E; ++f) {
+        const int32_t kf = key[f];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) r4[u] += kf > k4[u] || (kf == k4[u] && f < tid + u * nthr);
+    }
+    int16_t* perm = reinterpret_cast<int16_t*>(s.scan);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+        if (tid + u * nthr < E) perm[r4[u]] = (int16_t)(tid + u * nthr);
+    __syncthreads();
+    // exclusive prefix of the item counts in the new order: per-thread runs,
+    // then a serial scan of the run sums (in key[], no longer needed)
+    const int per = (E + nthr - 1) / nthr;
+    const int lo = min(tid * per, E), hi = min(lo + per, E);
+    int32_t run = 0;
+    for (int q = lo; q < hi; ++q) run += wk[perm[q]];
+    key[tid] = run;
+    __syncthreads();
+    if (tid == 0) {
+        int32_t acc = 0;
+        for (int t = 0; t < nthr; ++t) {
+            const int32_t v = key[t];
+            key[t] = acc;
+            acc += v;
+        }
+        s.prefix[E] = acc;
+    }
+    __syncthreads();
+    int32_t acc = key[tid];
+    for (int q = lo; q < hi; ++q) {
+        s.prefix[q] = acc;
+        acc += wk[perm[q]];
+    }
+    __syncthreads();
+}
+
+// Work item of round r for the workgroup at (XCD-remapped) index wb of G:
+// rounds alternate direction.
+__device__ __forceinline__ int64_t snake_item(int64_t r, int64_t wb, int64_t G) {
+    return r * G + ((r & 1) ? G - 1 - wb : wb);
+}
+
 // Values read from LDS arrive in vector registers even when every lane reads
 // the same address; the tile decode is wave-uniform, so it is moved to scalar
 // registers (keeps the per-tile state out of the VGPR budget).
@@ -182,11 +269,6 @@ struct Operand {
     int32_t klen;
 };
 
-// LDS pointers keep their address space in the type, so that every access
-// compiles to ds_* instructions (a generic pointer would become a flat access
-// that also waits for outstanding global loads).
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(3))) char lds_t;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
 
@@ -1018,18 +1100,29 @@ __global__ __launch_bounds__(kGemmThreads) void gg_wgrad_det_kernel(GemmArgs a) 
         slot_base[a.E] = sb;
     }
     __syncthreads();
+    // the fold kernel's per-expert table (the same values from every
+    // workgroup; workgroup 0 writes it)
+    if (blockIdx.x == 0)
+        for (int e = threadIdx.x; e < a.E; e += blockDim.x) {
+            const int32_t T = sch.offs[e + 1] - sch.offs[e];
+            *reinterpret_cast<int4*>(a.fold_info + 4 * e) = int4{T, chunks_dev(T, cmax), slot_base[e], 0};
+        }
+    order_longest_first(sch, stg.b[0], a.E, [=](int32_t T) { return chunk_len_dev(T, cmax); },
+                        [=](int32_t T) { return P * chunks_dev(T, cmax); });
     const int64_t total = uni(sch.prefix[a.E]);
     const int64_t G = gridDim.x;
-    int64_t w = xcd_remap(blockIdx.x, G);
-    if (a.reverse) w = G - 1 - w;
+    int64_t wb = xcd_remap(blockIdx.x, G), round = 0;
+    if (a.reverse) wb = G - 1 - wb;
+    int64_t w = snake_item(0, wb, G);
     auto more = [&]() { return w < total; };
     auto next = [&](TileInfo& t) {
-        const int e = uni(find_expert(sch, a.E, (int32_t)w));
+        const int pos = uni(find_expert(sch, a.E, (int32_t)w));
+        const int e = uni(expert_at(sch, pos));
         const int32_t oe = uni(sch.offs[e]), oe1 = uni(sch.offs[e + 1]);
         const int32_t T = oe1 - oe;
         const int32_t clen = chunk_len_dev(T, cmax);
         const int32_t nch = (T + clen - 1) / clen;
-        const int32_t local = (int32_t)w - uni(sch.prefix[e]);
+        const int32_t local = (int32_t)w - uni(sch.prefix[pos]);
         const int32_t chunk = local / P, tile = local % P;   // chunk-major: tiles of a chunk adjacent
         const int32_t ti = tile / tk, tj = tile % tk;
         const int64_t n0 = (int64_t)ti * BM, k0 = (int64_t)tj * BN;
@@ -1044,7 +1137,7 @@ __global__ __launch_bounds__(kGemmThreads) void gg_wgrad_det_kernel(GemmArgs a) 
         // dW[n][k] = sum_t G[t][n] X[t][k]: both operands token-major (MN-major)
         t.A = Operand{a.A + tb * a.N + n0, a.N, t.rows, len};
         t.B = Operand{a.B + tb * a.K + k0, a.K, t.cols, len};
-        w += G;
+        w = snake_item(++round, wb, G);
     };
     auto finish = [&](const TileInfo& t, const TileMma<BM, BN, false, false>& mma) {
         const int64_t ld = a.K;
@@ -1069,29 +1162,15 @@ __global__ __launch_bounds__(kGemmThreads) void gg_wgrad_det_kernel(GemmArgs a) 
 template <bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void gg_wgrad_fold_kernel(GemmArgs a) {
     const int e = blockIdx.y;
-    __shared__ int32_t s_info[3];   // T_e, chunks_e, slot base
-    if (threadIdx.x == 0) {
-        // clamp like build_schedule: offsets into [0, M], running max
-        int64_t run = 0, sb = 0, Te = 0, ce = 0;
-        int64_t prev = 0;
-        for (int x = 0; x <= e + 1 && x <= a.E; ++x) {
-            int64_t v = a.offs[x];
-            v = v < 0 ? 0 : (v > a.M ? a.M : v);
-            run = v > run ? v : run;
-            if (x > 0) {
-                const int64_t T = run - prev;
-                const int32_t c = chunks_dev((int32_t)T, a.chunk_max);
-                if (x - 1 < e && c > 1) sb += c;
-                if (x - 1 == e) { Te = T; ce = c; }
-            }
-            prev = run;
-        }
-        s_info[0] = (int32_t)Te;
-        s_info[1] = (int32_t)ce;
-        s_info[2] = (int32_t)sb;
+    // T_e, chunks_e and the first partial slot, from the chunk kernel's
+    // table; with M = 0 that kernel does not run and every expert is empty
+    int32_t Te = 0, ce = 0, sb = 0;
+    if (a.M > 0) {
+        const int4 info = *reinterpret_cast<const int4*>(a.fold_info + 4 * e);
+        Te = info.x;
+        ce = info.y;
+        sb = info.z;
     }
-    __syncthreads();
-    const int32_t Te = s_info[0], ce = s_info[1], sb = s_info[2];
     if (Te > 0 && ce <= 1) return;   // written directly by the chunk kernel
     const int64_t nk = a.N * a.K;
     const int64_t i0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 8;
@@ -1106,10 +1185,26 @@ __global__ __launch_bounds__(kThreads) void gg_wgrad_fold_kernel(GemmArgs a) {
         f32x4 x1 = *reinterpret_cast<const f32x4*>(p + 4);
 #pragma unroll
         for (int j = 0; j < 4; ++j) { s[j] = x0[j]; s[4 + j] = x1[j]; }
-        for (int c = 1; c < ce; ++c) {
-            p += nk;
-            x0 = *reinterpret_cast<const f32x4*>(p);
-            x1 = *reinterpret_cast<const f32x4*>(p + 4);
+        // chunks 1 .. ce-1, added in chunk order; the loads of up to four
+        // chunks are in flight at once
+        int c = 1;
+        for (; c + 4 <= ce; c += 4) {
+            f32x4 y[4][2];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float* q = p + (int64_t)(c + u) * nk;
+                y[u][0] = *reinterpret_cast<const f32x4*>(q);
+                y[u][1] = *reinterpret_cast<const f32x4*>(q + 4);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) { s[j] += y[u][0][j]; s[4 + j] += y[u][1][j]; }
+        }
+        for (; c < ce; ++c) {
+            const float* q = p + (int64_t)c * nk;
+            x0 = *reinterpret_cast<const f32x4*>(q);
+            x1 = *reinterpret_cast<const f32x4*>(q + 4);
 #pragma unroll
             for (int j = 0; j < 4; ++j) { s[j] += x0[j]; s[4 + j] += x1[j]; }
         }
@@ -1153,19 +1248,23 @@ __global__ __launch_bounds__(kGemmThreads) void gg_wgrad_atomic_kernel(GemmArgs 
     const int32_t P = tn * tk;
     const int64_t cmax = a.chunk_max;
     build_schedule(sch, a.offs, a.E, a.M, [=](int, int32_t T) { return P * unit_chunks(T, cmax); });
+    order_longest_first(sch, stg.b[0], a.E, [=](int32_t T) { return unit_chunk_len(T, cmax); },
+                        [=](int32_t T) { return P * unit_chunks(T, cmax); });
     const int64_t total = uni(sch.prefix[a.E]);
     const int64_t G = gridDim.x;
     const int64_t b = blockIdx.x;
-    int64_t w = xcd_remap(blockIdx.x, G);
-    if (a.reverse) w = G - 1 - w;
+    int64_t wb = xcd_remap(blockIdx.x, G), round = 0;
+    if (a.reverse) wb = G - 1 - wb;
+    int64_t w = snake_item(0, wb, G);
     auto more = [&]() { return w < total; };
     auto next = [&](TileInfo& t) {
-        const int e = uni(find_expert(sch, a.E, (int32_t)w));
+        const int pos = uni(find_expert(sch, a.E, (int32_t)w));
+        const int e = uni(expert_at(sch, pos));
         const int32_t oe = uni(sch.offs[e]), oe1 = uni(sch.offs[e + 1]);
         const int32_t T = oe1 - oe;
         const int32_t clen = unit_chunk_len(T, cmax);
         const int32_t nch = (T + clen - 1) / clen;
-        const int32_t local = (int32_t)w - uni(sch.prefix[e]);
+        const int32_t local = (int32_t)w - uni(sch.prefix[pos]);
         const int32_t chunk = local / P, tile = local % P;   // chunk-major: tiles of a chunk adjacent
         const int32_t ti = tile / tk, tj = tile % tk;
         const int64_t n0 = (int64_t)ti * BM, k0 = (int64_t)tj * BN;
@@ -1180,7 +1279,7 @@ __global__ __launch_bounds__(kGemmThreads) void gg_wgrad_atomic_kernel(GemmArgs 
         t.aux2 = nch;                   // pieces of a split tile
         t.A = Operand{a.A + tb * a.N + n0, a.N, t.rows, len};
         t.B = Operand{a.B + tb * a.K + k0, a.K, t.cols, len};
-        w += G;
+        w = snake_item(++round, wb, G);
     };
     auto finish = [&](const TileInfo& t, const TileMma<BM, BN, false, false>& mma) {
         const int64_t base = (int64_t)t.e * a.N * a.K + t.o0 * a.K + t.o1;

@@ -125,7 +125,9 @@ drgg_status grouped_gemm_dgrad(const void *G, const void *W, const int32_t *grou
  * experts without tokens get dW[e] = +0.  X [M,K] BF16, G [M,N] BF16,
  * dW [E,N,K] out_dtype.
  * Workspace: at least grouped_gemm_workspace_size(DRGG_OP_WGRAD, ...) bytes.
- *   deterministic != 0: FP32 chunk partials; no initialisation needed.
+ *   deterministic != 0: FP32 chunk partials and a small per-expert table
+ *     that the chunk kernel writes for the ordered fold; no initialisation
+ *     needed.
  *   deterministic == 0: FP32 tile sums and tickets that must be zero before
  *     the first call (drgg_workspace_init); every call leaves them zero
  *     again.  A buffer that served a deterministic call holds partials
