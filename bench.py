@@ -173,10 +173,14 @@ def other_workloads(torch, drgg, synth, reps):
             # one workspace per variant: a deterministic call leaves partials
             # where the non-deterministic program needs zeroed tile sums
             ws = drgg.Workspace()
+            # "splitk": the split program, which the library's default
+            # route replaces by the deterministic one
+            drgg.set_knob(drgg.KNOB_NONDET, 0 if det else 1)
             fn = lambda: drgg.grouped_gemm_wgrad(X, G, offs, out_dtype=torch.float32, deterministic=det,
                                                  out=dW, workspace=ws)
             fn()
             t = time_call(torch, drgg, fn, reps)
+            drgg.set_knob(drgg.KNOB_NONDET, 0)
             ms = sum(t.values())
             flop = 2.0 * p.M * p.N * p.K
             byt = 2.0 * p.M * (p.N + p.K) + 4.0 * p.N * p.K
@@ -189,10 +193,12 @@ def other_workloads(torch, drgg, synth, reps):
     dW = torch.empty((p.E, p.N, p.K), dtype=torch.float32, device="cuda")
     for det in (True, False):
         ws = drgg.Workspace()
+        drgg.set_knob(drgg.KNOB_NONDET, 0 if det else 1)
         fn = lambda: drgg.grouped_gemm_wgrad(X, G, offs, out_dtype=torch.float32, deterministic=det,
                                              out=dW, workspace=ws)
         fn()
         t = time_call(torch, drgg, fn, reps)
+        drgg.set_knob(drgg.KNOB_NONDET, 0)
         ms = sum(t.values())
         flop = 2.0 * p.M * p.N * p.K
         out[f"moe_down_zipf_wgrad_{'det' if det else 'splitk'}"] = {

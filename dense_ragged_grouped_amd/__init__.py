@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(_HERE, "libdrgg.so")
 
 BF16, FP32 = 0, 1
 OP_FWD, OP_DGRAD, OP_WGRAD = 0, 1, 2
-KNOB_TILE, KNOB_GRID, KNOB_REVERSE, KNOB_TIMING = 1, 2, 3, 4
+KNOB_TILE, KNOB_GRID, KNOB_REVERSE, KNOB_TIMING, KNOB_NONDET = 1, 2, 3, 4, 5
 TILE_AUTO, TILE_256x256, TILE_128x128, TILE_256x128, TILE_128x256, TILE_64x256 = range(6)
 
 # the symbols include/drgg.h declares
@@ -125,9 +125,18 @@ def wgrad_chunking(T: int, chunk_max: int):
     return ln.value, n.value
 
 
+# the program a non-deterministic weight gradient runs (KNOB_NONDET): False =
+# routed to the deterministic one (the library default), True = split program
+_split_nondet = False
+
+
 def set_knob(knob: int, value: int):
-    """Test knobs (tile shape, stream-K grid, reverse walk); 0 restores the default."""
+    """Test knobs (tile shape, stream-K grid, reverse walk, timing, split
+    program for non-deterministic weight gradients); 0 restores the default."""
+    global _split_nondet
     _check(lib.drgg_set_knob(knob, int(value)), "drgg_set_knob")
+    if knob == KNOB_NONDET:
+        _split_nondet = bool(value)
 
 
 def last_call_kernel_times():
@@ -208,9 +217,9 @@ class Workspace:
         return self.buf
 
 
-# Default workspaces, one per (device, variant): a deterministic call leaves
-# its FP32 partials in the buffer, while the non-deterministic program needs
-# its tile sums and tickets to be zero, so the two never share a buffer.
+# Default workspaces, one per (device, program): a deterministic call leaves
+# its FP32 partials in the buffer, while the split program needs its tile
+# sums and tickets to be zero, so the two never share a buffer.
 _default_ws = {}
 
 
@@ -218,7 +227,9 @@ def _workspace(device, nbytes, workspace, deterministic):
     if workspace is not None:
         buf = workspace.get(nbytes) if isinstance(workspace, Workspace) else workspace
     else:
-        key = (str(device), bool(deterministic))
+        # keyed by the program that runs: a routed non-deterministic call
+        # shares the deterministic buffer
+        key = (str(device), bool(deterministic) or not _split_nondet)
         if key not in _default_ws:
             _default_ws[key] = Workspace(device)
         buf = _default_ws[key].get(nbytes)

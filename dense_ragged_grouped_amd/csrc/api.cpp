@@ -18,7 +18,7 @@ namespace drgg {
 
 namespace {
 
-std::atomic<int64_t> g_knob_tile{0}, g_knob_grid{0}, g_knob_reverse{0};
+std::atomic<int64_t> g_knob_tile{0}, g_knob_grid{0}, g_knob_reverse{0}, g_knob_nondet{0};
 
 constexpr int64_t kMaxBytes = (int64_t)1 << 62;
 constexpr int kMaxDevices = 64;
@@ -74,6 +74,7 @@ struct Plan {
     int64_t chunk_max;
     int64_t max_partials;
     size_t ws_bytes;
+    int det;   // weight gradient: the program that runs (1 = deterministic)
 };
 
 // ws layout, det weight gradient: [partial slots: max_partials*N*K fp32][fold table: E int32x4]
@@ -81,6 +82,14 @@ struct Plan {
 drgg_status make_plan(drgg_op op, int32_t E, int64_t M, int64_t N, int64_t K, int det, int cu_count,
                       Plan* p) {
     std::memset(p, 0, sizeof *p);
+    // Route table for the non-deterministic weight gradient: on gfx950 the
+    // deterministic program (chunk partials + ordered fold) was faster at
+    // every measured shape, because the atomic tile sums of the split
+    // program are performed beyond the XCDs' L2s; its result is a valid
+    // non-deterministic result.  DRGG_KNOB_NONDET = 1 keeps the atomic
+    // program.
+    if (op == DRGG_OP_WGRAD && !det && g_knob_nondet.load() == 0) det = 1;
+    p->det = det;
     int tile = (int)g_knob_tile.load();
     if (tile < kTileAuto || tile > kTile64x256) tile = kTileAuto;
     if (tile == kTile64x256 && op != DRGG_OP_WGRAD) tile = kTileAuto;
@@ -237,7 +246,7 @@ drgg_status grouped_gemm_wgrad(const void* X, const void* G, const int32_t* grou
     a.M = M; a.N = N; a.K = K; a.E = E;
     a.reverse = (int32_t)(g_knob_reverse.load() != 0);
     const bool bf16 = out_dtype == DRGG_BF16;
-    if (deterministic) {
+    if (p.det) {
         a.partial = static_cast<float*>(workspace);
         a.fold_info = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + p.max_partials * N * K * 4);
         a.chunk_max = p.chunk_max;
@@ -310,7 +319,7 @@ drgg_status drgg_plan(drgg_op op, int32_t E, int64_t M, int64_t N, int64_t K, dr
     out->mfma_k = kMfmaK;
     out->grid = p.grid;
     out->chunk_max = p.chunk_max;
-    out->unit = (op == DRGG_OP_WGRAD && !deterministic) ? kStreamKUnit : 0;
+    out->unit = (op == DRGG_OP_WGRAD && !p.det) ? kStreamKUnit : 0;
     out->max_partials = p.max_partials;
     out->workspace_bytes = p.ws_bytes;
     return DRGG_OK;
@@ -338,6 +347,9 @@ drgg_status drgg_set_knob(int knob, int64_t value) {
             return DRGG_OK;
         case DRGG_KNOB_TIMING:
             g_timing_on.store(value != 0);
+            return DRGG_OK;
+        case DRGG_KNOB_NONDET:
+            g_knob_nondet.store(value != 0);
             return DRGG_OK;
         default:
             return DRGG_EINVAL;

@@ -31,7 +31,11 @@
  *                       (never on the device), writes one FP32 partial per
  *                       chunk and folds the partials in chunk order before a
  *                       single rounding.
- *   deterministic == 0  the weight gradient cuts an expert's token range into
+ *   deterministic == 0  routed by default to the deterministic program (whose
+ *                       result is a valid non-deterministic result): on
+ *                       gfx950 it was the faster one at every measured shape.
+ *                       With DRGG_KNOB_NONDET = 1 the split program runs:
+ *                       the weight gradient cuts an expert's token range into
  *                       chunks of whole 512-token units (the deterministic
  *                       chunk lengths rounded up); the pieces of a tile cut
  *                       into several chunks add their FP32 partials into an
@@ -128,10 +132,12 @@ drgg_status grouped_gemm_dgrad(const void *G, const void *W, const int32_t *grou
  *   deterministic != 0: FP32 chunk partials and a small per-expert table
  *     that the chunk kernel writes for the ordered fold; no initialisation
  *     needed.
- *   deterministic == 0: FP32 tile sums and tickets that must be zero before
- *     the first call (drgg_workspace_init); every call leaves them zero
- *     again.  A buffer that served a deterministic call holds partials
- *     afterwards and must be zeroed again before a non-deterministic call.
+ *   deterministic == 0, routed (the default): as deterministic != 0.
+ *   deterministic == 0, split program (DRGG_KNOB_NONDET = 1): FP32 tile sums
+ *     and tickets that must be zero before the first call
+ *     (drgg_workspace_init); every call leaves them zero again.  A buffer
+ *     that served a deterministic (or routed) call holds partials afterwards
+ *     and must be zeroed again before a split-program call.
  *   Two calls in flight at once must not share a workspace.
  */
 drgg_status grouped_gemm_wgrad(const void *X, const void *G, const int32_t *group_offsets,
@@ -174,7 +180,7 @@ typedef struct {
     int32_t mfma_m, mfma_n, mfma_k;   /* MFMA instruction shape               */
     int64_t grid;                     /* workgroups launched (persistent)     */
     int64_t chunk_max;                /* wgrad det: longest token chunk; 0 otherwise */
-    int64_t unit;                     /* wgrad non-det: token units; 0 otherwise */
+    int64_t unit;                     /* wgrad split program: token units; 0 otherwise */
     int64_t max_partials;             /* wgrad det: partial slots reserved     */
     size_t workspace_bytes;
 } drgg_plan_info;
@@ -197,12 +203,17 @@ drgg_status drgg_wgrad_chunking(int64_t T, int64_t chunk_max, int64_t *chunk_len
  *   DRGG_KNOB_GRID        force the workgroup count of the persistent kernels
  *                         (every program)
  *   DRGG_KNOB_REVERSE     1 = walk the work items in reverse order
+ *   DRGG_KNOB_NONDET      1 = a non-deterministic weight gradient runs the
+ *                         split program (atomic tile sums) instead of being
+ *                         routed to the deterministic one; the workspace
+ *                         size and plan follow the program chosen
  *   DRGG_KNOB_TIMING      1 = record a HIP event on the stream before every
  *                         kernel launch of a call and after its last launch
  *                         (read back with drgg_timing_read)
  * None of them changes the arithmetic of the deterministic variant.
  */
-enum { DRGG_KNOB_TILE = 1, DRGG_KNOB_GRID = 2, DRGG_KNOB_REVERSE = 3, DRGG_KNOB_TIMING = 4 };
+enum { DRGG_KNOB_TILE = 1, DRGG_KNOB_GRID = 2, DRGG_KNOB_REVERSE = 3, DRGG_KNOB_TIMING = 4,
+       DRGG_KNOB_NONDET = 5 };
 drgg_status drgg_set_knob(int knob, int64_t value);
 
 /*

@@ -31,6 +31,9 @@ def drgg():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     import dense_ragged_grouped_amd as d
+    # non-deterministic calls in these tests exercise the split program
+    # (by default the library routes them to the deterministic one)
+    d.set_knob(d.KNOB_NONDET, 1)
     return d
 
 
@@ -50,6 +53,21 @@ def test_deterministic_20_runs_bitwise(drgg, program):
         for i in range(19):
             got = bits(run_program(drgg, program, dv, out_dtype, True))
             assert np.array_equal(got, ref), f"run {i + 2} differs"
+
+
+def test_nondet_default_route_runs_the_det_program(drgg):
+    """With the library's default route a non-deterministic weight gradient
+    runs the deterministic program: bitwise the deterministic result."""
+    prob = ragged_problem(*DET_CASE)
+    dv = dev_inputs(prob)
+    for out_dtype in (torch.float32, torch.bfloat16):
+        det = bits(run_program(drgg, "wgrad", dv, out_dtype, True))
+        drgg.set_knob(drgg.KNOB_NONDET, 0)
+        try:
+            nd = bits(run_program(drgg, "wgrad", dv, out_dtype, False))
+        finally:
+            drgg.set_knob(drgg.KNOB_NONDET, 1)
+        assert np.array_equal(nd, det)
 
 
 @pytest.mark.parametrize("program", ["fwd", "dgrad", "wgrad"])

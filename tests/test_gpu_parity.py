@@ -21,6 +21,9 @@ def drgg():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     import dense_ragged_grouped_amd as d
+    # non-deterministic calls in these tests exercise the split program
+    # (by default the library routes them to the deterministic one)
+    d.set_knob(d.KNOB_NONDET, 1)
     return d
 
 

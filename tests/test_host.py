@@ -193,11 +193,31 @@ def test_grid_and_slot_bounds_cover_every_distribution(drgg, name):
 
 
 def test_nondet_plan_uses_the_cu_count_and_unit(drgg):
-    p = drgg.plan(drgg.OP_WGRAD, 32, 131072, 2048, 768, drgg.FP32, False, 256)
-    assert p["grid"] == 256 and p["unit"] == 512            # one 256x256 workgroup per CU
-    P = (2048 // 256) * (768 // 256)
-    assert p["workspace_bytes"] >= 32 * P * 256 * 256 * 4 + 32 * P * 4
-    assert drgg.plan(drgg.OP_WGRAD, 32, 131072, 2048, 768, drgg.FP32, False, 80)["grid"] == 80
+    drgg.set_knob(drgg.KNOB_NONDET, 1)   # the split program
+    try:
+        p = drgg.plan(drgg.OP_WGRAD, 32, 131072, 2048, 768, drgg.FP32, False, 256)
+        assert p["grid"] == 256 and p["unit"] == 512            # one 256x256 workgroup per CU
+        P = (2048 // 256) * (768 // 256)
+        assert p["workspace_bytes"] >= 32 * P * 256 * 256 * 4 + 32 * P * 4
+        assert drgg.plan(drgg.OP_WGRAD, 32, 131072, 2048, 768, drgg.FP32, False, 80)["grid"] == 80
+    finally:
+        drgg.set_knob(drgg.KNOB_NONDET, 0)
+
+
+def test_nondet_routes_to_the_det_program_by_default(drgg):
+    # the default route runs the deterministic program: its plan and
+    # workspace; the split program only with the knob
+    for E, M, N, K in ((32, 131072, 2048, 768), (8, 131072, 1536, 2048), (1, 16384, 48, 4096)):
+        det = drgg.plan(drgg.OP_WGRAD, E, M, N, K, drgg.FP32, True, 256)
+        nd = drgg.plan(drgg.OP_WGRAD, E, M, N, K, drgg.FP32, False, 256)
+        assert nd == det
+        assert drgg.workspace_size(drgg.OP_WGRAD, E, M, N, K, drgg.FP32, False) == \
+            drgg.workspace_size(drgg.OP_WGRAD, E, M, N, K, drgg.FP32, True)
+        drgg.set_knob(drgg.KNOB_NONDET, 1)
+        try:
+            assert drgg.plan(drgg.OP_WGRAD, E, M, N, K, drgg.FP32, False, 256)["unit"] == 512
+        finally:
+            drgg.set_knob(drgg.KNOB_NONDET, 0)
     drgg.set_knob(drgg.KNOB_GRID, 7)
     try:
         assert drgg.plan(drgg.OP_WGRAD, 32, 131072, 2048, 768, drgg.FP32, False, 256)["grid"] == 7
