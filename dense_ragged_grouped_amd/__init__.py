@@ -223,13 +223,15 @@ class Workspace:
 _default_ws = {}
 
 
-def _workspace(device, nbytes, workspace, deterministic):
+def _workspace(device, nbytes, workspace, deterministic, kind="wgrad"):
+    if workspace is False:   # explicitly none (the data gradient's direct program)
+        return None, 0
     if workspace is not None:
         buf = workspace.get(nbytes) if isinstance(workspace, Workspace) else workspace
     else:
         # keyed by the program that runs: a routed non-deterministic call
-        # shares the deterministic buffer
-        key = (str(device), bool(deterministic) or not _split_nondet)
+        # shares the deterministic buffer; the data gradient's W^T has its own
+        key = (str(device), "dgrad") if kind == "dgrad" else (str(device), bool(deterministic) or not _split_nondet)
         if key not in _default_ws:
             _default_ws[key] = Workspace(device)
         buf = _default_ws[key].get(nbytes)
@@ -267,8 +269,11 @@ def grouped_gemm_fwd(X, W, group_offsets, out_dtype=None, deterministic=True, ou
     return out
 
 
-def grouped_gemm_dgrad(G, W, group_offsets, out_dtype=None, deterministic=True, out=None, stream=None):
-    """dX[t] = G[t] W[e(t)] with FP32 accumulation."""
+def grouped_gemm_dgrad(G, W, group_offsets, out_dtype=None, deterministic=True, out=None, workspace=None,
+                       stream=None):
+    """dX[t] = G[t] W[e(t)] with FP32 accumulation.  `workspace` (a Workspace,
+    a device tensor, None for the default buffer, or False for none) holds
+    W^T, which makes the product faster; the result is bitwise the same."""
     torch = _torch()
     _need(G, torch.bfloat16, "G", 2)
     _need(W, torch.bfloat16, "W", 3)
@@ -284,8 +289,11 @@ def grouped_gemm_dgrad(G, W, group_offsets, out_dtype=None, deterministic=True, 
         _need(out, _torch_dtype(code), "out", 2)
         if tuple(out.shape) != (M, K):
             raise ValueError("out has the wrong shape")
+    nbytes = workspace_size(OP_DGRAD, E, M, N, K, code, deterministic)
+    ws_ptr, ws_bytes = _workspace(G.device, nbytes, workspace, deterministic, kind="dgrad")
     st = lib.grouped_gemm_dgrad(G.data_ptr(), W.data_ptr(), group_offsets.data_ptr(), E, M, N, K, code,
-                                int(bool(deterministic)), out.data_ptr(), None, 0, _stream(G.device, stream))
+                                int(bool(deterministic)), out.data_ptr(), ws_ptr, ws_bytes,
+                                _stream(G.device, stream))
     _check(st, "grouped_gemm_dgrad")
     return out
 

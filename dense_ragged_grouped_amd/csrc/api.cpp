@@ -109,6 +109,11 @@ drgg_status make_plan(drgg_op op, int32_t E, int64_t M, int64_t N, int64_t K, in
     if (op == DRGG_OP_FWD || op == DRGG_OP_DGRAD) {
         const int64_t ncols = op == DRGG_OP_FWD ? N : K;
         p->grid = grid_for((M / bm + E) * ceil_div(ncols, bn));
+        if (op == DRGG_OP_DGRAD) {   // optional: room for W^T
+            int64_t b;
+            if (!mul_ok((int64_t)E * N, K, &b) || !mul_ok(b, 2, &b)) return DRGG_EOVERFLOW;
+            p->ws_bytes = (size_t)round_up(b, 256);
+        }
         return p->grid > INT32_MAX ? DRGG_ESHAPE : DRGG_OK;
     }
     const int64_t P = ceil_div(N, bm) * ceil_div(K, bn);
@@ -169,8 +174,12 @@ void timing_end(hipStream_t s) {
 
 namespace {
 
+// WT: for the data gradient, a workspace of at least E*N*K*2 bytes to hold
+// W^T (then W is transposed into it and the data gradient runs with both
+// operands reduction-contiguous), or null (W read transposed in the kernel).
 drgg_status run_fwd_dgrad(drgg_op op, const void* A, const void* W, const int32_t* offs, int32_t E,
-                          int64_t M, int64_t N, int64_t K, drgg_dtype dt, void* out, hipStream_t s) {
+                          int64_t M, int64_t N, int64_t K, drgg_dtype dt, void* out, hipStream_t s,
+                          void* WT = nullptr) {
     drgg_status st = check_problem(E, M, N, K, dt);
     if (st != DRGG_OK) return st;
     // with no tokens the token-indexed buffers may be empty (null)
@@ -192,6 +201,12 @@ drgg_status run_fwd_dgrad(drgg_op op, const void* A, const void* W, const int32_
     a.M = M; a.N = N; a.K = K; a.E = E;
     a.items_max = p.grid;
     a.reverse = (int32_t)(g_knob_reverse.load() != 0);
+    if (op == DRGG_OP_DGRAD && WT) {
+        hipError_t e = launch_transpose_w(a.B, static_cast<uint16_t*>(WT), E, N, K, s);
+        if (e != hipSuccess) return DRGG_EDEVICE;
+        a.B = static_cast<const uint16_t*>(WT);
+        return launch_status(launch_fwd_dgrad(2, p.tile, a, dt == DRGG_BF16, s));
+    }
     return launch_status(launch_fwd_dgrad((int)op, p.tile, a, dt == DRGG_BF16, s));
 }
 
@@ -212,8 +227,20 @@ drgg_status grouped_gemm_fwd(const void* X, const void* W, const int32_t* group_
 drgg_status grouped_gemm_dgrad(const void* G, const void* W, const int32_t* group_offsets, int32_t E,
                                int64_t M, int64_t N, int64_t K, drgg_dtype out_dtype, int deterministic,
                                void* dX, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    (void)deterministic; (void)workspace; (void)workspace_bytes;
-    return run_fwd_dgrad(DRGG_OP_DGRAD, G, W, group_offsets, E, M, N, K, out_dtype, dX, stream);
+    (void)deterministic;
+    // with a large enough workspace, W^T goes there (the faster program;
+    // the results are bitwise the same either way)
+    drgg_status st = check_problem(E, M, N, K, out_dtype);
+    if (st != DRGG_OK) return st;
+    Plan p;
+    st = make_plan(DRGG_OP_DGRAD, E, M, N, K, 1, 1, &p);
+    if (st != DRGG_OK) return st;
+    void* WT = nullptr;
+    if (workspace && workspace_bytes >= p.ws_bytes && p.ws_bytes > 0) {
+        if (!aligned16(workspace)) return DRGG_EALIGN;
+        WT = workspace;
+    }
+    return run_fwd_dgrad(DRGG_OP_DGRAD, G, W, group_offsets, E, M, N, K, out_dtype, dX, stream, WT);
 }
 
 drgg_status grouped_gemm_wgrad(const void* X, const void* G, const int32_t* group_offsets, int32_t E,

@@ -26,7 +26,9 @@ struct GemmArgs {
     int32_t reverse;       // walk work items in reverse (test knob)
 };
 
+// op 0: forward; 1: data gradient; 2: data gradient with a.B = W^T [E][K][N]
 hipError_t launch_fwd_dgrad(int op, int tile, const GemmArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_transpose_w(const uint16_t* W, uint16_t* WT, int32_t E, int64_t N, int64_t K, hipStream_t s);
 hipError_t launch_wgrad_det(int tile, const GemmArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_wgrad_atomic(int tile, const GemmArgs& a, int64_t grid_n, bool bf16, hipStream_t s);
 hipError_t launch_router(const float* X, const float* Wr, float* out, int64_t M, int64_t N, int64_t K,

@@ -1022,6 +1022,50 @@ __device__ __forceinline__ void store4(void* out, int64_t idx, f32x4 v) {
 }
 
 // ---------------------------------------------------------------------------
+// W^T for the data gradient: WT[e][k][n] = W[e][n][k] (BF16 bits), in 64x64
+// tiles through LDS.  Grid (ceil(K/64), ceil(N/64), E), 256 threads; each
+// thread reads two 16-byte row pieces of W and writes two of WT, so both
+// sides are whole 16-byte, row-contiguous accesses.  N and K are multiples
+// of 8, so a 16-byte piece is either inside the matrix or wholly outside.
+// The tile is kept in LDS with a row pitch of 66 values, which spreads the
+// column reads of the write-out over the banks.
+__global__ __launch_bounds__(kThreads) void gg_transpose_w_kernel(const uint16_t* __restrict__ W,
+                                                                  uint16_t* __restrict__ WT, int64_t N,
+                                                                  int64_t K) {
+    constexpr int P = 66;
+    __shared__ uint16_t t[64 * P];
+    const int64_t e = blockIdx.z, n0 = (int64_t)blockIdx.y * 64, k0 = (int64_t)blockIdx.x * 64;
+    const uint16_t* src = W + e * N * K;
+    uint16_t* dst = WT + e * N * K;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int c = threadIdx.x + i * kThreads, r = c >> 3, q = c & 7;   // tile row n0+r, columns k0+8q..
+        const int64_t n = n0 + r, k = k0 + 8 * q;
+        if (n < N && k < K) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(src + n * K + k);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                t[r * P + 8 * q + 2 * j] = (uint16_t)(v[j] & 0xFFFFu);
+                t[r * P + 8 * q + 2 * j + 1] = (uint16_t)(v[j] >> 16);
+            }
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int c = threadIdx.x + i * kThreads, r = c >> 3, q = c & 7;   // WT row k0+r, columns n0+8q..
+        const int64_t k = k0 + r, n = n0 + 8 * q;
+        if (k < K && n < N) {
+            u32x4 v;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                v[j] = (uint32_t)t[(8 * q + 2 * j) * P + r] | ((uint32_t)t[(8 * q + 2 * j + 1) * P + r] << 16);
+            *reinterpret_cast<u32x4*>(dst + k * N + n) = v;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // forward / data gradient (identical in both variants)
 //
 // Persistent: workgroup b of G takes work items xcd_remap(b) + i*G, so at any
@@ -1030,7 +1074,11 @@ __device__ __forceinline__ void store4(void* out, int64_t idx, f32x4 v) {
 
 template <int OP, int BM, int BN, bool OUT_BF16, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void gg_fwd_dgrad_kernel(GemmArgs a) {
-    DRGG_STAGES(BM, BN, true, OP == 0, stg);
+    // OP 0: forward; 1: data gradient; 2: data gradient with B = W^T
+    // ([E][K][N], made by gg_transpose_w_kernel), so that both operands are
+    // reduction-contiguous like the forward's
+    constexpr bool BK = OP != 1;
+    DRGG_STAGES(BM, BN, true, BK, stg);
     __shared__ Sched sch;
     __shared__ __attribute__((aligned(16))) char ep[WAVES * ep_rows(BM, BN) * 128];
     // output columns: N (forward) or K (data gradient)
@@ -1059,19 +1107,22 @@ __global__ __launch_bounds__(64 * WAVES) void gg_fwd_dgrad_kernel(GemmArgs a) {
         if constexpr (OP == 0) {   // Y = X W^T: both reduction-contiguous
             t.A = Operand{a.A + t0 * a.K, a.K, t.rows, (int32_t)a.K};
             t.B = Operand{We + c0 * a.K, a.K, t.cols, (int32_t)a.K};
-        } else {                   // dX = G W: W is [n][k], reduction n strided
+        } else if constexpr (OP == 1) {   // dX = G W: W is [n][k], reduction n strided
             t.A = Operand{a.A + t0 * a.N, a.N, t.rows, (int32_t)a.N};
             t.B = Operand{We + c0, a.K, t.cols, (int32_t)a.N};
+        } else {                   // dX = G (W^T)^T: W^T is [k][n], reduction n contiguous
+            t.A = Operand{a.A + t0 * a.N, a.N, t.rows, (int32_t)a.N};
+            t.B = Operand{We + c0 * a.N, a.N, t.cols, (int32_t)a.N};
         }
         w += G;
     };
     void* out = a.out;
-    auto finish = [&](const TileInfo& t, const TileMma<BM, BN, true, OP == 0, WAVES>& mma) {
+    auto finish = [&](const TileInfo& t, const TileMma<BM, BN, true, BK, WAVES>& mma) {
         void* base = OUT_BF16 ? (void*)(reinterpret_cast<uint16_t*>(out) + t.o0 * ncols + t.o1)
                               : (void*)(reinterpret_cast<float*>(out) + t.o0 * ncols + t.o1);
         store_tile_lines<OUT_BF16, ep_rows(BM, BN)>(mma, (lds_t*)ep, base, ncols, t.rows, t.cols);
     };
-    TileRunner<BM, BN, true, OP == 0, WAVES> runner;
+    TileRunner<BM, BN, true, BK, WAVES> runner;
     runner.st = stg;
     runner.run(more, next, finish);
 }
@@ -1619,17 +1670,27 @@ static hipError_t launch_fwd_dgrad_t(const GemmArgs& a, bool bf16, hipStream_t s
     return hipGetLastError();
 }
 
-hipError_t launch_fwd_dgrad(int op, int tile, const GemmArgs& a, bool bf16, hipStream_t s) {
+template <int OP>
+static hipError_t launch_fwd_dgrad_op(int tile, const GemmArgs& a, bool bf16, hipStream_t s) {
     switch (tile) {
-        case kTile128x128:
-            return op == 0 ? launch_fwd_dgrad_t<0, 128, 128>(a, bf16, s) : launch_fwd_dgrad_t<1, 128, 128>(a, bf16, s);
-        case kTile256x128:
-            return op == 0 ? launch_fwd_dgrad_t<0, 256, 128>(a, bf16, s) : launch_fwd_dgrad_t<1, 256, 128>(a, bf16, s);
-        case kTile128x256:
-            return op == 0 ? launch_fwd_dgrad_t<0, 128, 256>(a, bf16, s) : launch_fwd_dgrad_t<1, 128, 256>(a, bf16, s);
-        default:
-            return op == 0 ? launch_fwd_dgrad_t<0, 256, 256>(a, bf16, s) : launch_fwd_dgrad_t<1, 256, 256>(a, bf16, s);
+        case kTile128x128: return launch_fwd_dgrad_t<OP, 128, 128>(a, bf16, s);
+        case kTile256x128: return launch_fwd_dgrad_t<OP, 256, 128>(a, bf16, s);
+        case kTile128x256: return launch_fwd_dgrad_t<OP, 128, 256>(a, bf16, s);
+        default: return launch_fwd_dgrad_t<OP, 256, 256>(a, bf16, s);
     }
+}
+
+hipError_t launch_fwd_dgrad(int op, int tile, const GemmArgs& a, bool bf16, hipStream_t s) {
+    if (op == 0) return launch_fwd_dgrad_op<0>(tile, a, bf16, s);
+    if (op == 1) return launch_fwd_dgrad_op<1>(tile, a, bf16, s);
+    return launch_fwd_dgrad_op<2>(tile, a, bf16, s);
+}
+
+hipError_t launch_transpose_w(const uint16_t* W, uint16_t* WT, int32_t E, int64_t N, int64_t K, hipStream_t s) {
+    dim3 grid((unsigned)((K + 63) / 64), (unsigned)((N + 63) / 64), (unsigned)E), block(kThreads);
+    timing_mark("gg_transpose_w_kernel", s);
+    hipLaunchKernelGGL(gg_transpose_w_kernel, grid, block, 0, s, W, WT, N, K);
+    return hipGetLastError();
 }
 
 template <int BM, int BN>

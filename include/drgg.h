@@ -117,7 +117,13 @@ drgg_status grouped_gemm_fwd(const void *X, const void *W, const int32_t *group_
 
 /*
  * Data gradient: dX[t,k] = sum_n G[t,n] * W[e(t),n,k].  G [M,N] BF16,
- * W [E,N,K] BF16, dX [M,K] out_dtype.  No workspace is needed.
+ * W [E,N,K] BF16, dX [M,K] out_dtype.  The workspace is optional: with at
+ * least grouped_gemm_workspace_size(DRGG_OP_DGRAD, ...) bytes (E*N*K*2,
+ * rounded up to 256; 16-byte aligned) W is first transposed into it
+ * (W^T [E,K,N]) and the product runs with both operands
+ * reduction-contiguous, which is faster; with less (or NULL) W is read
+ * transposed by the kernel.  The results are bitwise the same either way.
+ * The workspace needs no initialisation and holds W^T after the call.
  */
 drgg_status grouped_gemm_dgrad(const void *G, const void *W, const int32_t *group_offsets,
                                int32_t E, int64_t M, int64_t N, int64_t K,
@@ -161,7 +167,8 @@ drgg_status router_gemm_fp32_bf16x3(const float *X, const float *Wr, int64_t M, 
 /*
  * Workspace bytes (written to *bytes, a HOST pointer) that a call with these
  * arguments needs; they do not depend on the CU count (cu_count is accepted
- * for symmetry with drgg_plan and ignored).  0 bytes for fwd and dgrad.
+ * for symmetry with drgg_plan and ignored).  0 bytes for fwd; for dgrad the
+ * optional W^T buffer.
  */
 drgg_status grouped_gemm_workspace_size(drgg_op op, int32_t E, int64_t M, int64_t N, int64_t K,
                                         drgg_dtype out_dtype, int deterministic, int cu_count,

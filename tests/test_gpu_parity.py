@@ -116,3 +116,22 @@ def test_wgrad_det_multi_chunk_case_is_split(drgg):
     counts = synth.ragged_counts(101, 1000, 3, (1,))
     chunks = [drgg.wgrad_chunking(int(t), plan["chunk_max"])[1] for t in counts]
     assert max(chunks) > 1 or plan["chunk_max"] >= 1000
+
+
+@pytest.mark.parametrize("shape", [(302, 3, 1000, 264, 520, (1,)), (303, 8, 4096, 1536, 2048, ()),
+                                   (304, 1, 700, 72, 136, ())])
+def test_dgrad_transposed_w_matches_direct_bitwise(drgg, shape):
+    """The data gradient with a workspace (W transposed into it first) and
+    without (W read transposed by the kernel) multiply the same values in the
+    same order: bitwise equal outputs; the direct one also against the
+    oracle."""
+    prob = ragged_problem(*shape)
+    print(f"dgrad W^T vs direct shape={shape}", flush=True)
+    dv = dev_inputs(prob)
+    for out_dtype, view in ((torch.float32, torch.int32), (torch.bfloat16, torch.int16)):
+        via_wt = drgg.grouped_gemm_dgrad(dv["G"], dv["W"], dv["offs"], out_dtype=out_dtype)
+        direct = drgg.grouped_gemm_dgrad(dv["G"], dv["W"], dv["offs"], out_dtype=out_dtype, workspace=False)
+        torch.cuda.synchronize()
+        assert torch.equal(via_wt.view(view), direct.view(view))
+        if out_dtype == torch.float32:
+            parity.compare(prob, "dgrad", parity.from_dev(direct), False, what=f"dgrad direct {shape}")
