@@ -92,6 +92,28 @@ def test_deterministic_across_tile_shapes_and_walk_order(drgg, program):
     parity.compare(prob, program, parity.from_dev(run_program(drgg, program, dv, torch.float32, True)), False)
 
 
+@pytest.mark.parametrize("program", ["fwd", "dgrad", "wgrad"])
+def test_deterministic_across_grid_sizes(drgg, program):
+    """The number of workgroups (what the CU count sets) decides which
+    workgroup takes which work item, and for the weight gradient the snake
+    walk over the longest-first order: it must not change a bit.  Many
+    experts of very different lengths, a few equal, some empty."""
+    counts = np.array([900, 40, 2500, 0, 40, 1300, 700, 3100, 40, 0, 260, 1800, 900, 120, 5000, 600],
+                      dtype=np.int64)
+    prob = synth.make_problem("ragged_grid", 305, counts, N=264, K=520, w_std=0.02)
+    dv = dev_inputs(prob)
+    ref = bits(run_program(drgg, program, dv, torch.float32, True))
+    try:
+        for grid in (1, 3, 17, 64, 255):
+            drgg.set_knob(drgg.KNOB_GRID, grid)
+            got = bits(run_program(drgg, program, dv, torch.float32, True))
+            assert np.array_equal(got, ref), f"grid {grid} changed the bits"
+    finally:
+        drgg.set_knob(drgg.KNOB_GRID, 0)
+    parity.compare(prob, program, parity.from_dev(run_program(drgg, program, dv, torch.float32, True)), False,
+                   what=f"ragged grid {program}")
+
+
 def _hip():
     return ctypes.CDLL("libamdhip64.so")
 
