@@ -164,6 +164,21 @@ def measured_traffic(kernel):
     return None
 
 
+def trace_mark(torch):
+    """A tiny torch fill kernel between workloads (outside every timed
+    region): in a rocprofv3 kernel trace of `--all` these split the
+    dispatches into the workloads, in the order of other_workloads."""
+    torch.cuda.synchronize()
+    torch.empty(1, dtype=torch.float64, device="cuda").fill_(0.0)   # FillFunctor<double>
+    torch.cuda.synchronize()
+
+
+# the workloads of other_workloads, in order (one trace_mark before each)
+OTHER_ORDER = ([f"dense_wgrad_n{d}_{v}" for d in (48, 64, 512, 1024) for v in ("det", "splitk")] +
+               ["moe_down_zipf_wgrad_det", "moe_down_zipf_wgrad_splitk", "dense_square_fwd",
+                "dense_square_dgrad", "dense_square_wgrad", "router_fp32_bf16x3"])
+
+
 def other_workloads(torch, drgg, synth, reps):
     """Per-program times of the other measured workloads (context lines)."""
     out = {}
@@ -176,6 +191,7 @@ def other_workloads(torch, drgg, synth, reps):
             # one workspace per variant: a deterministic call leaves partials
             # where the non-deterministic program needs zeroed tile sums
             ws = drgg.Workspace()
+            trace_mark(torch)
             # "splitk": the split program, which the library's default
             # route replaces by the deterministic one
             drgg.set_knob(drgg.KNOB_NONDET, 0 if det else 1)
@@ -196,6 +212,7 @@ def other_workloads(torch, drgg, synth, reps):
     dW = torch.empty((p.E, p.N, p.K), dtype=torch.float32, device="cuda")
     for det in (True, False):
         ws = drgg.Workspace()
+        trace_mark(torch)
         drgg.set_knob(drgg.KNOB_NONDET, 0 if det else 1)
         fn = lambda: drgg.grouped_gemm_wgrad(X, G, offs, out_dtype=torch.float32, deterministic=det,
                                              out=dW, workspace=ws)
@@ -218,6 +235,7 @@ def other_workloads(torch, drgg, synth, reps):
         "wgrad": lambda: drgg.grouped_gemm_wgrad(X, G, offs),
     }
     for name, fn in fns.items():
+        trace_mark(torch)
         fn()
         t = time_call(torch, drgg, fn, reps)
         ms = sum(t.values())
@@ -227,6 +245,7 @@ def other_workloads(torch, drgg, synth, reps):
     Xr, Wr = synth.router_inputs()
     Xr, Wr = torch.from_numpy(Xr).cuda(), torch.from_numpy(Wr).cuda()
     fn = lambda: drgg.router_gemm_fp32_bf16x3(Xr, Wr)
+    trace_mark(torch)
     fn()
     t = time_call(torch, drgg, fn, reps)
     ms = sum(t.values())
