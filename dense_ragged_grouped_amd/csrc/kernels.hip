@@ -438,11 +438,16 @@ struct StageLoader {
     // everything when !valid (or when L lies past the last stage): such a
     // load accesses no memory.
     __device__ __forceinline__ void issue(lds_t* buf, int L, bool valid) const {
+        issue_part<0, kPerWave>(buf, L, valid);
+    }
+    // instructions J0 .. J1-1 of that load (a load may be spread over steps)
+    template <int J0, int J1>
+    __device__ __forceinline__ void issue_part(lds_t* buf, int L, bool valid) const {
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         const __amdgpu_buffer_rsrc_t r = make_rsrc(base + L * step_bytes);
         const int rem = valid ? klen - L * kStageK : 0;
 #pragma unroll
-        for (int i = 0; i < kPerWave; ++i) {
+        for (int i = J0; i < J1; ++i) {
             const uint32_t o = kp[i] < rem ? off[i] : kOOB;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 r, (lds_void_t*)(buf + (wave * kPerWave + i) * 1024), 16, o, 0, 0, 0);
@@ -888,47 +893,104 @@ struct TileRunner {
     // issued at the previous barrier, which steps t and t+1 read.
     static constexpr bool kBar2 = WAVES == 8;
 
-    // The loads of step t (t % 4 == ST) for operand loader `ld`: stage t+4,
-    // or for a K-major operand at odd t the pair t+3, t+4 (with kBar2, an
-    // MN-major operand also loads stages t+3 and t+4 at odd t), of this tile
-    // or, past nk4, of the next one (the loaders then point at the next
-    // tile).
+    // With kBar2 the loads of an odd step t (stages t+3 and t+4: kNLT wave
+    // instructions per wave, A's before B's) may be spread over three
+    // sub-steps: instructions [0, kS1) go out in sub-step 1 of step t,
+    // [kS1, kS2) in sub-step 0 of step t+1 and [kS2, kNLT) in its sub-step 1,
+    // interleaved with their MFMAs.  All of them still land before the
+    // barrier of step t+2, which waits for every load in flight.  The last
+    // odd step of a tile fetches the next tile's stages 2 and 3, and that
+    // tile's first step issues the rest; the prologue issues the first
+    // tile's stages 0 and 1 and part of 2 and 3 in the same way.  As
+    // measured, spreading pays only with a transposed (MN-major) B operand,
+    // whose loads are the more numerous (3/3/2 of 8: 4 % on the data
+    // gradient without W^T); with both operands K-major it gained nothing or
+    // lost, so they issue everything at the odd step.
+    static constexpr int kNLT = (AK ? 1 : 2) * LA::kPerWave + (BK ? 1 : 2) * LB::kPerWave;
+    static constexpr int kS1 = kBar2 && !BK && kNLT == 8 ? 3 : kNLT;
+    static constexpr int kS2 = kBar2 && !BK && kNLT == 8 ? 6 : kNLT;
+    // the step that switches the loaders to the next tile: the first one
+    // whose loads fetch from it
+    static constexpr int kReinitST = kBar2 ? 1 : 0;
+
+    // Instructions [I0, I1) of the loads of odd step kt_odd (STO = kt_odd % 4).
+    template <int STO, int I0, int I1, int Q>
+    __device__ __forceinline__ void issue_odd_entry(int kt_odd) {
+        // entry Q: a load of A for Q < nA, else of B; a K-major operand has
+        // one (the pair t+3, t+4), an MN-major one two (t+3, then t+4)
+        constexpr int nA = AK ? 1 : 2;
+        constexpr bool isA = Q < nA;
+        constexpr int P = isA ? LA::kPerWave : LB::kPerWave;
+        constexpr int start = isA ? Q * LA::kPerWave : nA * LA::kPerWave + (Q - nA) * LB::kPerWave;
+        constexpr int j0 = I0 - start < 0 ? 0 : I0 - start > P ? P : I0 - start;
+        constexpr int j1 = I1 - start < 0 ? 0 : I1 - start > P ? P : I1 - start;
+        if constexpr (j0 < j1) {
+            constexpr int d = 3 + (isA ? Q : Q - nA);
+            const int L = kt_odd + d;
+            const int Ls = L < nk4 ? L : L - nk4;
+            if constexpr (isA) la.template issue_part<j0, j1>(st.a[(STO + d) % kStages], Ls, L < nk4 || has_next);
+            else lb.template issue_part<j0, j1>(st.b[(STO + d) % kStages], Ls, L < nk4 || has_next);
+        }
+    }
+    template <int STO, int I0, int I1, int... Q>
+    __device__ __forceinline__ void issue_odd_entries(int kt_odd, std::integer_sequence<int, Q...>) {
+        (issue_odd_entry<STO, I0, I1, Q>(kt_odd), ...);
+    }
+    template <int STO, int I0, int I1>
+    __device__ __forceinline__ void issue_odd(int kt_odd) {
+        if constexpr (I0 < I1)
+            issue_odd_entries<STO, I0, I1>(kt_odd, std::make_integer_sequence<int, (AK ? 1 : 2) + (BK ? 1 : 2)>{});
+    }
+
+    // Without kBar2, the loads of step t (t % 4 == ST) for operand loader
+    // `ld`: stage t+4, or for a K-major operand at odd t the pair t+3, t+4,
+    // of this tile or, past nk4, of the next one (the loaders then point at
+    // the next tile).
     template <int ST, bool K, class Ld>
     __device__ __forceinline__ void issue(Ld& ld, lds_t* const* bufs, int kt) {
-        if constexpr (kBar2 && !K) {
-            if constexpr (ST & 1) {
-#pragma unroll
-                for (int d = 3; d <= 4; ++d) {
-                    const int L = kt + d;
-                    const int Ls = L < nk4 ? L : L - nk4;
-                    ld.issue(bufs[(ST + d) % kStages], Ls, L < nk4 || has_next);
-                }
-            }
-        } else if constexpr (!K || (ST & 1)) {
+        static_assert(!kBar2, "with kBar2 the loads go through issue_odd");
+        if constexpr (!K || (ST & 1)) {
             const int L = kt + (K ? 3 : 4);
             const int Ls = L < nk4 ? L : L - nk4;
             ld.issue(bufs[(ST + (K ? 3 : 4)) % kStages], Ls, L < nk4 || has_next);
         }
     }
 
+    // Sub-step 1 of odd step kt with kBar2: its MFMAs, the loads [0, N) of
+    // the step, the sub-step 0 fragments of stage kt+1.
+    template <int ST, int N>
+    __device__ __forceinline__ void odd_substep1(int kt) {
+        issue_odd<ST, 0, N>(kt);
+        mma.template read<0, (ST + 1) % kStages>(st, 0);
+        mma.template mfma<1>();
+        if constexpr (AK && BK) sched_interleave<Mma::kMfmas, Mma::kReads, N>();
+    }
+
     // Step kt of the current tile; ST = kt % 4; FIRST for step 0.
     template <int ST, bool FIRST = false, class Next>
     __device__ __forceinline__ void step(int kt, Next& next) {
         constexpr int NX = (ST + 1) % kStages;
-        // loads issued in this step (the schedule hints place them)
-        constexpr int NL = kBar2 ? ((ST & 1) ? (AK ? 1 : 2) * LA::kPerWave + (BK ? 1 : 2) * LB::kPerWave : 0)
-                                 : (AK && !(ST & 1) ? 0 : LA::kPerWave) + (BK && !(ST & 1) ? 0 : LB::kPerWave);
-        if (kt + kStages == nk4 && has_next) {
-            next(nxt);
-            nk_nxt = stages_of(nxt);
-            la.init(nxt.A);
-            lb.init(nxt.B);
+        constexpr int STO = (ST + kStages - 1) % kStages;
+        // with kBar2 an even step issues the deferred loads of step kt-1 (for
+        // a tile's first step, those of the previous tile's last step or of
+        // the prologue: its stages 2 and 3)
+        constexpr bool DEF = kBar2 && !(ST & 1);
+        // loads issued in this step without kBar2 (the schedule hints place them)
+        constexpr int NL = (AK && !(ST & 1) ? 0 : LA::kPerWave) + (BK && !(ST & 1) ? 0 : LB::kPerWave);
+        if constexpr (ST == kReinitST) {
+            if (kt - ST + kStages == nk4 && has_next) {
+                next(nxt);
+                nk_nxt = stages_of(nxt);
+                la.init(nxt.A);
+                lb.init(nxt.B);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
         // sub-step 0: its MFMAs; the sub-step 1 fragments
         mma.template read<1, ST>(st, 1);
+        if constexpr (DEF) issue_odd<STO, kS1, kS2>(kt - 1);
         mma.template mfma<0, FIRST>();
-        if constexpr (AK && BK) sched_interleave<Mma::kMfmas, Mma::kReads, 0>();
+        if constexpr (AK && BK) sched_interleave<Mma::kMfmas, Mma::kReads, DEF ? kS2 - kS1 : 0>();
         __builtin_amdgcn_sched_barrier(0);
         // stage kt+1 has landed for every wave, and every wave is done
         // reading stage kt
@@ -938,11 +1000,20 @@ struct TileRunner {
         }
         // sub-step 1: its MFMAs; the loads into the buffers just freed; the
         // sub-step 0 fragments of stage kt+1
-        issue<ST, AK>(la, st.a, kt);
-        issue<ST, BK>(lb, st.b, kt);
-        mma.template read<0, NX>(st, 0);
-        mma.template mfma<1>();
-        if constexpr (AK && BK) sched_interleave<Mma::kMfmas, Mma::kReads, NL>();
+        if constexpr (kBar2 && (ST & 1)) {
+            odd_substep1<ST, kS1>(kt);
+        } else if constexpr (kBar2) {
+            if constexpr (DEF) issue_odd<STO, kS2, kNLT>(kt - 1);
+            mma.template read<0, NX>(st, 0);
+            mma.template mfma<1>();
+            if constexpr (AK && BK) sched_interleave<Mma::kMfmas, Mma::kReads, DEF ? kNLT - kS2 : 0>();
+        } else {
+            issue<ST, AK>(la, st.a, kt);
+            issue<ST, BK>(lb, st.b, kt);
+            mma.template read<0, NX>(st, 0);
+            mma.template mfma<1>();
+            if constexpr (AK && BK) sched_interleave<Mma::kMfmas, Mma::kReads, NL>();
+        }
         __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -955,20 +1026,29 @@ struct TileRunner {
         has_next = false;
         la.init(cur.A);
         lb.init(cur.B);
-        // prologue: stages 0..3 (zeros past nk) in the order of steps -4..-1
+        if constexpr (kBar2) {
+            // prologue: stages 0, 1 and the first part of 2, 3, as odd
+            // steps -3 and -1 would issue them; then wait for stages 0 and 1
+            // (step 0 reads both)
+            issue_odd<1, 0, kNLT>(-3);
+            issue_odd<3, 0, kS1>(-1);
+            wait_vm_lgkm<kS1>();
+        } else {
+            // prologue: stages 0..3 (zeros past nk) in the order of steps -4..-1
 #pragma unroll
-        for (int t = -4; t < 0; ++t) {
+            for (int t = -4; t < 0; ++t) {
 #pragma unroll
-            for (int op = 0; op < 2; ++op) {
-                const bool k = op == 0 ? AK : BK;
-                if (k && !(t & 1)) continue;
-                const int L = t + (k ? 3 : 4);
-                if (op == 0) la.issue(st.a[L], L, true);
-                else lb.issue(st.b[L], L, true);
+                for (int op = 0; op < 2; ++op) {
+                    const bool k = op == 0 ? AK : BK;
+                    if (k && !(t & 1)) continue;
+                    const int L = t + (k ? 3 : 4);
+                    if (op == 0) la.issue(st.a[L], L, true);
+                    else lb.issue(st.b[L], L, true);
+                }
             }
+            // stage 0 landed
+            wait_vm_lgkm<Plan::prologue>();
         }
-        // stage 0 landed (and with kBar2 stage 1 too, which step 0 reads)
-        wait_vm_lgkm<kBar2 ? Plan::after(1, -1) : Plan::prologue>();
         barrier_nofence();
         mma.template read<0, 0>(st, 0);
         for (;;) {
