@@ -1210,8 +1210,15 @@ __global__ __launch_bounds__(64 * WAVES) void gg_fwd_dgrad_kernel(GemmArgs a) {
 // ---------------------------------------------------------------------------
 // deterministic weight gradient: chunk partials (K3) and ordered fold (K4)
 
+// Waves of the chunk kernel: 8 for the 256x256 tile (two per SIMD, VGPR
+// accumulators, the barrier at every second step and the spread loads of
+// the runner), 4 for the smaller tiles.  The arithmetic does not depend on it.
+template <int BM, int BN>
+constexpr int wgrad_det_waves() { return BM == 256 && BN == 256 ? 8 : 4; }
+
 template <int BM, int BN, bool OUT_BF16>
-__global__ __launch_bounds__(kGemmThreads) void gg_wgrad_det_kernel(GemmArgs a) {
+__global__ __launch_bounds__((64 * wgrad_det_waves<BM, BN>())) void gg_wgrad_det_kernel(GemmArgs a) {
+    constexpr int WV = wgrad_det_waves<BM, BN>();
     DRGG_STAGES(BM, BN, false, false, stg);
     __shared__ Sched sch;
     __shared__ int32_t slot_base[kMaxExperts + 1];
@@ -1270,7 +1277,7 @@ __global__ __launch_bounds__(kGemmThreads) void gg_wgrad_det_kernel(GemmArgs a) 
         t.B = Operand{a.B + tb * a.K + k0, a.K, t.cols, len};
         w = snake_item(++round, wb, G);
     };
-    auto finish = [&](const TileInfo& t, const TileMma<BM, BN, false, false>& mma) {
+    auto finish = [&](const TileInfo& t, const TileMma<BM, BN, false, false, WV>& mma) {
         const int64_t ld = a.K;
         if (t.aux < 0) {   // one chunk: round and store the output directly
             const int64_t off = (int64_t)t.e * a.N * a.K + t.o0 * a.K + t.o1;
@@ -1282,7 +1289,7 @@ __global__ __launch_bounds__(kGemmThreads) void gg_wgrad_det_kernel(GemmArgs a) 
             store_tile<false>(mma, dst, ld, t.rows, t.cols);
         }
     };
-    TileRunner<BM, BN, false, false> runner;
+    TileRunner<BM, BN, false, false, WV> runner;
     runner.st = stg;
     runner.run(more, next, finish);
 }
@@ -1776,7 +1783,7 @@ hipError_t launch_transpose_w(const uint16_t* W, uint16_t* WT, int32_t E, int64_
 template <int BM, int BN>
 static hipError_t launch_wgrad_det_t(const GemmArgs& a, bool bf16, hipStream_t s) {
     if (a.items_max > 0) {
-        dim3 grid((unsigned)a.items_max), block(kGemmThreads);
+        dim3 grid((unsigned)a.items_max), block(64 * wgrad_det_waves<BM, BN>());
         timing_mark("gg_wgrad_det_kernel", s);
         if (bf16) hipLaunchKernelGGL((gg_wgrad_det_kernel<BM, BN, true>), grid, block, 0, s, a);
         else hipLaunchKernelGGL((gg_wgrad_det_kernel<BM, BN, false>), grid, block, 0, s, a);

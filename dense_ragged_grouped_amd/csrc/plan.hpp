@@ -107,8 +107,9 @@ constexpr int ep_rows(int bm, int bn) { return bm * bn >= 256 * 128 ? 16 : 8; }
 // of LDS: kStages stages of (BM + BN) x kStageK BF16, the schedule tables
 // (10 KB; the deterministic weight gradient adds 4 KB of partial-slot
 // bases), the forward/data-gradient epilogue scratch, and 1 KB for
-// alignment.  Workgroups have 4 waves, except the 8 of the 256x256 forward
-// and data-gradient kernels.
+// alignment.  Workgroups have 4 waves, except the 8 of the 256x256 forward,
+// data-gradient and deterministic weight-gradient kernels (only the first two
+// have the epilogue scratch).
 inline int64_t wgs_per_cu(TileShape t, bool fwd_dgrad, bool det_wgrad) {
     const int64_t waves = fwd_dgrad && t.bm == 256 && t.bn == 256 ? 8 : 4;
     const int64_t lds = (int64_t)kStages * (t.bm + t.bn) * kStageK * 2 + 10248 + (det_wgrad ? 4100 : 0) +
