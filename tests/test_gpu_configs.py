@@ -95,6 +95,20 @@ def test_moe_gate_up_integer_bitwise(drgg, program):
         sampled_check(prob, program, out, True, integer=True, what=f"gate_up integer {program} det={det}")
 
 
+def test_moe_gate_up_dgrad_direct_bitwise(drgg):
+    """The data gradient without a workspace (W read transposed, its loads
+    spread over the steps and across tile boundaries) at a size with 16
+    tiles per workgroup: bitwise equal to the W^T program, and exact against
+    the oracle on integer inputs."""
+    prob = synth.config3(integer=True)
+    dv = dev_inputs(prob)
+    via_wt = drgg.grouped_gemm_dgrad(dv["G"], dv["W"], dv["offs"], out_dtype=torch.bfloat16)
+    direct = drgg.grouped_gemm_dgrad(dv["G"], dv["W"], dv["offs"], out_dtype=torch.bfloat16, workspace=False)
+    torch.cuda.synchronize()
+    assert torch.equal(via_wt.view(torch.int16), direct.view(torch.int16))
+    sampled_check(prob, "dgrad", direct, True, integer=True, what="gate_up integer dgrad direct")
+
+
 # ---- workload 4: MoE down, Zipf-skewed, 2 empty experts --------------------------
 
 @pytest.mark.parametrize("integer", [False, True])
