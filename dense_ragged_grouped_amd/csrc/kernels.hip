@@ -813,8 +813,8 @@ __device__ __forceinline__ void drain_tile_sum(const Mma& mma, float* ts, void* 
     }
 }
 
-// Issue schedule of the stage loads (steps t of the global step sequence;
-// the prologue acts as steps -4 .. -1).  A K-major operand loads stages t+3
+// Issue schedule of the stage loads of a 4-wave runner (steps t of the
+// global step sequence; the prologue acts as steps -4 .. -1).  A K-major operand loads stages t+3
 // and t+4 at odd steps (into the pair buffer whose two stages t-1 and t were
 // read by then), an MN-major operand stage t+4 at every step; within a step
 // A goes before B.  The pipeline waits, at the barrier of step s, until
@@ -886,11 +886,11 @@ struct TileRunner {
 
     // With 8 waves the workgroup barrier is passed at odd steps only: the
     // two waves of a SIMD stop issuing MFMAs at a barrier, and with two of
-    // them per SIMD that stall is the larger cost.  Every load is then issued
-    // at an odd step t (stages t+3 and t+4, into the buffers of stages t-1
-    // and t, which every wave has finished reading at that barrier), and the
-    // barrier waits for all loads in flight: those of stages t+1 and t+2,
-    // issued at the previous barrier, which steps t and t+1 read.
+    // them per SIMD that stall is the larger cost.  The loads then belong to
+    // the odd steps: step t loads stages t+3 and t+4 into the buffers of
+    // stages t-1 and t, which every wave has finished reading at its
+    // barrier, and that barrier waits for all loads in flight: those of
+    // stages t+1 and t+2, which steps t and t+1 read.
     static constexpr bool kBar2 = WAVES == 8;
 
     // With kBar2 the loads of an odd step t (stages t+3 and t+4: kNLT wave
@@ -902,10 +902,12 @@ struct TileRunner {
     // odd step of a tile fetches the next tile's stages 2 and 3, and that
     // tile's first step issues the rest; the prologue issues the first
     // tile's stages 0 and 1 and part of 2 and 3 in the same way.  As
-    // measured, spreading pays only with a transposed (MN-major) B operand,
-    // whose loads are the more numerous (3/3/2 of 8: 4 % on the data
-    // gradient without W^T); with both operands K-major it gained nothing or
-    // lost, so they issue everything at the odd step.
+    // measured, spreading pays with a transposed (MN-major) B operand, read
+    // back with two LDS instructions per fragment: 3/3/2 of the 8 gained 4 %
+    // on the data gradient without W^T and 1 % on the weight gradient (8 of
+    // 8 at the odd step and the other splits tried were slower); with both
+    // operands K-major it gained nothing or lost, so they issue everything
+    // at the odd step.
     static constexpr int kNLT = (AK ? 1 : 2) * LA::kPerWave + (BK ? 1 : 2) * LB::kPerWave;
     static constexpr int kS1 = kBar2 && !BK && kNLT == 8 ? 3 : kNLT;
     static constexpr int kS2 = kBar2 && !BK && kNLT == 8 ? 6 : kNLT;
