@@ -176,7 +176,8 @@ def trace_mark(torch):
 # the workloads of other_workloads, in order (one trace_mark before each)
 OTHER_ORDER = ([f"dense_wgrad_n{d}_{v}" for d in (48, 64, 512, 1024) for v in ("det", "splitk")] +
                ["moe_down_zipf_wgrad_det", "moe_down_zipf_wgrad_splitk", "dense_square_fwd",
-                "dense_square_dgrad", "dense_square_wgrad", "router_fp32_bf16x3"])
+                "dense_square_dgrad", "dense_square_wgrad", "router_fp32_bf16x3",
+                "moe_gate_up_ckpt", "moe_gate_up_ckpt_es"])
 
 
 def other_workloads(torch, drgg, synth, reps):
@@ -257,6 +258,42 @@ def other_workloads(torch, drgg, synth, reps):
     return out
 
 
+def ckpt_workloads(torch, prob, reps):
+    """The checkpointed step of the gate_up layer through autograd: one
+    grouped GEMM in a non-reentrant checkpoint, forward + backward (dX, dW),
+    with checkpoint early stop off ("ckpt": the backward recomputes the
+    forward, 4 GEMMs) and on ("ckpt_es": the recompute ends before the
+    forward kernel, 3 GEMMs).  GPU time from the first kernel to the last of
+    the step (stream events), inputs resident."""
+    from dense_ragged_grouped_amd.autograd import checkpointed_grouped_linear
+    X = to_dev_bf16(torch, prob.X).requires_grad_(True)
+    W = to_dev_bf16(torch, prob.W).requires_grad_(True)
+    G = to_dev_bf16(torch, prob.G)
+    offs = torch.from_numpy(prob.offs).cuda()
+    flop = 2.0 * prob.M * prob.N * prob.K
+    out = {}
+    for name, early_stop, gemms in (("moe_gate_up_ckpt", False, 4), ("moe_gate_up_ckpt_es", True, 3)):
+        def step():
+            Y = checkpointed_grouped_linear(X, W, offs, early_stop=early_stop)
+            torch.autograd.grad(Y, (X, W), G)
+
+        trace_mark(torch)
+        for _ in range(2):
+            step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[name] = {"us": ms * 1e3, "gemms": gemms, "tflops": gemms * flop / ms / 1e9,
+                     "pct_peak": 100 * gemms * flop / ms / 1e9 / PEAK_BF16_TFLOPS}
+        log(f"{name}: {ms * 1e3:.1f} us per step ({gemms} GEMMs), {gemms * flop / ms / 1e9:.1f} TFLOP/s")
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -328,7 +365,10 @@ def main():
         cpu = cpu_baseline(prob)
         log(f"cpu baseline: {cpu['value'] * 1e3:.3f} GFLOP/s on {cpu['cores']} threads")
 
-    extra = other_workloads(torch, drgg, synth, args.reps) if args.all else None
+    extra = None
+    if args.all:
+        extra = other_workloads(torch, drgg, synth, args.reps)
+        extra.update(ckpt_workloads(torch, prob, args.reps))
 
     line = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
