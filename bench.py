@@ -177,6 +177,7 @@ def trace_mark(torch):
 OTHER_ORDER = ([f"dense_wgrad_n{d}_{v}" for d in (48, 64, 512, 1024) for v in ("det", "splitk")] +
                ["moe_down_zipf_wgrad_det", "moe_down_zipf_wgrad_splitk", "dense_square_fwd",
                 "dense_square_dgrad", "dense_square_wgrad", "router_fp32_bf16x3",
+                "mla_heads_fwd", "mla_heads_dgrad", "mla_heads_wgrad",
                 "moe_gate_up_ckpt", "moe_gate_up_ckpt_es"])
 
 
@@ -255,6 +256,44 @@ def other_workloads(torch, drgg, synth, reps):
                                  "tflops_mfma": 3 * flop / ms / 1e9,
                                  "gbs_algorithmic": 4.0 * (16384 * 4096 + 256 * 4096 + 16384 * 256) / ms / 1e6,
                                  "kernels_ms": t}
+    return out
+
+
+def batched_workloads(torch, drgg, reps):
+    """A head-batched projection (batch = head, the batched form of the
+    projection family): T = 4096 tokens, H = 128 heads, K = 128, N = 512, like
+    an MLA per-head projection; activations X [T, H, K] and gradients G
+    [T, H, N] are read in place (strided), Y [T, H, N] / dX [T, H, K] written
+    in place, W [H, N, K]; BF16 out, deterministic.  Seeded normal inputs."""
+    T, H, K, N = 4096, 128, 128, 512
+    gen = torch.Generator(device="cuda").manual_seed(4242)
+    Xi = torch.randn(T, H, K, device="cuda", generator=gen).to(torch.bfloat16)
+    Gi = torch.randn(T, H, N, device="cuda", generator=gen).to(torch.bfloat16)
+    W = (0.02 * torch.randn(H, N, K, device="cuda", generator=gen)).to(torch.bfloat16)
+    Yi = torch.empty(T, H, N, dtype=torch.bfloat16, device="cuda")
+    dXi = torch.empty(T, H, K, dtype=torch.bfloat16, device="cuda")
+    dW = torch.empty(H, N, K, dtype=torch.bfloat16, device="cuda")
+    ws, wsw = drgg.Workspace(), drgg.Workspace()
+    flop = 2.0 * T * H * N * K
+    fns = {
+        "mla_heads_fwd": (lambda: drgg.batched_gemm_fwd(Xi.transpose(0, 1), W, out=Yi.transpose(0, 1)),
+                          2.0 * (T * H * K + H * N * K + T * H * N)),
+        "mla_heads_dgrad": (lambda: drgg.batched_gemm_dgrad(Gi.transpose(0, 1), W, out=dXi.transpose(0, 1),
+                                                            workspace=ws),
+                            2.0 * (T * H * N + H * N * K + T * H * K)),
+        "mla_heads_wgrad": (lambda: drgg.batched_gemm_wgrad(Xi.transpose(0, 1), Gi.transpose(0, 1), out=dW,
+                                                            workspace=wsw),
+                            2.0 * (T * H * K + T * H * N + H * N * K)),
+    }
+    out = {}
+    for name, (fn, byt) in fns.items():
+        trace_mark(torch)
+        fn()
+        t = time_call(torch, drgg, fn, reps)
+        ms = sum(t.values())
+        out[name] = {"us": ms * 1e3, "tflops": flop / ms / 1e9, "pct_peak": 100 * flop / ms / 1e9 / PEAK_BF16_TFLOPS,
+                     "gbs_algorithmic": byt / ms / 1e6, "kernels_ms": t}
+        log(f"{name}: {ms * 1e3:.1f} us, {flop / ms / 1e9:.1f} TFLOP/s, {byt / ms / 1e6:.0f} GB/s algorithmic")
     return out
 
 
@@ -368,6 +407,7 @@ def main():
     extra = None
     if args.all:
         extra = other_workloads(torch, drgg, synth, args.reps)
+        extra.update(batched_workloads(torch, drgg, args.reps))
         extra.update(ckpt_workloads(torch, prob, args.reps))
 
     line = {

@@ -31,6 +31,7 @@ TILE_AUTO, TILE_256x256, TILE_128x128, TILE_256x128, TILE_128x256, TILE_64x256 =
 # the symbols include/drgg.h declares
 EXPORTS = (
     "grouped_gemm_fwd", "grouped_gemm_dgrad", "grouped_gemm_wgrad", "router_gemm_fp32_bf16x3",
+    "batched_gemm_fwd", "batched_gemm_dgrad", "batched_gemm_wgrad",
     "grouped_gemm_workspace_size", "drgg_workspace_init", "drgg_plan", "drgg_wgrad_chunking",
     "drgg_set_knob", "drgg_timing_count", "drgg_timing_read", "drgg_status_string", "drgg_abi_version",
 )
@@ -56,6 +57,16 @@ class PlanInfo(ctypes.Structure):
         return {name: getattr(self, name) for name, _ in self._fields_}
 
 
+class Batched(ctypes.Structure):
+    """drgg_batched: shape and element strides of a batched call."""
+    _fields_ = [
+        ("B", ctypes.c_int32), ("T", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+        ("a_row", ctypes.c_int64), ("a_batch", ctypes.c_int64),
+        ("b_row", ctypes.c_int64), ("b_batch", ctypes.c_int64),
+        ("o_row", ctypes.c_int64), ("o_batch", ctypes.c_int64),
+    ]
+
+
 def _load(path=LIB_PATH):
     if not os.path.exists(path):
         raise ImportError(
@@ -66,6 +77,12 @@ def _load(path=LIB_PATH):
     gemm = [vp, vp, vp, i32, i64, i64, i64, c_int, c_int, vp, vp, sz, vp]
     for name in ("grouped_gemm_fwd", "grouped_gemm_dgrad", "grouped_gemm_wgrad"):
         getattr(lib, name).argtypes = gemm
+        getattr(lib, name).restype = c_int
+    pb = ctypes.POINTER(Batched)
+    lib.batched_gemm_fwd.argtypes = [vp, vp, pb, c_int, vp, vp]
+    lib.batched_gemm_dgrad.argtypes = [vp, vp, pb, c_int, vp, vp, sz, vp]
+    lib.batched_gemm_wgrad.argtypes = [vp, vp, pb, c_int, c_int, vp, vp, sz, vp]
+    for name in ("batched_gemm_fwd", "batched_gemm_dgrad", "batched_gemm_wgrad"):
         getattr(lib, name).restype = c_int
     lib.router_gemm_fp32_bf16x3.argtypes = [vp, vp, i64, i64, i64, vp, vp]
     lib.router_gemm_fp32_bf16x3.restype = c_int
@@ -322,6 +339,105 @@ def grouped_gemm_wgrad(X, G, group_offsets, out_dtype=None, deterministic=True, 
                                 int(bool(deterministic)), out.data_ptr(), ws_ptr, ws_bytes,
                                 _stream(X.device, stream))
     _check(st, "grouped_gemm_wgrad")
+    return out
+
+
+# ---- batched calls: [B, T, row] views with any batch and row strides -----------
+
+def _need_rows(t, name, shape=None):
+    """A BF16 CUDA tensor [B, T, row] whose rows are contiguous (any batch
+    and row strides, e.g. a transposed head-interleaved [T, B, row])."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a CUDA tensor")
+    if t.dim() != 3 or t.stride(2) != 1:
+        raise ValueError(f"{name} must be a 3-d tensor with contiguous rows")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _out_rows(out, shape, code, device, name="out"):
+    torch = _torch()
+    if out is None:
+        return torch.empty(shape, dtype=_torch_dtype(code), device=device)
+    if out.dtype != _torch_dtype(code):
+        raise TypeError(f"{name} must be {_torch_dtype(code)}")
+    _need_rows(out, name, shape)
+    return out
+
+
+def batched_gemm_fwd(X, W, out_dtype=None, out=None, stream=None):
+    """Y[b] = X[b] W[b]^T for b < B: X [B, T, K] (rows contiguous, any
+    strides, e.g. a head-interleaved [T, H, K] activation passed as
+    X.transpose(0, 1)), W [B, N, K] contiguous; Y [B, T, N] (new and
+    contiguous, or `out` with contiguous rows)."""
+    torch = _torch()
+    _need_rows(X, "X")
+    if X.dtype != torch.bfloat16:
+        raise TypeError("X must be bfloat16")
+    _need(W, torch.bfloat16, "W", 3)
+    B, T, K = X.shape
+    if W.shape[0] != B or W.shape[2] != K:
+        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, W {tuple(W.shape)}")
+    N = W.shape[1]
+    code = _dtype_code(out_dtype if out_dtype is not None else torch.bfloat16)
+    out = _out_rows(out, (B, T, N), code, X.device)
+    b = Batched(B, T, N, K, X.stride(1), X.stride(0), 0, 0, out.stride(1), out.stride(0))
+    st = lib.batched_gemm_fwd(X.data_ptr(), W.data_ptr(), ctypes.byref(b), code, out.data_ptr(),
+                              _stream(X.device, stream))
+    _check(st, "batched_gemm_fwd")
+    return out
+
+
+def batched_gemm_dgrad(G, W, out_dtype=None, out=None, workspace=None, stream=None):
+    """dX[b] = G[b] W[b]: G [B, T, N] (rows contiguous), W [B, N, K]
+    contiguous; dX [B, T, K].  `workspace` as for grouped_gemm_dgrad."""
+    torch = _torch()
+    _need_rows(G, "G")
+    if G.dtype != torch.bfloat16:
+        raise TypeError("G must be bfloat16")
+    _need(W, torch.bfloat16, "W", 3)
+    B, T, N = G.shape
+    if W.shape[0] != B or W.shape[1] != N:
+        raise ValueError(f"shape mismatch: G {tuple(G.shape)}, W {tuple(W.shape)}")
+    K = W.shape[2]
+    code = _dtype_code(out_dtype if out_dtype is not None else torch.bfloat16)
+    out = _out_rows(out, (B, T, K), code, G.device)
+    nbytes = workspace_size(OP_DGRAD, B, B * T, N, K, code, True)
+    ws_ptr, ws_bytes = _workspace(G.device, nbytes, workspace, True, kind="dgrad")
+    b = Batched(B, T, N, K, G.stride(1), G.stride(0), 0, 0, out.stride(1), out.stride(0))
+    st = lib.batched_gemm_dgrad(G.data_ptr(), W.data_ptr(), ctypes.byref(b), code, out.data_ptr(), ws_ptr,
+                                ws_bytes, _stream(G.device, stream))
+    _check(st, "batched_gemm_dgrad")
+    return out
+
+
+def batched_gemm_wgrad(X, G, out_dtype=None, deterministic=True, out=None, workspace=None, stream=None):
+    """dW[b] = G[b]^T X[b]: X [B, T, K], G [B, T, N] (rows contiguous, any
+    strides); dW [B, N, K] contiguous.  Workspace as for grouped_gemm_wgrad
+    with E = B, M = B*T."""
+    torch = _torch()
+    _need_rows(X, "X")
+    _need_rows(G, "G")
+    if X.dtype != torch.bfloat16 or G.dtype != torch.bfloat16:
+        raise TypeError("X and G must be bfloat16")
+    B, T, K = X.shape
+    if G.shape[0] != B or G.shape[1] != T:
+        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, G {tuple(G.shape)}")
+    N = G.shape[2]
+    code = _dtype_code(out_dtype if out_dtype is not None else torch.bfloat16)
+    if out is None:
+        out = torch.empty((B, N, K), dtype=_torch_dtype(code), device=X.device)
+    else:
+        _need(out, _torch_dtype(code), "out", 3)
+        if tuple(out.shape) != (B, N, K):
+            raise ValueError("out has the wrong shape")
+    nbytes = workspace_size(OP_WGRAD, B, B * T, N, K, code, deterministic)
+    ws_ptr, ws_bytes = _workspace(X.device, nbytes, workspace, deterministic)
+    b = Batched(B, T, N, K, X.stride(1), X.stride(0), G.stride(1), G.stride(0), 0, 0)
+    st = lib.batched_gemm_wgrad(X.data_ptr(), G.data_ptr(), ctypes.byref(b), code, int(bool(deterministic)),
+                                out.data_ptr(), ws_ptr, ws_bytes, _stream(X.device, stream))
+    _check(st, "batched_gemm_wgrad")
     return out
 
 

@@ -67,6 +67,42 @@ drgg_status check_problem(int32_t E, int64_t M, int64_t N, int64_t K, drgg_dtype
     return DRGG_OK;
 }
 
+// Element strides of the token-major buffers (see GemmArgs).
+struct Layout {
+    int64_t a_rs, a_gs, b_rs, b_gs, o_rs, o_gs, T;
+};
+// grouped calls: rows of one buffer are contiguous, one after the other
+Layout grouped_layout(drgg_op op, int64_t N, int64_t K) {
+    if (op == DRGG_OP_FWD) return Layout{K, 0, 0, 0, N, 0, 0};
+    if (op == DRGG_OP_DGRAD) return Layout{N, 0, 0, 0, K, 0, 0};
+    return Layout{N, 0, K, 0, 0, 0, 0};   // weight gradient: A = G rows, B = X rows
+}
+void set_layout(GemmArgs& a, const Layout& L) {
+    a.a_rs = L.a_rs; a.a_gs = L.a_gs; a.b_rs = L.b_rs; a.b_gs = L.b_gs;
+    a.o_rs = L.o_rs; a.o_gs = L.o_gs; a.T = L.T;
+}
+
+// A batched buffer of B batches x T rows of `row` elements at element
+// strides (rs, bs): strides are multiples of 8 (16-byte rows), a row fits
+// in its stride, per-lane offsets inside a tile stay below 2^31 (rs <=
+// 2^22) and the last element's index fits in 62 bits.  With `output`, no
+// two rows may overlap: the batches are either stacked (bs covers T rows)
+// or interleaved (rs covers B rows).
+drgg_status check_strides(int64_t rs, int64_t bs, int32_t B, int64_t T, int64_t row, bool output) {
+    if (rs < row || bs < 0 || rs > (int64_t(1) << 22)) return DRGG_ESHAPE;
+    if (rs % 8 != 0 || bs % 8 != 0) return DRGG_EALIGN;
+    int64_t a, b;
+    if (!mul_ok(T > 0 ? T - 1 : 0, rs, &a) || !mul_ok(B - 1, bs, &b) || a > kMaxBytes - b - row)
+        return DRGG_EOVERFLOW;
+    if (output && B > 1 && T > 0) {
+        const bool stacked = bs >= a + row;
+        int64_t c;
+        const bool interleaved = bs >= row && mul_ok(B - 1, bs, &c) && rs >= c + row;
+        if (!stacked && !interleaved) return DRGG_ESHAPE;
+    }
+    return DRGG_OK;
+}
+
 struct Plan {
     int tile;
     TileShape ts;
@@ -179,11 +215,12 @@ namespace {
 // operands reduction-contiguous), or null (W read transposed in the kernel).
 drgg_status run_fwd_dgrad(drgg_op op, const void* A, const void* W, const int32_t* offs, int32_t E,
                           int64_t M, int64_t N, int64_t K, drgg_dtype dt, void* out, hipStream_t s,
-                          void* WT = nullptr) {
+                          void* WT, const Layout& L) {
     drgg_status st = check_problem(E, M, N, K, dt);
     if (st != DRGG_OK) return st;
-    // with no tokens the token-indexed buffers may be empty (null)
-    if (!W || !offs || (M > 0 && (!A || !out))) return DRGG_EINVAL;
+    // with no tokens the token-indexed buffers may be empty (null); a
+    // batched call (L.T > 0 or M == 0 with uniform groups) has no offsets
+    if (!W || (!offs && L.T == 0 && M > 0) || (M > 0 && (!A || !out))) return DRGG_EINVAL;
     if (!aligned16(A) || !aligned16(W) || !aligned16(out) || (reinterpret_cast<uintptr_t>(offs) & 3u))
         return DRGG_EALIGN;
     if (M == 0) return DRGG_OK;   // no rows to write
@@ -199,6 +236,7 @@ drgg_status run_fwd_dgrad(drgg_op op, const void* A, const void* W, const int32_
     a.offs = offs;
     a.out = out;
     a.M = M; a.N = N; a.K = K; a.E = E;
+    set_layout(a, L);
     a.items_max = p.grid;
     a.reverse = (int32_t)(g_knob_reverse.load() != 0);
     if (op == DRGG_OP_DGRAD && WT) {
@@ -210,45 +248,12 @@ drgg_status run_fwd_dgrad(drgg_op op, const void* A, const void* W, const int32_
     return launch_status(launch_fwd_dgrad((int)op, p.tile, a, dt == DRGG_BF16, s));
 }
 
-}  // namespace
-}  // namespace drgg
-
-using namespace drgg;
-
-extern "C" {
-
-drgg_status grouped_gemm_fwd(const void* X, const void* W, const int32_t* group_offsets, int32_t E,
-                             int64_t M, int64_t N, int64_t K, drgg_dtype out_dtype, int deterministic,
-                             void* Y, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    (void)deterministic; (void)workspace; (void)workspace_bytes;   // one program for both variants
-    return run_fwd_dgrad(DRGG_OP_FWD, X, W, group_offsets, E, M, N, K, out_dtype, Y, stream);
-}
-
-drgg_status grouped_gemm_dgrad(const void* G, const void* W, const int32_t* group_offsets, int32_t E,
-                               int64_t M, int64_t N, int64_t K, drgg_dtype out_dtype, int deterministic,
-                               void* dX, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    (void)deterministic;
-    // with a large enough workspace, W^T goes there (the faster program;
-    // the results are bitwise the same either way)
+drgg_status run_wgrad(const void* X, const void* G, const int32_t* group_offsets, int32_t E, int64_t M, int64_t N,
+                      int64_t K, drgg_dtype out_dtype, int deterministic, void* dW, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream, const Layout& L) {
     drgg_status st = check_problem(E, M, N, K, out_dtype);
     if (st != DRGG_OK) return st;
-    Plan p;
-    st = make_plan(DRGG_OP_DGRAD, E, M, N, K, 1, 1, &p);
-    if (st != DRGG_OK) return st;
-    void* WT = nullptr;
-    if (workspace && workspace_bytes >= p.ws_bytes && p.ws_bytes > 0) {
-        if (!aligned16(workspace)) return DRGG_EALIGN;
-        WT = workspace;
-    }
-    return run_fwd_dgrad(DRGG_OP_DGRAD, G, W, group_offsets, E, M, N, K, out_dtype, dX, stream, WT);
-}
-
-drgg_status grouped_gemm_wgrad(const void* X, const void* G, const int32_t* group_offsets, int32_t E,
-                               int64_t M, int64_t N, int64_t K, drgg_dtype out_dtype, int deterministic,
-                               void* dW, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    drgg_status st = check_problem(E, M, N, K, out_dtype);
-    if (st != DRGG_OK) return st;
-    if (!group_offsets || !dW || (M > 0 && (!X || !G))) return DRGG_EINVAL;
+    if (!dW || (M > 0 && (!X || !G))) return DRGG_EINVAL;
     if (!aligned16(X) || !aligned16(G) || !aligned16(dW) ||
         (reinterpret_cast<uintptr_t>(group_offsets) & 3u))
         return DRGG_EALIGN;
@@ -271,6 +276,7 @@ drgg_status grouped_gemm_wgrad(const void* X, const void* G, const int32_t* grou
     a.offs = group_offsets;
     a.out = dW;
     a.M = M; a.N = N; a.K = K; a.E = E;
+    set_layout(a, L);
     a.reverse = (int32_t)(g_knob_reverse.load() != 0);
     const bool bf16 = out_dtype == DRGG_BF16;
     if (p.det) {
@@ -286,6 +292,115 @@ drgg_status grouped_gemm_wgrad(const void* X, const void* G, const int32_t* grou
     a.tilesum = static_cast<float*>(workspace);
     a.tickets = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + sums);
     return launch_status(launch_wgrad_atomic(p.tile, a, p.grid, bf16, stream));
+}
+
+// The data gradient: with a large enough workspace, W^T goes there (the
+// faster program; the results are bitwise the same either way).
+drgg_status run_dgrad(const void* G, const void* W, const int32_t* offs, int32_t E, int64_t M, int64_t N,
+                      int64_t K, drgg_dtype out_dtype, void* dX, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream, const Layout& L) {
+    drgg_status st = check_problem(E, M, N, K, out_dtype);
+    if (st != DRGG_OK) return st;
+    Plan p;
+    st = make_plan(DRGG_OP_DGRAD, E, M, N, K, 1, 1, &p);
+    if (st != DRGG_OK) return st;
+    void* WT = nullptr;
+    if (workspace && workspace_bytes >= p.ws_bytes && p.ws_bytes > 0) {
+        if (!aligned16(workspace)) return DRGG_EALIGN;
+        WT = workspace;
+    }
+    return run_fwd_dgrad(DRGG_OP_DGRAD, G, W, offs, E, M, N, K, out_dtype, dX, stream, WT, L);
+}
+
+// Checks shared by the batched calls; fills E, M and the layout.
+drgg_status batched_setup(drgg_op op, const drgg_batched* b, int32_t* E, int64_t* M, Layout* L) {
+    if (!b) return DRGG_EINVAL;
+    if (b->B < 1 || b->B > kMaxExperts) return DRGG_EINVAL;
+    if (b->T < 0 || b->N < 8 || b->K < 8) return DRGG_ESHAPE;
+    int64_t m;
+    if (!mul_ok(b->B, b->T, &m) || m > INT32_MAX) return DRGG_ESHAPE;
+    const int64_t alen = op == DRGG_OP_DGRAD ? b->N : b->K;   // A: dgrad G, else X
+    const int64_t olen = op == DRGG_OP_FWD ? b->N : b->K;     // out: Y or dX
+    drgg_status st = check_strides(b->a_row, b->a_batch, b->B, b->T, alen, false);
+    if (st != DRGG_OK) return st;
+    if (op == DRGG_OP_WGRAD) {
+        st = check_strides(b->b_row, b->b_batch, b->B, b->T, b->N, false);
+        if (st != DRGG_OK) return st;
+        // kernel operands: A = G rows (b_*), B = X rows (a_*)
+        *L = Layout{b->b_row, b->b_batch - b->T * b->b_row, b->a_row, b->a_batch - b->T * b->a_row, 0, 0, b->T};
+    } else {
+        st = check_strides(b->o_row, b->o_batch, b->B, b->T, olen, true);
+        if (st != DRGG_OK) return st;
+        *L = Layout{b->a_row, b->a_batch - b->T * b->a_row, 0, 0, b->o_row, b->o_batch - b->T * b->o_row, b->T};
+    }
+    *E = b->B;
+    *M = m;
+    return DRGG_OK;
+}
+
+}  // namespace
+}  // namespace drgg
+
+using namespace drgg;
+
+extern "C" {
+
+drgg_status grouped_gemm_fwd(const void* X, const void* W, const int32_t* group_offsets, int32_t E,
+                             int64_t M, int64_t N, int64_t K, drgg_dtype out_dtype, int deterministic,
+                             void* Y, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    (void)deterministic; (void)workspace; (void)workspace_bytes;   // one program for both variants
+    if (!group_offsets) return DRGG_EINVAL;
+    return run_fwd_dgrad(DRGG_OP_FWD, X, W, group_offsets, E, M, N, K, out_dtype, Y, stream, nullptr,
+                         grouped_layout(DRGG_OP_FWD, N, K));
+}
+
+drgg_status grouped_gemm_dgrad(const void* G, const void* W, const int32_t* group_offsets, int32_t E,
+                               int64_t M, int64_t N, int64_t K, drgg_dtype out_dtype, int deterministic,
+                               void* dX, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    (void)deterministic;
+    if (!group_offsets) return DRGG_EINVAL;
+    return run_dgrad(G, W, group_offsets, E, M, N, K, out_dtype, dX, workspace, workspace_bytes, stream,
+                     grouped_layout(DRGG_OP_DGRAD, N, K));
+}
+
+drgg_status grouped_gemm_wgrad(const void* X, const void* G, const int32_t* group_offsets, int32_t E,
+                               int64_t M, int64_t N, int64_t K, drgg_dtype out_dtype, int deterministic,
+                               void* dW, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!group_offsets) return DRGG_EINVAL;
+    return run_wgrad(X, G, group_offsets, E, M, N, K, out_dtype, deterministic, dW, workspace, workspace_bytes,
+                     stream, grouped_layout(DRGG_OP_WGRAD, N, K));
+}
+
+drgg_status batched_gemm_fwd(const void* X, const void* W, const drgg_batched* shape, drgg_dtype out_dtype,
+                             void* Y, hipStream_t stream) {
+    int32_t E;
+    int64_t M;
+    Layout L;
+    drgg_status st = batched_setup(DRGG_OP_FWD, shape, &E, &M, &L);
+    if (st != DRGG_OK) return st;
+    return run_fwd_dgrad(DRGG_OP_FWD, X, W, nullptr, E, M, shape->N, shape->K, out_dtype, Y, stream, nullptr, L);
+}
+
+drgg_status batched_gemm_dgrad(const void* G, const void* W, const drgg_batched* shape, drgg_dtype out_dtype,
+                               void* dX, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    int32_t E;
+    int64_t M;
+    Layout L;
+    drgg_status st = batched_setup(DRGG_OP_DGRAD, shape, &E, &M, &L);
+    if (st != DRGG_OK) return st;
+    return run_dgrad(G, W, nullptr, E, M, shape->N, shape->K, out_dtype, dX, workspace, workspace_bytes, stream, L);
+}
+
+drgg_status batched_gemm_wgrad(const void* X, const void* G, const drgg_batched* shape, drgg_dtype out_dtype,
+                               int deterministic, void* dW, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+    int32_t E;
+    int64_t M;
+    Layout L;
+    drgg_status st = batched_setup(DRGG_OP_WGRAD, shape, &E, &M, &L);
+    if (st != DRGG_OK) return st;
+    return run_wgrad(X, G, nullptr, E, M, shape->N, shape->K, out_dtype, deterministic, dW, workspace,
+                     workspace_bytes, stream, L);
 }
 
 drgg_status router_gemm_fp32_bf16x3(const float* X, const float* Wr, int64_t M, int64_t N, int64_t K,

@@ -13,13 +13,21 @@ namespace drgg {
 struct GemmArgs {
     const uint16_t* A;     // fwd: X   dgrad: G   wgrad: G  (BF16 bits)
     const uint16_t* B;     // fwd: W   dgrad: W   wgrad: X
-    const int32_t* offs;   // group offsets [E+1], device
+    const int32_t* offs;   // group offsets [E+1], device (null: uniform groups of T rows)
     void* out;             // Y / dX / dW
     float* partial;        // det wgrad: chunk partial slots [slot][N][K]
     int32_t* fold_info;    // det wgrad: [E][4] = T_e, chunks_e, first slot, 0 (chunk kernel -> fold)
     float* tilesum;        // non-det wgrad: FP32 tile sums [E*P][BM*BN]
     uint32_t* tickets;     // non-det wgrad: [E*P]
     int64_t M, N, K;
+    // Token-major operands and the fwd/dgrad output: row r (its index in the
+    // offsets' row space) of group e starts at element base + r * rs + e * gs.
+    // Grouped calls: rs = the row length, gs = 0.  Batched calls (offs null,
+    // groups of T rows): rs = the row stride, gs = batch stride - T * rs.
+    int64_t a_rs, a_gs;    // A: fwd X, dgrad G, wgrad G
+    int64_t b_rs, b_gs;    // wgrad B: X
+    int64_t o_rs, o_gs;    // fwd Y, dgrad dX
+    int64_t T;             // offs null: group e is rows e*T .. e*T+T-1
     int64_t chunk_max;     // det wgrad: longest chunk
     int64_t items_max;     // workgroups launched (fwd/dgrad/det wgrad)
     int32_t E;

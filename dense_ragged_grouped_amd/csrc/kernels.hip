@@ -84,13 +84,15 @@ struct Sched {
 
 // Fills s.offs[0..E] with the offsets clamped into [0, M] (and made
 // non-decreasing), and s.prefix[0..E] with the exclusive prefix of
-// work(e, T_e).  Must be called by all threads; ends with a barrier.
+// work(e, T_e).  With no offsets array (a batched call) the groups are
+// uniform: offs[e] = e * T.  Must be called by all threads; ends with a
+// barrier.
 template <class WorkFn>
-__device__ void build_schedule(Sched& s, const int32_t* __restrict__ offs, int E, int64_t M,
+__device__ void build_schedule(Sched& s, const int32_t* __restrict__ offs, int E, int64_t M, int64_t T,
                                WorkFn work) {
     const int tid = threadIdx.x, nthr = blockDim.x;
     for (int e = tid; e <= E; e += nthr) {
-        int64_t v = offs[e];
+        int64_t v = offs ? (int64_t)offs[e] : e * T;
         v = v < 0 ? 0 : (v > M ? M : v);
         s.offs[e] = (int32_t)v;
     }
@@ -1166,7 +1168,7 @@ __global__ __launch_bounds__(64 * WAVES) void gg_fwd_dgrad_kernel(GemmArgs a) {
     // output columns: N (forward) or K (data gradient)
     const int64_t ncols = OP == 0 ? a.N : a.K;
     const int32_t ntn = (int32_t)((ncols + BN - 1) / BN);
-    build_schedule(sch, a.offs, a.E, a.M,
+    build_schedule(sch, a.offs, a.E, a.M, a.T,
                    [=](int, int32_t T) { return ((T + BM - 1) / BM) * ntn; });
     const int64_t total = uni(sch.prefix[a.E]);
     const int64_t G = gridDim.x;
@@ -1187,22 +1189,22 @@ __global__ __launch_bounds__(64 * WAVES) void gg_fwd_dgrad_kernel(GemmArgs a) {
         t.cols = (int32_t)min<int64_t>(BN, ncols - c0);
         t.e = e;
         if constexpr (OP == 0) {   // Y = X W^T: both reduction-contiguous
-            t.A = Operand{a.A + t0 * a.K, a.K, t.rows, (int32_t)a.K};
+            t.A = Operand{a.A + t0 * a.a_rs + e * a.a_gs, a.a_rs, t.rows, (int32_t)a.K};
             t.B = Operand{We + c0 * a.K, a.K, t.cols, (int32_t)a.K};
         } else if constexpr (OP == 1) {   // dX = G W: W is [n][k], reduction n strided
-            t.A = Operand{a.A + t0 * a.N, a.N, t.rows, (int32_t)a.N};
+            t.A = Operand{a.A + t0 * a.a_rs + e * a.a_gs, a.a_rs, t.rows, (int32_t)a.N};
             t.B = Operand{We + c0, a.K, t.cols, (int32_t)a.N};
         } else {                   // dX = G (W^T)^T: W^T is [k][n], reduction n contiguous
-            t.A = Operand{a.A + t0 * a.N, a.N, t.rows, (int32_t)a.N};
+            t.A = Operand{a.A + t0 * a.a_rs + e * a.a_gs, a.a_rs, t.rows, (int32_t)a.N};
             t.B = Operand{We + c0 * a.N, a.N, t.cols, (int32_t)a.N};
         }
         w += G;
     };
     void* out = a.out;
     auto finish = [&](const TileInfo& t, const TileMma<BM, BN, true, BK, WAVES>& mma) {
-        void* base = OUT_BF16 ? (void*)(reinterpret_cast<uint16_t*>(out) + t.o0 * ncols + t.o1)
-                              : (void*)(reinterpret_cast<float*>(out) + t.o0 * ncols + t.o1);
-        store_tile_lines<OUT_BF16, ep_rows(BM, BN)>(mma, (lds_t*)ep, base, ncols, t.rows, t.cols);
+        const int64_t o = t.o0 * a.o_rs + (int64_t)t.e * a.o_gs + t.o1;
+        void* base = OUT_BF16 ? (void*)(reinterpret_cast<uint16_t*>(out) + o) : (void*)(reinterpret_cast<float*>(out) + o);
+        store_tile_lines<OUT_BF16, ep_rows(BM, BN)>(mma, (lds_t*)ep, base, a.o_rs, t.rows, t.cols);
     };
     TileRunner<BM, BN, true, BK, WAVES> runner;
     runner.st = stg;
@@ -1227,7 +1229,7 @@ __global__ __launch_bounds__((64 * wgrad_det_waves<BM, BN>())) void gg_wgrad_det
     const int32_t tn = (int32_t)((a.N + BM - 1) / BM), tk = (int32_t)((a.K + BN - 1) / BN);
     const int32_t P = tn * tk;
     const int64_t cmax = a.chunk_max;
-    build_schedule(sch, a.offs, a.E, a.M,
+    build_schedule(sch, a.offs, a.E, a.M, a.T,
                    [=](int, int32_t T) { return P * chunks_dev(T, cmax); });
     // partial slots: experts cut into more than one chunk, in expert order
     if (threadIdx.x == 0) {
@@ -1275,8 +1277,8 @@ __global__ __launch_bounds__((64 * wgrad_det_waves<BM, BN>())) void gg_wgrad_det
         t.e = e;
         t.aux = nch == 1 ? -1 : uni(slot_base[e]) + chunk;   // -1: store the output directly
         // dW[n][k] = sum_t G[t][n] X[t][k]: both operands token-major (MN-major)
-        t.A = Operand{a.A + tb * a.N + n0, a.N, t.rows, len};
-        t.B = Operand{a.B + tb * a.K + k0, a.K, t.cols, len};
+        t.A = Operand{a.A + tb * a.a_rs + e * a.a_gs + n0, a.a_rs, t.rows, len};
+        t.B = Operand{a.B + tb * a.b_rs + e * a.b_gs + k0, a.b_rs, t.cols, len};
         w = snake_item(++round, wb, G);
     };
     auto finish = [&](const TileInfo& t, const TileMma<BM, BN, false, false, WV>& mma) {
@@ -1387,7 +1389,7 @@ __global__ __launch_bounds__(kGemmThreads) void gg_wgrad_atomic_kernel(GemmArgs 
     const int32_t tn = (int32_t)((a.N + BM - 1) / BM), tk = (int32_t)((a.K + BN - 1) / BN);
     const int32_t P = tn * tk;
     const int64_t cmax = a.chunk_max;
-    build_schedule(sch, a.offs, a.E, a.M, [=](int, int32_t T) { return P * unit_chunks(T, cmax); });
+    build_schedule(sch, a.offs, a.E, a.M, a.T, [=](int, int32_t T) { return P * unit_chunks(T, cmax); });
     order_longest_first(sch, stg.b[0], a.E, [=](int32_t T) { return unit_chunk_len(T, cmax); },
                         [=](int32_t T) { return P * unit_chunks(T, cmax); });
     const int64_t total = uni(sch.prefix[a.E]);
@@ -1417,8 +1419,8 @@ __global__ __launch_bounds__(kGemmThreads) void gg_wgrad_atomic_kernel(GemmArgs 
         t.e = e;
         t.aux = nch == 1 ? -1 : tile;   // -1: the whole tile in this item, store directly
         t.aux2 = nch;                   // pieces of a split tile
-        t.A = Operand{a.A + tb * a.N + n0, a.N, t.rows, len};
-        t.B = Operand{a.B + tb * a.K + k0, a.K, t.cols, len};
+        t.A = Operand{a.A + tb * a.a_rs + e * a.a_gs + n0, a.a_rs, t.rows, len};
+        t.B = Operand{a.B + tb * a.b_rs + e * a.b_gs + k0, a.b_rs, t.cols, len};
         w = snake_item(++round, wb, G);
     };
     auto finish = [&](const TileInfo& t, const TileMma<BM, BN, false, false>& mma) {

@@ -118,10 +118,15 @@ inline int64_t wgs_per_cu(TileShape t, bool fwd_dgrad, bool det_wgrad) {
     return n < 1 ? 1 : n;
 }
 
-// Default output tile per program.
+// Default output tile per program: 256x256, except the skinny weight
+// gradient (N <= 64: 64x256) and outputs of at most 128 columns (Y has N,
+// dX and dW have K), where a 256-wide tile would be at least half masked:
+// 128x128 (measured on per-head projections with K = 128: data gradient
+// -12 %, weight gradient -5 %).
 inline int default_tile(int op, int64_t N, int64_t K) {
-    if (op == 2 && N <= 64) return kTile64x256;   // skinny weight gradient
-    (void)K;
+    if (op == 2 && N <= 64) return kTile64x256;
+    const int64_t cols = op == 0 ? N : K;
+    if (cols <= 128) return kTile128x128;
     return kTile256x256;
 }
 

@@ -152,6 +152,46 @@ drgg_status grouped_gemm_wgrad(const void *X, const void *G, const int32_t *grou
                                void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Batched projection GEMM: the projection family also covers batched
+ * products (PR #8363, Summary; its #8438 commit body names batched "MLA head
+ * rows"), read here as B independent products of one shape -- batch b has
+ * its own weight W[b] and T token rows -- with the token-major buffers
+ * addressed through element strides, so that a head-interleaved activation
+ * [T, H, K] (MLA's per-head projections, batch = head) is used in place:
+ *
+ *   row t of batch b of a token-major buffer = base + b*batch + t*row
+ *   (elements; each row is contiguous: K values for X and dX, N for G and Y)
+ *
+ * W [B, N, K] and dW [B, N, K] are contiguous.  Same programs, rounding and
+ * determinism as the grouped calls; the result is bitwise that of the
+ * grouped call on the same rows laid out contiguously with
+ * group_offsets = {0, T, 2T, ..., B*T}.  Strides: row >= the row length,
+ * batch >= 0, both multiples of 8, row <= 2^22 (DRGG_ESHAPE / DRGG_EALIGN
+ * otherwise); an output's rows must not overlap: its batches either stacked
+ * (batch >= (T-1)*row + row length) or interleaved (row >= (B-1)*batch +
+ * row length, batch >= row length), else DRGG_ESHAPE.  B in 1..1024,
+ * B*T <= 2^31-1.  Workspace: as for the grouped call with E = B,
+ * M = B*T (grouped_gemm_workspace_size); the forward needs none.
+ */
+typedef struct {
+    int32_t B;                 /* batches */
+    int64_t T;                 /* token rows per batch */
+    int64_t N, K;              /* output features, input features */
+    int64_t a_row, a_batch;    /* fwd, wgrad: X; dgrad: G */
+    int64_t b_row, b_batch;    /* wgrad: G (unused otherwise) */
+    int64_t o_row, o_batch;    /* fwd: Y; dgrad: dX (unused for wgrad) */
+} drgg_batched;
+
+drgg_status batched_gemm_fwd(const void *X, const void *W, const drgg_batched *shape,
+                             drgg_dtype out_dtype, void *Y, hipStream_t stream);
+drgg_status batched_gemm_dgrad(const void *G, const void *W, const drgg_batched *shape,
+                               drgg_dtype out_dtype, void *dX, void *workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+drgg_status batched_gemm_wgrad(const void *X, const void *G, const drgg_batched *shape,
+                               drgg_dtype out_dtype, int deterministic, void *dW,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * FP32 router GEMM out[m,n] = sum_k X[m,k] * Wr[n,k] computed on BF16 MFMA
  * as a BF16x3 split (PR #8363, Summary: "FP32 router GEMM (256 experts,
  * BF16x3 emulation)"): each FP32 operand value v is split into

@@ -79,6 +79,47 @@ def test_fwd_argument_checks(drgg):
     assert fwd(drgg, M=2 ** 31) == 2
 
 
+def batched(drgg, op, **kw):
+    """A batched call with fake device pointers whose arguments are invalid
+    (valid ones would reach the GPU)."""
+    f = dict(B=4, T=64, N=64, K=64, a_row=64, a_batch=64 * 64, b_row=64, b_batch=64 * 64,
+             o_row=64, o_batch=64 * 64)
+    ptr = {k: kw.pop(k) for k in ("X", "W", "Y") if k in kw}
+    f.update(kw)
+    b = drgg.Batched(**f)
+    X, W, Y = ptr.get("X", A16), ptr.get("W", A16), ptr.get("Y", A16)
+    lib = drgg.lib
+    if op == "fwd":
+        return lib.batched_gemm_fwd(X, W, ctypes.byref(b), 1, Y, None)
+    if op == "dgrad":
+        return lib.batched_gemm_dgrad(X, W, ctypes.byref(b), 1, Y, None, 0, None)
+    return lib.batched_gemm_wgrad(X, W, ctypes.byref(b), 1, 1, Y, None, 0, None)
+
+
+def test_batched_argument_checks(drgg):
+    for op in ("fwd", "dgrad", "wgrad"):
+        assert batched(drgg, op, B=0) == 1
+        assert batched(drgg, op, B=1025) == 1
+        assert batched(drgg, op, T=-1) == 2
+        assert batched(drgg, op, N=4) == 2
+        assert batched(drgg, op, a_row=60) == 2          # a row longer than its stride
+        assert batched(drgg, op, a_row=68) == 3          # stride not a multiple of 8
+        assert batched(drgg, op, a_batch=12) == 3
+        assert batched(drgg, op, a_row=2 ** 22 + 8) == 2
+        assert batched(drgg, op, a_batch=2 ** 61) == 4   # last element beyond 2^62
+        assert batched(drgg, op, B=2 ** 10, T=2 ** 22) == 2   # B*T beyond int32
+        assert batched(drgg, op, X=0) == 1
+    assert drgg.lib.batched_gemm_fwd(A16, A16, None, 1, A16, None) == 1
+    assert batched(drgg, "wgrad", b_row=32) == 2
+    assert batched(drgg, "wgrad", b_batch=4) == 3
+    # outputs whose rows would overlap: neither stacked nor interleaved batches
+    assert batched(drgg, "fwd", o_row=64, o_batch=64 * 32) == 2
+    assert batched(drgg, "fwd", o_row=128, o_batch=64) == 2
+    assert batched(drgg, "dgrad", o_row=64, o_batch=0) == 2
+    # a strided output layout that is valid passes the checks (and fails on the null X)
+    assert batched(drgg, "fwd", o_row=256, o_batch=64, X=0) == 1
+
+
 def test_wgrad_workspace_checks(drgg):
     lib = drgg.lib
     # deterministic: needs partial slots when experts may be cut into chunks
