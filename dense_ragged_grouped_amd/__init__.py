@@ -32,6 +32,7 @@ TILE_AUTO, TILE_256x256, TILE_128x128, TILE_256x128, TILE_128x256, TILE_64x256 =
 EXPORTS = (
     "grouped_gemm_fwd", "grouped_gemm_dgrad", "grouped_gemm_wgrad", "router_gemm_fp32_bf16x3",
     "batched_gemm_fwd", "batched_gemm_dgrad", "batched_gemm_wgrad",
+    "drgg_route_split", "drgg_route_clear", "drgg_route_count", "drgg_hold_cus",
     "grouped_gemm_workspace_size", "drgg_workspace_init", "drgg_plan", "drgg_wgrad_chunking",
     "drgg_set_knob", "drgg_timing_count", "drgg_timing_read", "drgg_status_string", "drgg_abi_version",
 )
@@ -72,6 +73,15 @@ def _load(path=LIB_PATH):
         raise ImportError(
             f"{path} is not built; run `python -m dense_ragged_grouped_amd.build` "
             "(the grouped GEMM has no fallback path)")
+    # One HIP runtime per process: libdrgg.so needs libamdhip64.so.7, which
+    # resolves to the runtime already loaded under that name.  torch bundles
+    # its own; loaded first, it serves both.  Loaded after this library (whose
+    # runpath finds the system runtime), torch would bring a second HIP/HSA
+    # runtime, and the one initialised last finds no device.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     vp, i32, i64, sz, c_int = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
     gemm = [vp, vp, vp, i32, i64, i64, i64, c_int, c_int, vp, vp, sz, vp]
@@ -95,6 +105,14 @@ def _load(path=LIB_PATH):
     lib.drgg_plan.restype = c_int
     lib.drgg_wgrad_chunking.argtypes = [i64, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
     lib.drgg_wgrad_chunking.restype = c_int
+    lib.drgg_route_split.argtypes = [i32, i64, i64, i64, c_int]
+    lib.drgg_route_split.restype = c_int
+    lib.drgg_hold_cus.argtypes = [c_int, i64, vp]
+    lib.drgg_hold_cus.restype = c_int
+    lib.drgg_route_clear.argtypes = []
+    lib.drgg_route_clear.restype = c_int
+    lib.drgg_route_count.argtypes = []
+    lib.drgg_route_count.restype = c_int
     lib.drgg_set_knob.argtypes = [c_int, i64]
     lib.drgg_set_knob.restype = c_int
     lib.drgg_timing_count.argtypes = []
@@ -142,18 +160,65 @@ def wgrad_chunking(T: int, chunk_max: int):
     return ln.value, n.value
 
 
-# the program a non-deterministic weight gradient runs (KNOB_NONDET): False =
-# routed to the deterministic one (the library default), True = split program
-_split_nondet = False
+def wgrad_runs_deterministic(E: int, M: int, N: int, K: int, out_dtype: int = BF16,
+                             deterministic: bool = True) -> bool:
+    """Whether a weight-gradient call runs the deterministic program: always
+    for deterministic=True; for deterministic=False unless the route table
+    (or KNOB_NONDET) sends the point to the split program."""
+    if deterministic:
+        return True
+    return plan(OP_WGRAD, E, M, N, K, out_dtype, False, 1)["unit"] == 0
+
+
+def route_split(E: int, M: int, N: int, K: int, out_dtype: int = BF16):
+    """Send non-deterministic weight-gradient calls at this exact point to the
+    split program (see load_routes)."""
+    _check(lib.drgg_route_split(E, M, N, K, out_dtype), "drgg_route_split")
+
+
+def hold_cus(cus: int, microseconds: int, stream=None):
+    """Calibration aid: occupy `cus` compute units for `microseconds` on
+    `stream` (default: the current stream)."""
+    torch = _torch()
+    _check(lib.drgg_hold_cus(int(cus), int(microseconds), _stream(torch.device("cuda"), stream)), "drgg_hold_cus")
+
+
+def route_clear():
+    _check(lib.drgg_route_clear(), "drgg_route_clear")
+
+
+def route_count() -> int:
+    return lib.drgg_route_count()
+
+
+DEFAULT_ROUTES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "routes_mi355x.json")
+
+
+def load_default_routes() -> int:
+    """Install the route table measured on MI355X (256 CUs) that ships with
+    the package (done at import unless DRGG_NO_ROUTES=1)."""
+    return load_routes(DEFAULT_ROUTES) if os.path.exists(DEFAULT_ROUTES) else 0
+
+
+def load_routes(path: str) -> int:
+    """Install the split points of a route table written by
+    `python -m dense_ragged_grouped_amd.calibrate` (JSON); returns how many.
+    The table applies to the kind of device it was measured on."""
+    import json
+    with open(path) as f:
+        table = json.load(f)
+    n = 0
+    for pt in table.get("points", []):
+        if pt.get("program") == "split":
+            route_split(pt["E"], pt["M"], pt["N"], pt["K"], pt.get("out_dtype", BF16))
+            n += 1
+    return n
 
 
 def set_knob(knob: int, value: int):
     """Test knobs (tile shape, stream-K grid, reverse walk, timing, split
     program for non-deterministic weight gradients); 0 restores the default."""
-    global _split_nondet
     _check(lib.drgg_set_knob(knob, int(value)), "drgg_set_knob")
-    if knob == KNOB_NONDET:
-        _split_nondet = bool(value)
 
 
 def last_call_kernel_times():
@@ -246,9 +311,11 @@ def _workspace(device, nbytes, workspace, deterministic, kind="wgrad"):
     if workspace is not None:
         buf = workspace.get(nbytes) if isinstance(workspace, Workspace) else workspace
     else:
-        # keyed by the program that runs: a routed non-deterministic call
-        # shares the deterministic buffer; the data gradient's W^T has its own
-        key = (str(device), "dgrad") if kind == "dgrad" else (str(device), bool(deterministic) or not _split_nondet)
+        # keyed by the program that runs (`deterministic` here: whether the
+        # deterministic program runs): a non-deterministic call routed to it
+        # shares its buffer of partials, the split program has its own,
+        # zeroed one; the data gradient's W^T has its own
+        key = (str(device), "dgrad") if kind == "dgrad" else (str(device), bool(deterministic))
         if key not in _default_ws:
             _default_ws[key] = Workspace(device)
         buf = _default_ws[key].get(nbytes)
@@ -334,7 +401,8 @@ def grouped_gemm_wgrad(X, G, group_offsets, out_dtype=None, deterministic=True, 
         if tuple(out.shape) != (E, N, K):
             raise ValueError("out has the wrong shape")
     nbytes = workspace_size(OP_WGRAD, E, M, N, K, code, deterministic)
-    ws_ptr, ws_bytes = _workspace(X.device, nbytes, workspace, deterministic)
+    ws_ptr, ws_bytes = _workspace(X.device, nbytes, workspace,
+                                  wgrad_runs_deterministic(E, M, N, K, code, deterministic))
     st = lib.grouped_gemm_wgrad(X.data_ptr(), G.data_ptr(), group_offsets.data_ptr(), E, M, N, K, code,
                                 int(bool(deterministic)), out.data_ptr(), ws_ptr, ws_bytes,
                                 _stream(X.device, stream))
@@ -433,7 +501,8 @@ def batched_gemm_wgrad(X, G, out_dtype=None, deterministic=True, out=None, works
         if tuple(out.shape) != (B, N, K):
             raise ValueError("out has the wrong shape")
     nbytes = workspace_size(OP_WGRAD, B, B * T, N, K, code, deterministic)
-    ws_ptr, ws_bytes = _workspace(X.device, nbytes, workspace, deterministic)
+    ws_ptr, ws_bytes = _workspace(X.device, nbytes, workspace,
+                                  wgrad_runs_deterministic(B, B * T, N, K, code, deterministic))
     b = Batched(B, T, N, K, X.stride(1), X.stride(0), G.stride(1), G.stride(0), 0, 0)
     st = lib.batched_gemm_wgrad(X.data_ptr(), G.data_ptr(), ctypes.byref(b), code, int(bool(deterministic)),
                                 out.data_ptr(), ws_ptr, ws_bytes, _stream(X.device, stream))
@@ -464,3 +533,7 @@ def workspace_init(buf, stream=None):
     """Zero a workspace tensor with the library's fill kernel."""
     _check(lib.drgg_workspace_init(buf.data_ptr(), buf.numel() * buf.element_size(),
                                    _stream(buf.device, stream)), "drgg_workspace_init")
+
+
+if os.environ.get("DRGG_NO_ROUTES", "0") in ("", "0"):
+    load_default_routes()

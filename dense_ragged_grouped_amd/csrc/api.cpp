@@ -7,6 +7,7 @@
 
 #include <atomic>
 #include <cstdint>
+#include <cstdio>
 #include <cstring>
 #include <mutex>
 
@@ -33,18 +34,29 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// The HIP error behind this thread's most recent DRGG_EDEVICE (its text is
+// appended to drgg_status_string(DRGG_EDEVICE)).
+thread_local hipError_t g_last_hip_error = hipSuccess;
+
+drgg_status device_error(hipError_t e) {
+    g_last_hip_error = e;
+    return DRGG_EDEVICE;
+}
+
 // CU count of the current device, cached per device.
 drgg_status current_cu_count(int* cus) {
     static std::mutex mu;
     static int cache[kMaxDevices] = {0};
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return DRGG_EDEVICE;
-    if (dev < 0 || dev >= kMaxDevices) return DRGG_EDEVICE;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return device_error(e);
+    if (dev < 0 || dev >= kMaxDevices) return DRGG_EUNSUPPORTED;
     std::lock_guard<std::mutex> lock(mu);
     if (cache[dev] == 0) {
         int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            return DRGG_EDEVICE;
+        e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return device_error(e);
+        if (n <= 0) return DRGG_EUNSUPPORTED;
         cache[dev] = n;
     }
     *cus = cache[dev];
@@ -103,6 +115,31 @@ drgg_status check_strides(int64_t rs, int64_t bs, int32_t B, int64_t T, int64_t 
     return DRGG_OK;
 }
 
+// Route table of the non-deterministic weight gradient: the problem points
+// (E, M, N, K, output type) that run the split program; every other point
+// runs the deterministic one.  Filled by the caller from a calibration
+// (see drgg_route_split); small and looked up on the host.
+constexpr int kMaxRoutes = 256;
+struct Route {
+    int32_t E;
+    int64_t M, N, K;
+    int dt;
+};
+struct RouteTable {
+    std::mutex mu;
+    Route r[kMaxRoutes];
+    int n = 0;
+} g_routes;
+
+bool routed_to_split(int32_t E, int64_t M, int64_t N, int64_t K, int dt) {
+    std::lock_guard<std::mutex> lock(g_routes.mu);
+    for (int i = 0; i < g_routes.n; ++i) {
+        const Route& q = g_routes.r[i];
+        if (q.E == E && q.M == M && q.N == N && q.K == K && q.dt == dt) return true;
+    }
+    return false;
+}
+
 struct Plan {
     int tile;
     TileShape ts;
@@ -116,15 +153,16 @@ struct Plan {
 // ws layout, det weight gradient: [partial slots: max_partials*N*K fp32][fold table: E int32x4]
 // ws layout, non-det weight gradient: [tile sums: E*P*BM*BN fp32][tickets: E*P u32]
 drgg_status make_plan(drgg_op op, int32_t E, int64_t M, int64_t N, int64_t K, int det, int cu_count,
-                      Plan* p) {
+                      Plan* p, int dt = DRGG_BF16) {
     std::memset(p, 0, sizeof *p);
-    // Route table for the non-deterministic weight gradient: on gfx950 the
-    // deterministic program (chunk partials + ordered fold) was faster at
-    // every measured shape, because the atomic tile sums of the split
-    // program are performed beyond the XCDs' L2s; its result is a valid
-    // non-deterministic result.  DRGG_KNOB_NONDET = 1 keeps the atomic
-    // program.
-    if (op == DRGG_OP_WGRAD && !det && g_knob_nondet.load() == 0) det = 1;
+    // The non-deterministic weight gradient runs the deterministic program
+    // (chunk partials + ordered fold; its result is a valid
+    // non-deterministic result) unless the route table sends the point to
+    // the split program; on gfx950 the deterministic program was the faster
+    // one at every measured point, because the split program's atomic tile
+    // sums are performed beyond the XCDs' L2s.  DRGG_KNOB_NONDET = 1 runs
+    // the split program at every point.
+    if (op == DRGG_OP_WGRAD && !det && g_knob_nondet.load() == 0 && !routed_to_split(E, M, N, K, dt)) det = 1;
     p->det = det;
     int tile = (int)g_knob_tile.load();
     if (tile < kTileAuto || tile > kTile64x256) tile = kTileAuto;
@@ -173,7 +211,7 @@ drgg_status make_plan(drgg_op op, int32_t E, int64_t M, int64_t N, int64_t K, in
     return DRGG_OK;
 }
 
-drgg_status launch_status(hipError_t e) { return e == hipSuccess ? DRGG_OK : DRGG_EDEVICE; }
+drgg_status launch_status(hipError_t e) { return e == hipSuccess ? DRGG_OK : device_error(e); }
 
 // ---- timing marks (DRGG_KNOB_TIMING) ----------------------------------------
 constexpr int kMaxMarks = 8;
@@ -241,7 +279,7 @@ drgg_status run_fwd_dgrad(drgg_op op, const void* A, const void* W, const int32_
     a.reverse = (int32_t)(g_knob_reverse.load() != 0);
     if (op == DRGG_OP_DGRAD && WT) {
         hipError_t e = launch_transpose_w(a.B, static_cast<uint16_t*>(WT), E, N, K, s);
-        if (e != hipSuccess) return DRGG_EDEVICE;
+        if (e != hipSuccess) return device_error(e);
         a.B = static_cast<const uint16_t*>(WT);
         return launch_status(launch_fwd_dgrad(2, p.tile, a, dt == DRGG_BF16, s));
     }
@@ -257,9 +295,10 @@ drgg_status run_wgrad(const void* X, const void* G, const int32_t* group_offsets
     if (!aligned16(X) || !aligned16(G) || !aligned16(dW) ||
         (reinterpret_cast<uintptr_t>(group_offsets) & 3u))
         return DRGG_EALIGN;
-    // the workspace size does not depend on the CU count: check it first
+    // the workspace size does not depend on the CU count: check it before
+    // touching the device
     Plan p;
-    st = make_plan(DRGG_OP_WGRAD, E, M, N, K, deterministic, 1, &p);
+    st = make_plan(DRGG_OP_WGRAD, E, M, N, K, deterministic, 1, &p, out_dtype);
     if (st != DRGG_OK) return st;
     if (p.ws_bytes > 0) {
         if (!workspace || workspace_bytes < p.ws_bytes) return DRGG_EWORKSPACE;
@@ -268,8 +307,10 @@ drgg_status run_wgrad(const void* X, const void* G, const int32_t* group_offsets
     int cus = 0;
     st = current_cu_count(&cus);
     if (st != DRGG_OK) return st;
-    st = make_plan(DRGG_OP_WGRAD, E, M, N, K, deterministic, cus, &p);
+    const size_t checked = p.ws_bytes;
+    st = make_plan(DRGG_OP_WGRAD, E, M, N, K, deterministic, cus, &p, out_dtype);
     if (st != DRGG_OK) return st;
+    if (p.ws_bytes != checked) return DRGG_EWORKSPACE;   // the route table changed in between
     GemmArgs a{};
     a.A = static_cast<const uint16_t*>(G);   // A rows: output rows n of dW (from G)
     a.B = static_cast<const uint16_t*>(X);   // B rows: output cols k of dW (from X)
@@ -427,7 +468,7 @@ drgg_status grouped_gemm_workspace_size(drgg_op op, int32_t E, int64_t M, int64_
     drgg_status st = check_problem(E, M, N, K, out_dtype);
     if (st != DRGG_OK) return st;
     Plan p;   // the workspace size does not depend on the CU count
-    st = make_plan(op, E, M, N, K, deterministic, cu_count > 0 ? cu_count : 1, &p);
+    st = make_plan(op, E, M, N, K, deterministic, cu_count > 0 ? cu_count : 1, &p, out_dtype);
     if (st != DRGG_OK) return st;
     *bytes = p.ws_bytes;
     return DRGG_OK;
@@ -450,7 +491,7 @@ drgg_status drgg_plan(drgg_op op, int32_t E, int64_t M, int64_t N, int64_t K, dr
         if (st != DRGG_OK) return st;
     }
     Plan p;
-    st = make_plan(op, E, M, N, K, deterministic, cu_count, &p);
+    st = make_plan(op, E, M, N, K, deterministic, cu_count, &p, out_dtype);
     if (st != DRGG_OK) return st;
     std::memset(out, 0, sizeof *out);
     out->tile_m = p.ts.bm;
@@ -472,6 +513,35 @@ drgg_status drgg_wgrad_chunking(int64_t T, int64_t chunk_max, int64_t* chunk_len
         return DRGG_EINVAL;
     wgrad_chunking(T, chunk_max, chunk_len, chunks);
     return DRGG_OK;
+}
+
+drgg_status drgg_route_split(int32_t E, int64_t M, int64_t N, int64_t K, drgg_dtype out_dtype) {
+    drgg_status st = check_problem(E, M, N, K, out_dtype);
+    if (st != DRGG_OK) return st;
+    std::lock_guard<std::mutex> lock(g_routes.mu);
+    for (int i = 0; i < g_routes.n; ++i) {
+        const Route& q = g_routes.r[i];
+        if (q.E == E && q.M == M && q.N == N && q.K == K && q.dt == (int)out_dtype) return DRGG_OK;
+    }
+    if (g_routes.n >= kMaxRoutes) return DRGG_EUNSUPPORTED;
+    g_routes.r[g_routes.n++] = Route{E, M, N, K, (int)out_dtype};
+    return DRGG_OK;
+}
+
+drgg_status drgg_hold_cus(int cus, int64_t microseconds, hipStream_t stream) {
+    if (cus < 1 || cus > 4096 || microseconds < 0 || microseconds > 1000000) return DRGG_EINVAL;
+    return launch_status(launch_hold_cus(cus, (uint64_t)microseconds * 100, stream));
+}
+
+drgg_status drgg_route_clear(void) {
+    std::lock_guard<std::mutex> lock(g_routes.mu);
+    g_routes.n = 0;
+    return DRGG_OK;
+}
+
+int drgg_route_count(void) {
+    std::lock_guard<std::mutex> lock(g_routes.mu);
+    return g_routes.n;
 }
 
 drgg_status drgg_set_knob(int knob, int64_t value) {
@@ -522,7 +592,12 @@ const char* drgg_status_string(drgg_status s) {
         case DRGG_EOVERFLOW: return "size overflow in 64-bit arithmetic";
         case DRGG_EWORKSPACE: return "workspace missing or too small";
         case DRGG_EUNSUPPORTED: return "unsupported on this device or combination";
-        case DRGG_EDEVICE: return "HIP error while querying the device or launching";
+        case DRGG_EDEVICE: {
+            thread_local char msg[256];
+            snprintf(msg, sizeof msg, "HIP error while querying the device or launching (%s: %s)",
+                     hipGetErrorName(g_last_hip_error), hipGetErrorString(g_last_hip_error));
+            return msg;
+        }
     }
     return "unknown status";
 }

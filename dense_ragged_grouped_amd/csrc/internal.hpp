@@ -42,6 +42,7 @@ hipError_t launch_wgrad_atomic(int tile, const GemmArgs& a, int64_t grid_n, bool
 hipError_t launch_router(const float* X, const float* Wr, float* out, int64_t M, int64_t N, int64_t K,
                          hipStream_t s);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_hold_cus(int n, uint64_t ticks, hipStream_t s);
 
 // Per-launch timing marks (a measurement knob, off by default): when on, an
 // event is recorded on the stream before every kernel launch of a call and

@@ -1843,6 +1843,23 @@ hipError_t launch_router(const float* X, const float* Wr, float* out, int64_t M,
     return hipGetLastError();
 }
 
+// Calibration aid: each workgroup takes (almost) all of one CU's LDS, so n
+// workgroups hold n CUs, and waits (sleeping) until `ticks` of the 100 MHz
+// real-time counter have passed, then exits.
+constexpr int kHoldLds = 160 * 1024 - 1024;
+__global__ __launch_bounds__(64) void hold_cus_kernel(uint64_t ticks) {
+    __shared__ char pad[kHoldLds];
+    pad[threadIdx.x] = 0;   // keeps the allocation
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    while (__builtin_amdgcn_s_memrealtime() - t0 < ticks) __builtin_amdgcn_s_sleep(8);
+    if (pad[(threadIdx.x + 1) & 63] != 0) pad[0] = 1;
+}
+
+hipError_t launch_hold_cus(int n, uint64_t ticks, hipStream_t s) {
+    hipLaunchKernelGGL(hold_cus_kernel, dim3((unsigned)n), dim3(64), 0, s, ticks);
+    return hipGetLastError();
+}
+
 // Fill kernel for workspace initialisation (a kernel rather than a memset so
 // that the call can be captured into a HIP graph and replayed).
 __global__ void zero_kernel(uint8_t* p, size_t bytes) {

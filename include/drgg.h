@@ -264,6 +264,35 @@ enum { DRGG_KNOB_TILE = 1, DRGG_KNOB_GRID = 2, DRGG_KNOB_REVERSE = 3, DRGG_KNOB_
 drgg_status drgg_set_knob(int knob, int64_t value);
 
 /*
+ * Route table of the non-deterministic weight gradient (HOST only).  A call
+ * with deterministic == 0 runs the deterministic program unless its point
+ * (E, M, N, K, out_dtype), matched exactly, is in this table; then it runs
+ * the split program (atomic FP32 tile sums and tickets, its workspace zeroed
+ * as described at grouped_gemm_wgrad; the batched weight gradient's point is
+ * E = B, M = B*T).  The entries come from a calibration on the device that
+ * will run them: the package's calibrate module measures both programs at a
+ * point and keeps the split one only where it passes the selection rule of
+ * PR #8363 (Summary; restated as three conditions in its #8438 commit body):
+ * faster in every run at the op level (one-sided paired sign test p < 0.05,
+ * median ratio < 0.99) in eager launches and graph replays, at most 3 %
+ * slower next to a kernel holding 8, 16 or 32 compute units, and the
+ * backward and checkpointed step at most 1.3 % slower.  DRGG_KNOB_NONDET = 1
+ * overrides the table (split program everywhere).
+ *   drgg_route_split   add a point (no-op if present; DRGG_EUNSUPPORTED when
+ *                      256 points are stored; shape checks as for the calls)
+ *   drgg_route_clear   remove every point
+ *   drgg_route_count   number of points stored
+ * Thread-safe; a change applies to calls planned afterwards.
+ */
+drgg_status drgg_route_split(int32_t E, int64_t M, int64_t N, int64_t K, drgg_dtype out_dtype);
+/* Calibration aid for the co-run condition: occupies `cus` compute units
+ * (one workgroup with a whole CU's LDS each) for `microseconds` on `stream`,
+ * then exits.  cus in 1..4096, microseconds in 0..10^6, else DRGG_EINVAL. */
+drgg_status drgg_hold_cus(int cus, int64_t microseconds, hipStream_t stream);
+drgg_status drgg_route_clear(void);
+int drgg_route_count(void);
+
+/*
  * With DRGG_KNOB_TIMING on: the number of kernels the most recent call
  * launched, and for kernel i (0-based, launch order) its name (*kernel, a
  * static string) and duration in milliseconds (*ms), both HOST pointers.
