@@ -18,7 +18,12 @@ def drgg():
         pytest.skip("no GPU")
     import dense_ragged_grouped_amd as d
     import dense_ragged_grouped_amd.autograd  # noqa: F401
-    return d
+    # the library's default route (other modules' fixtures select the split
+    # program): a non-deterministic weight gradient at these points is then
+    # bitwise reproducible, which the comparisons below rely on
+    d.set_knob(d.KNOB_NONDET, 0)
+    yield d
+    d.set_knob(d.KNOB_NONDET, 0)
 
 
 def problem(seed=401, E=4, M=1500, N=136, K=328, empty=(2,)):
