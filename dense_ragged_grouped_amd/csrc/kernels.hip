@@ -1490,7 +1490,7 @@ __global__ __launch_bounds__(kGemmThreads) void gg_wgrad_atomic_kernel(GemmArgs 
 
 // ---------------------------------------------------------------------------
 // FP32 router GEMM as a BF16x3 split on MFMA (flashinfer PR #8363, Summary:
-// "FP32 router GEMM (256 experts, BF16x3 emulation)").
+// a 256-expert router whose FP32 products are emulated by three BF16 ones).
 //   out[m,n] = sum_k X[m,k] Wr[n,k];  v = hi + lo, hi = bf16(v), lo = bf16(v - hi)
 //   per 16-step: acc += hi_x hi_w, then hi_x lo_w, then lo_x hi_w.
 //

@@ -26,7 +26,7 @@ constexpr int kTileK = 64;
 
 // Token unit of the non-deterministic (stream-K) weight gradient: the K range
 // of a split tile is handed out in 512-token units (flashinfer PR #8258,
-// summary: the "unordered K=512 path").
+// Summary: the k512 path, whose 512-token pieces are summed in no fixed order).
 constexpr int64_t kStreamKUnit = 512;
 
 // The reference CU count the deterministic chunk rule is written against.  It

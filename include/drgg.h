@@ -193,8 +193,9 @@ drgg_status batched_gemm_wgrad(const void *X, const void *G, const drgg_batched 
 
 /*
  * FP32 router GEMM out[m,n] = sum_k X[m,k] * Wr[n,k] computed on BF16 MFMA
- * as a BF16x3 split (PR #8363, Summary: "FP32 router GEMM (256 experts,
- * BF16x3 emulation)"): each FP32 operand value v is split into
+ * as a BF16x3 split (PR #8363, Summary: the family's router GEMM has 256
+ * experts and emulates FP32 with three BF16 products): each FP32 operand
+ * value v is split into
  * hi = bf16(v), lo = bf16(v - hi) (round to nearest even) and every product
  * is taken as hi*hi + hi*lo + lo*hi with FP32 accumulation.
  * X [M,K] FP32, Wr [N,K] FP32, out [M,N] FP32.  K must be a multiple of 8

@@ -31,8 +31,8 @@
  * double once to FP32 or to BF16 (round to nearest, ties to even, straight
  * from the double so there is no double rounding).
  *
- * The FP32 router GEMM ("an FP32 router GEMM (256 experts, BF16x3
- * emulation)", PR #8363, Summary) has two oracles here: the exact FP32 x FP32
+ * The FP32 router GEMM (PR #8363, Summary: 256 experts, FP32 emulated with
+ * three BF16 products) has two oracles here: the exact FP32 x FP32
  * product summed in binary64, and the BF16x3 emulation written out step by
  * step: hi = bf16(x), lo = bf16(x - hi) for both operands, and the sum of
  * hi*hi + hi*lo + lo*hi (the lo*lo term is dropped), in binary64.
