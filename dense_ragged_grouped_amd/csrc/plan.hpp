@@ -54,31 +54,6 @@ inline TileShape tile_shape(int id) {
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
-// Deterministic weight gradient, chunk rule part 1 (host): the longest chunk
-// an expert's token range is cut into.  A function of (E, M, N, K) only.
-//   P0    = output tiles per expert at a 256x256 reference tile
-//   S     = smallest chunk count per (balanced) expert whose item count fills
-//           whole waves of kRuleCUs to >= 90 %
-//   chunk_max = max(ceil(M / (E*S)), half a reference CU's share of the
-//               token-tile work, 512), rounded up to a multiple of 64.
-// Long experts are cut into more chunks; short ones are never cut.
-inline int64_t wgrad_chunk_max(int32_t E, int64_t M, int64_t N, int64_t K) {
-    if (M <= 0) return 512;
-    const int64_t p0 = ceil_div(N, 256) * ceil_div(K, 256);
-    const int64_t base = p0 * E;
-    int64_t s = 1;
-    for (; s < 64; ++s) {
-        const int64_t items = base * s;
-        const int64_t slots = kRuleCUs * ceil_div(items, kRuleCUs);
-        if (items * 10 >= slots * 9) break;
-    }
-    int64_t a = ceil_div(M, (int64_t)E * s);
-    int64_t b = ceil_div(ceil_div(M * p0, kRuleCUs), 2);
-    int64_t c = a > b ? a : b;
-    if (c < 512) c = 512;
-    return round_up(c, kTileK);
-}
-
 // Chunk rule part 2 (host mirror of the device function): an expert with T
 // tokens is cut into chunks of `len` tokens (the last one shorter), starting
 // at its first token.  S = ceil(T / chunk_max), len = ceil(T / S) rounded up
@@ -89,6 +64,42 @@ inline void wgrad_chunking(int64_t T, int64_t chunk_max, int64_t* len, int64_t* 
     const int64_t l = round_up(ceil_div(T, s), kTileK);
     *len = l;
     *chunks = ceil_div(T, l);
+}
+
+// What one work item costs beyond its reduction steps (pipeline fill and the
+// store of a 256x256 FP32 tile), in tokens of reduction: about eight 32-token
+// steps.
+constexpr int64_t kItemOverheadTokens = 256;
+
+// Deterministic weight gradient, chunk rule part 1 (host): the longest chunk
+// an expert's token range is cut into.  A function of (E, M, N, K) only.
+//   P0    = output tiles per expert at a 256x256 reference tile
+//   floor = max(half a reference CU's share of the token-tile work, 512)
+//   chunk_max(S) = max(ceil(M / (E*S)), floor) rounded up to a multiple of 64
+//   S     = the chunk count per balanced expert (ceil(M/E) tokens) that
+//           minimises the estimated time on kRuleCUs workgroups: the waves
+//           of its P0*E*chunks items times (its chunk length + the item
+//           overhead); the smallest S on ties (fewest partials).
+// Long experts are cut into more chunks; short ones are never cut.
+inline int64_t wgrad_chunk_max(int32_t E, int64_t M, int64_t N, int64_t K) {
+    if (M <= 0) return 512;
+    const int64_t p0 = ceil_div(N, 256) * ceil_div(K, 256);
+    const int64_t tb = ceil_div(M, (int64_t)E);
+    int64_t floor = ceil_div(ceil_div(M * p0, kRuleCUs), 2);
+    if (floor < 512) floor = 512;
+    int64_t best = 0, best_cost = 0;
+    for (int64_t s = 1; s <= 64; ++s) {
+        int64_t c = ceil_div(M, (int64_t)E * s);
+        c = round_up(c > floor ? c : floor, kTileK);
+        int64_t len, chunks;
+        wgrad_chunking(tb, c, &len, &chunks);
+        const int64_t cost = ceil_div(p0 * E * chunks, kRuleCUs) * (len + kItemOverheadTokens);
+        if (best == 0 || cost < best_cost) {
+            best = c;
+            best_cost = cost;
+        }
+    }
+    return best;
 }
 
 // Partial slots the deterministic weight gradient may need: only experts cut

@@ -166,6 +166,12 @@ def test_chunk_rule_values(drgg):
     assert cm["down"] == 6144 and drgg.wgrad_chunking(42987, cm["down"])[1] == 7
     assert cm["square"] == 16384 and drgg.wgrad_chunking(16384, cm["square"]) == (16384, 1)
     assert drgg.wgrad_chunking(128, cm["tiny"]) == (128, 1)
+    # skinny dense: 16 equal chunks, 16 tiles x 16 chunks = one full wave of 256 items
+    for n in (48, 64):
+        c = drgg.plan(drgg.OP_WGRAD, 1, 16384, n, 4096, drgg.FP32, True)["chunk_max"]
+        assert c == 1024 and drgg.wgrad_chunking(16384, c) == (1024, 16)
+    for n, want in ((512, 2048), (1024, 4096)):
+        assert drgg.plan(drgg.OP_WGRAD, 1, 16384, n, 4096, drgg.FP32, True)["chunk_max"] == want
 
 
 @pytest.mark.parametrize("chunk_max", [512, 1152, 6144, 12288, 16384])
