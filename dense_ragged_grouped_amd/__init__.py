@@ -277,6 +277,21 @@ def _stream(device, stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on_one_device(stream, *tensors):
+    """Check that the tensors of one call (None entries skipped) and the
+    stream, if given, are on one device, and return a context that makes
+    that device current for the launch (the library plans for, and launches
+    on, the current device)."""
+    torch = _torch()
+    dev = tensors[0].device
+    for t in tensors[1:]:
+        if t is not None and t.device != dev:
+            raise ValueError(f"the tensors of one call must be on one device ({dev} and {t.device})")
+    if stream is not None and stream.device != dev:
+        raise ValueError(f"the stream is on {stream.device}, the tensors on {dev}")
+    return torch.cuda.device(dev)
+
+
 class Workspace:
     """Device workspace for the weight gradient, grown on demand.
 
@@ -310,6 +325,8 @@ def _workspace(device, nbytes, workspace, deterministic, kind="wgrad"):
         return None, 0
     if workspace is not None:
         buf = workspace.get(nbytes) if isinstance(workspace, Workspace) else workspace
+        if buf is not None and buf.device != device:
+            raise ValueError(f"the workspace is on {buf.device}, the operands on {device}")
     else:
         # keyed by the program that runs (`deterministic` here: whether the
         # deterministic program runs): a non-deterministic call routed to it
@@ -324,7 +341,7 @@ def _workspace(device, nbytes, workspace, deterministic, kind="wgrad"):
     return ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size()
 
 
-def _offsets(offsets, E_hint=None):
+def _offsets(offsets):
     torch = _torch()
     _need(offsets, torch.int32, "group_offsets", 1)
     return offsets.numel() - 1
@@ -347,8 +364,9 @@ def grouped_gemm_fwd(X, W, group_offsets, out_dtype=None, deterministic=True, ou
         _need(out, _torch_dtype(code), "out", 2)
         if tuple(out.shape) != (M, N):
             raise ValueError("out has the wrong shape")
-    st = lib.grouped_gemm_fwd(X.data_ptr(), W.data_ptr(), group_offsets.data_ptr(), E, M, N, K, code,
-                              int(bool(deterministic)), out.data_ptr(), None, 0, _stream(X.device, stream))
+    with _on_one_device(stream, X, W, group_offsets, out):
+        st = lib.grouped_gemm_fwd(X.data_ptr(), W.data_ptr(), group_offsets.data_ptr(), E, M, N, K, code,
+                                  int(bool(deterministic)), out.data_ptr(), None, 0, _stream(X.device, stream))
     _check(st, "grouped_gemm_fwd")
     return out
 
@@ -374,10 +392,11 @@ def grouped_gemm_dgrad(G, W, group_offsets, out_dtype=None, deterministic=True, 
         if tuple(out.shape) != (M, K):
             raise ValueError("out has the wrong shape")
     nbytes = workspace_size(OP_DGRAD, E, M, N, K, code, deterministic)
-    ws_ptr, ws_bytes = _workspace(G.device, nbytes, workspace, deterministic, kind="dgrad")
-    st = lib.grouped_gemm_dgrad(G.data_ptr(), W.data_ptr(), group_offsets.data_ptr(), E, M, N, K, code,
-                                int(bool(deterministic)), out.data_ptr(), ws_ptr, ws_bytes,
-                                _stream(G.device, stream))
+    with _on_one_device(stream, G, W, group_offsets, out):
+        ws_ptr, ws_bytes = _workspace(G.device, nbytes, workspace, deterministic, kind="dgrad")
+        st = lib.grouped_gemm_dgrad(G.data_ptr(), W.data_ptr(), group_offsets.data_ptr(), E, M, N, K, code,
+                                    int(bool(deterministic)), out.data_ptr(), ws_ptr, ws_bytes,
+                                    _stream(G.device, stream))
     _check(st, "grouped_gemm_dgrad")
     return out
 
@@ -401,11 +420,12 @@ def grouped_gemm_wgrad(X, G, group_offsets, out_dtype=None, deterministic=True, 
         if tuple(out.shape) != (E, N, K):
             raise ValueError("out has the wrong shape")
     nbytes = workspace_size(OP_WGRAD, E, M, N, K, code, deterministic)
-    ws_ptr, ws_bytes = _workspace(X.device, nbytes, workspace,
-                                  wgrad_runs_deterministic(E, M, N, K, code, deterministic))
-    st = lib.grouped_gemm_wgrad(X.data_ptr(), G.data_ptr(), group_offsets.data_ptr(), E, M, N, K, code,
-                                int(bool(deterministic)), out.data_ptr(), ws_ptr, ws_bytes,
-                                _stream(X.device, stream))
+    with _on_one_device(stream, X, G, group_offsets, out):
+        ws_ptr, ws_bytes = _workspace(X.device, nbytes, workspace,
+                                      wgrad_runs_deterministic(E, M, N, K, code, deterministic))
+        st = lib.grouped_gemm_wgrad(X.data_ptr(), G.data_ptr(), group_offsets.data_ptr(), E, M, N, K, code,
+                                    int(bool(deterministic)), out.data_ptr(), ws_ptr, ws_bytes,
+                                    _stream(X.device, stream))
     _check(st, "grouped_gemm_wgrad")
     return out
 
@@ -451,8 +471,9 @@ def batched_gemm_fwd(X, W, out_dtype=None, out=None, stream=None):
     code = _dtype_code(out_dtype if out_dtype is not None else torch.bfloat16)
     out = _out_rows(out, (B, T, N), code, X.device)
     b = Batched(B, T, N, K, X.stride(1), X.stride(0), 0, 0, out.stride(1), out.stride(0))
-    st = lib.batched_gemm_fwd(X.data_ptr(), W.data_ptr(), ctypes.byref(b), code, out.data_ptr(),
-                              _stream(X.device, stream))
+    with _on_one_device(stream, X, W, out):
+        st = lib.batched_gemm_fwd(X.data_ptr(), W.data_ptr(), ctypes.byref(b), code, out.data_ptr(),
+                                  _stream(X.device, stream))
     _check(st, "batched_gemm_fwd")
     return out
 
@@ -472,10 +493,11 @@ def batched_gemm_dgrad(G, W, out_dtype=None, out=None, workspace=None, stream=No
     code = _dtype_code(out_dtype if out_dtype is not None else torch.bfloat16)
     out = _out_rows(out, (B, T, K), code, G.device)
     nbytes = workspace_size(OP_DGRAD, B, B * T, N, K, code, True)
-    ws_ptr, ws_bytes = _workspace(G.device, nbytes, workspace, True, kind="dgrad")
     b = Batched(B, T, N, K, G.stride(1), G.stride(0), 0, 0, out.stride(1), out.stride(0))
-    st = lib.batched_gemm_dgrad(G.data_ptr(), W.data_ptr(), ctypes.byref(b), code, out.data_ptr(), ws_ptr,
-                                ws_bytes, _stream(G.device, stream))
+    with _on_one_device(stream, G, W, out):
+        ws_ptr, ws_bytes = _workspace(G.device, nbytes, workspace, True, kind="dgrad")
+        st = lib.batched_gemm_dgrad(G.data_ptr(), W.data_ptr(), ctypes.byref(b), code, out.data_ptr(), ws_ptr,
+                                    ws_bytes, _stream(G.device, stream))
     _check(st, "batched_gemm_dgrad")
     return out
 
@@ -501,11 +523,12 @@ def batched_gemm_wgrad(X, G, out_dtype=None, deterministic=True, out=None, works
         if tuple(out.shape) != (B, N, K):
             raise ValueError("out has the wrong shape")
     nbytes = workspace_size(OP_WGRAD, B, B * T, N, K, code, deterministic)
-    ws_ptr, ws_bytes = _workspace(X.device, nbytes, workspace,
-                                  wgrad_runs_deterministic(B, B * T, N, K, code, deterministic))
     b = Batched(B, T, N, K, X.stride(1), X.stride(0), G.stride(1), G.stride(0), 0, 0)
-    st = lib.batched_gemm_wgrad(X.data_ptr(), G.data_ptr(), ctypes.byref(b), code, int(bool(deterministic)),
-                                out.data_ptr(), ws_ptr, ws_bytes, _stream(X.device, stream))
+    with _on_one_device(stream, X, G, out):
+        ws_ptr, ws_bytes = _workspace(X.device, nbytes, workspace,
+                                      wgrad_runs_deterministic(B, B * T, N, K, code, deterministic))
+        st = lib.batched_gemm_wgrad(X.data_ptr(), G.data_ptr(), ctypes.byref(b), code, int(bool(deterministic)),
+                                    out.data_ptr(), ws_ptr, ws_bytes, _stream(X.device, stream))
     _check(st, "batched_gemm_wgrad")
     return out
 
@@ -523,8 +546,11 @@ def router_gemm_fp32_bf16x3(X, Wr, out=None, stream=None):
         out = torch.empty((M, N), dtype=torch.float32, device=X.device)
     else:
         _need(out, torch.float32, "out", 2)
-    st = lib.router_gemm_fp32_bf16x3(X.data_ptr(), Wr.data_ptr(), M, N, K, out.data_ptr(),
-                                     _stream(X.device, stream))
+        if tuple(out.shape) != (M, N):
+            raise ValueError(f"out has shape {tuple(out.shape)}, expected {(M, N)}")
+    with _on_one_device(stream, X, Wr, out):
+        st = lib.router_gemm_fp32_bf16x3(X.data_ptr(), Wr.data_ptr(), M, N, K, out.data_ptr(),
+                                         _stream(X.device, stream))
     _check(st, "router_gemm_fp32_bf16x3")
     return out
 

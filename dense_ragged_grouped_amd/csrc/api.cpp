@@ -308,9 +308,12 @@ drgg_status run_wgrad(const void* X, const void* G, const int32_t* group_offsets
     st = current_cu_count(&cus);
     if (st != DRGG_OK) return st;
     const size_t checked = p.ws_bytes;
+    const int checked_det = p.det;
     st = make_plan(DRGG_OP_WGRAD, E, M, N, K, deterministic, cus, &p, out_dtype);
     if (st != DRGG_OK) return st;
-    if (p.ws_bytes != checked) return DRGG_EWORKSPACE;   // the route table changed in between
+    // the route table changed in between: the workspace was checked (and
+    // may have been prepared) for the other program
+    if (p.ws_bytes != checked || p.det != checked_det) return DRGG_EWORKSPACE;
     GemmArgs a{};
     a.A = static_cast<const uint16_t*>(G);   // A rows: output rows n of dW (from G)
     a.B = static_cast<const uint16_t*>(X);   // B rows: output cols k of dW (from X)

@@ -295,3 +295,13 @@ def test_error_paths(drgg):
     with pytest.raises(drgg.DrggError) as ei:
         drgg.grouped_gemm_wgrad(dv["X"], dv["G"], dv["offs"], deterministic=False, workspace=small)
     assert ei.value.status == 5
+    # outputs of the wrong shape are refused before anything is launched
+    with pytest.raises(ValueError):
+        drgg.grouped_gemm_fwd(dv["X"], dv["W"], dv["offs"], out=torch.empty(prob.M - 1, prob.N, dtype=torch.bfloat16,
+                                                                              device="cuda"))
+    Xr = torch.zeros(40, 64, device="cuda")
+    Wr = torch.zeros(24, 64, device="cuda")
+    with pytest.raises(ValueError):
+        drgg.router_gemm_fp32_bf16x3(Xr, Wr, out=torch.empty(39, 24, device="cuda"))
+    with pytest.raises(ValueError):
+        drgg.router_gemm_fp32_bf16x3(Xr, Wr, out=torch.empty(24, 40, device="cuda"))
