@@ -45,12 +45,13 @@ def _points():
 
 
 def _counts(E, M, kind):
-    if kind == "zipf":
-        try:   # the Zipf(1.2) routing of the measured down workload
+    if kind == "zipf":   # the Zipf(1.2) routing of the measured down workload
+        try:
             import synth
-            return np.asarray(synth.config4_counts(), dtype=np.int64)
-        except ImportError:
-            pass
+        except ImportError as exc:
+            raise SystemExit("the Zipf-routed point needs the repository's seeded input generators "
+                             "(package `synth`): run from the repository root") from exc
+        return np.asarray(synth.config4_counts(), dtype=np.int64)
     c = np.full(E, M // E, dtype=np.int64)
     c[: M - int(c.sum())] += 1
     return c
