@@ -336,7 +336,7 @@ def ckpt_workloads(torch, prob, reps):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the grouped GEMM runs on a single MI355X with no collectives)", file=sys.stderr)
         sys.exit(2)
     import torch
