@@ -1223,9 +1223,11 @@ constexpr int wgrad_det_waves() { return BM == 256 && BN == 256 ? 8 : 4; }
 template <int BM, int BN, bool OUT_BF16>
 __global__ __launch_bounds__((64 * wgrad_det_waves<BM, BN>())) void gg_wgrad_det_kernel(GemmArgs a) {
     constexpr int WV = wgrad_det_waves<BM, BN>();
+    constexpr bool kStaged = wgrad_det_staged(BM, BN);
     DRGG_STAGES(BM, BN, false, false, stg);
     __shared__ Sched sch;
     __shared__ int32_t slot_base[kMaxExperts + 1];
+    __shared__ __attribute__((aligned(16))) char ep[kStaged ? WV * ep_rows(BM, BN) * 128 : 16];
     const int32_t tn = (int32_t)((a.N + BM - 1) / BM), tk = (int32_t)((a.K + BN - 1) / BN);
     const int32_t P = tn * tk;
     const int64_t cmax = a.chunk_max;
@@ -1287,10 +1289,12 @@ __global__ __launch_bounds__((64 * wgrad_det_waves<BM, BN>())) void gg_wgrad_det
             const int64_t off = (int64_t)t.e * a.N * a.K + t.o0 * a.K + t.o1;
             void* base = OUT_BF16 ? (void*)(reinterpret_cast<uint16_t*>(a.out) + off)
                                   : (void*)(reinterpret_cast<float*>(a.out) + off);
-            store_tile<OUT_BF16>(mma, base, ld, t.rows, t.cols);
+            if constexpr (kStaged) store_tile_lines<OUT_BF16, ep_rows(BM, BN)>(mma, (lds_t*)ep, base, ld, t.rows, t.cols);
+            else store_tile<OUT_BF16>(mma, base, ld, t.rows, t.cols);
         } else {           // a chunk partial of an expert cut into several chunks
             float* dst = a.partial + (int64_t)t.aux * a.N * a.K + t.o0 * a.K + t.o1;
-            store_tile<false>(mma, dst, ld, t.rows, t.cols);
+            if constexpr (kStaged) store_tile_lines<false, ep_rows(BM, BN)>(mma, (lds_t*)ep, dst, ld, t.rows, t.cols);
+            else store_tile<false>(mma, dst, ld, t.rows, t.cols);
         }
     };
     TileRunner<BM, BN, false, false, WV> runner;

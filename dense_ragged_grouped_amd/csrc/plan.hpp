@@ -114,17 +114,23 @@ inline int64_t wgrad_max_partials(int64_t M, int64_t chunk_max) {
 // kernels (kernels.hip): its LDS scratch is that many 128-byte rows per
 // wave.  Tiles below 256x128 share a CU and get the smaller scratch.
 constexpr int ep_rows(int bm, int bn) { return bm * bn >= 256 * 128 ? 16 : 8; }
+// Whether the deterministic weight gradient writes its tiles through a
+// per-wave LDS scratch in whole 128-byte lines (as the forward does): every
+// tile shape but 128x128, where the scratch would leave room for one
+// workgroup per CU instead of two.
+constexpr bool wgrad_det_staged(int bm, int bn) { return !(bm == 128 && bn == 128); }
 // Workgroups of a persistent grouped-GEMM kernel that fit on one CU's 160 KB
 // of LDS: kStages stages of (BM + BN) x kStageK BF16, the schedule tables
 // (10 KB; the deterministic weight gradient adds 4 KB of partial-slot
-// bases), the forward/data-gradient epilogue scratch, and 1 KB for
-// alignment.  Workgroups have 4 waves, except the 8 of the 256x256 forward,
-// data-gradient and deterministic weight-gradient kernels (only the first two
-// have the epilogue scratch).
+// bases), the epilogue scratch (forward, data gradient, and the deterministic
+// weight gradient where wgrad_det_staged), and 1 KB for alignment.
+// Workgroups have 4 waves, except the 8 of the 256x256 forward,
+// data-gradient and deterministic weight-gradient kernels.
 inline int64_t wgs_per_cu(TileShape t, bool fwd_dgrad, bool det_wgrad) {
-    const int64_t waves = fwd_dgrad && t.bm == 256 && t.bn == 256 ? 8 : 4;
+    const int64_t waves = (fwd_dgrad || det_wgrad) && t.bm == 256 && t.bn == 256 ? 8 : 4;
+    const bool ep = fwd_dgrad || (det_wgrad && wgrad_det_staged(t.bm, t.bn));
     const int64_t lds = (int64_t)kStages * (t.bm + t.bn) * kStageK * 2 + 10248 + (det_wgrad ? 4100 : 0) +
-                        (fwd_dgrad ? waves * ep_rows(t.bm, t.bn) * 128 : 0) + 1024;
+                        (ep ? waves * ep_rows(t.bm, t.bn) * 128 : 0) + 1024;
     const int64_t n = (160 * 1024) / lds;
     return n < 1 ? 1 : n;
 }
