@@ -649,8 +649,10 @@ __device__ __forceinline__ void wave_lds_sync() {
 // at 16 * (c ^ (rr & 7)), so the read-back is free of bank conflicts.  Masking
 // as in store_tile; cols must be a multiple of 8 (BF16) or 4 (FP32).  The
 // scratch is private to the wave, so a wave-level sync between the phases is
-// all it needs.
-template <bool OUT_BF16, int R, class Mma>
+// all it needs.  CPOL is the stores' cache policy: non-temporal for outputs;
+// 0 for data read back soon (the weight gradient's chunk partials, which the
+// fold then finds in the last-level cache).
+template <bool OUT_BF16, int R, int CPOL = kCpolNT, class Mma>
 __device__ __forceinline__ void store_tile_lines(const Mma& mma, lds_t* scr, void* out, int64_t ld, int rows,
                                                  int cols) {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -711,7 +713,7 @@ __device__ __forceinline__ void store_tile_lines(const Mma& mma, lds_t* scr, voi
                     const int rowb = s * R + row;            // row within the 32-row block
                     const int col = c0 + c * (16 / ES);
                     const uint32_t o = r0 + rowb < rows && col < cols ? (uint32_t)((rowb * ld + col) * ES) : kOOB;
-                    __builtin_amdgcn_raw_buffer_store_b128(v, rs, o, 0, kCpolNT);
+                    __builtin_amdgcn_raw_buffer_store_b128(v, rs, o, 0, CPOL);
                 }
                 wave_lds_sync();   // read back before the next round overwrites it
             }
@@ -1293,7 +1295,7 @@ __global__ __launch_bounds__((64 * wgrad_det_waves<BM, BN>())) void gg_wgrad_det
             else store_tile<OUT_BF16>(mma, base, ld, t.rows, t.cols);
         } else {           // a chunk partial of an expert cut into several chunks
             float* dst = a.partial + (int64_t)t.aux * a.N * a.K + t.o0 * a.K + t.o1;
-            if constexpr (kStaged) store_tile_lines<false, ep_rows(BM, BN)>(mma, (lds_t*)ep, dst, ld, t.rows, t.cols);
+            if constexpr (kStaged) store_tile_lines<false, ep_rows(BM, BN), 0>(mma, (lds_t*)ep, dst, ld, t.rows, t.cols);
             else store_tile<false>(mma, dst, ld, t.rows, t.cols);
         }
     };
