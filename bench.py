@@ -298,12 +298,13 @@ def batched_workloads(torch, drgg, reps):
 
 
 def ckpt_workloads(torch, prob, reps):
-    """The checkpointed step of the gate_up layer through autograd: one
-    grouped GEMM in a non-reentrant checkpoint, forward + backward (dX, dW),
-    with checkpoint early stop off ("ckpt": the backward recomputes the
-    forward, 4 GEMMs) and on ("ckpt_es": the recompute ends before the
-    forward kernel, 3 GEMMs).  GPU time from the first kernel to the last of
-    the step (stream events), inputs resident."""
+    """The gate_up layer trained under activation checkpointing through the
+    autograd layer (PR #8258, "Operations and shapes", ckpt and ckpt ES
+    rows): its forward and backward with the checkpoint's early stop
+    disabled ("ckpt": the backward runs the forward again, 4 GEMMs) and
+    enabled ("ckpt_es": the re-run stops before the forward kernel, 3 GEMMs).
+    GPU time from the first kernel to the last of the step (stream events),
+    inputs resident."""
     from dense_ragged_grouped_amd.autograd import checkpointed_grouped_linear
     X = to_dev_bf16(torch, prob.X).requires_grad_(True)
     W = to_dev_bf16(torch, prob.W).requires_grad_(True)

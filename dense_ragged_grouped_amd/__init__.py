@@ -26,6 +26,7 @@ LIB_PATH = os.path.join(_HERE, "libdrgg.so")
 BF16, FP32 = 0, 1
 OP_FWD, OP_DGRAD, OP_WGRAD = 0, 1, 2
 KNOB_TILE, KNOB_GRID, KNOB_REVERSE, KNOB_TIMING, KNOB_NONDET = 1, 2, 3, 4, 5
+KNOB_CHECK_OFFSETS, KNOB_CHECK_WORKSPACE = 6, 7
 TILE_AUTO, TILE_256x256, TILE_128x128, TILE_256x128, TILE_128x256, TILE_64x256 = range(6)
 
 # the symbols include/drgg.h declares
@@ -34,6 +35,7 @@ EXPORTS = (
     "batched_gemm_fwd", "batched_gemm_dgrad", "batched_gemm_wgrad",
     "drgg_route_split", "drgg_route_clear", "drgg_route_count", "drgg_hold_cus",
     "grouped_gemm_workspace_size", "drgg_workspace_init", "drgg_plan", "drgg_wgrad_chunking",
+    "drgg_tailsplit_units",
     "drgg_set_knob", "drgg_timing_count", "drgg_timing_read", "drgg_status_string", "drgg_abi_version",
 )
 
@@ -105,6 +107,8 @@ def _load(path=LIB_PATH):
     lib.drgg_plan.restype = c_int
     lib.drgg_wgrad_chunking.argtypes = [i64, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
     lib.drgg_wgrad_chunking.restype = c_int
+    lib.drgg_tailsplit_units.argtypes = [i64, i64, ctypes.POINTER(i64)]
+    lib.drgg_tailsplit_units.restype = c_int
     lib.drgg_route_split.argtypes = [i32, i64, i64, i64, c_int]
     lib.drgg_route_split.restype = c_int
     lib.drgg_hold_cus.argtypes = [c_int, i64, vp]
@@ -158,6 +162,16 @@ def wgrad_chunking(T: int, chunk_max: int):
     ln, n = ctypes.c_int64(), ctypes.c_int64()
     _check(lib.drgg_wgrad_chunking(T, chunk_max, ctypes.byref(ln), ctypes.byref(n)), "drgg_wgrad_chunking")
     return ln.value, n.value
+
+
+def tailsplit_units(tiles: int, workers: int):
+    """(tiles, units, full, split) of the tail-split rule: `tiles` equal
+    tiles on `workers` persistent workers; a partial last wave of
+    tail = tiles mod workers tiles is cut into 2 * tail half units when that
+    fits one wave, else every tile stays whole."""
+    out = (ctypes.c_int64 * 4)()
+    _check(lib.drgg_tailsplit_units(int(tiles), int(workers), out), "drgg_tailsplit_units")
+    return tuple(int(v) for v in out)
 
 
 def wgrad_runs_deterministic(E: int, M: int, N: int, K: int, out_dtype: int = BF16,
@@ -216,8 +230,9 @@ def load_routes(path: str) -> int:
 
 
 def set_knob(knob: int, value: int):
-    """Test knobs (tile shape, stream-K grid, reverse walk, timing, split
-    program for non-deterministic weight gradients); 0 restores the default."""
+    """Test knobs (tile shape, persistent grid, reverse walk, timing, split
+    program for non-deterministic weight gradients, the debug checks of the
+    offsets and of the split program's workspace); 0 restores the default."""
     _check(lib.drgg_set_knob(knob, int(value)), "drgg_set_knob")
 
 
@@ -295,36 +310,50 @@ def _on_one_device(stream, *tensors):
 class Workspace:
     """Device workspace for the weight gradient, grown on demand.
 
-    Allocated zeroed; the non-deterministic program leaves its tile sums and
-    tickets zero after every call, so the buffer stays valid for later calls.
-    One Workspace must not serve two calls in flight on different streams.
+    Allocated and zeroed on the stream of the call that needs it (so the
+    zeroing is ordered before that call's kernels, and torch's allocator
+    ties the memory to that stream); used on another stream, the buffer is
+    recorded on it, so that a buffer replaced by a larger one is not handed
+    out again before the calls using it have finished.  The split program
+    leaves its tile sums and tickets zero after every call, so the buffer
+    stays valid for later calls.  One Workspace must not serve two calls in
+    flight on different streams at once.
     """
 
     def __init__(self, device=None):
         torch = _torch()
         self.device = torch.device(device if device is not None else "cuda")
         self.buf = None
+        self.home = None
 
-    def get(self, nbytes: int):
+    def get(self, nbytes: int, stream=None):
         torch = _torch()
         if nbytes == 0:
             return None
+        s = stream if stream is not None else torch.cuda.current_stream(self.device)
         if self.buf is None or self.buf.numel() < nbytes:
-            self.buf = torch.zeros(nbytes + 256, dtype=torch.uint8, device=self.device)
+            with torch.cuda.stream(s):
+                self.buf = torch.zeros(nbytes + 256, dtype=torch.uint8, device=self.device)
+            self.home = s
+        elif s != self.home:
+            self.buf.record_stream(s)
         return self.buf
 
 
-# Default workspaces, one per (device, program): a deterministic call leaves
-# its FP32 partials in the buffer, while the split program needs its tile
-# sums and tickets to be zero, so the two never share a buffer.
+# Default workspaces, one per (device, stream, program): a deterministic call
+# leaves its FP32 partials in the buffer, while the split program needs its
+# tile sums and tickets to be zero, so the two never share a buffer; calls on
+# different streams may run at the same time, so they never share one either.
 _default_ws = {}
 
 
-def _workspace(device, nbytes, workspace, deterministic, kind="wgrad"):
+def _workspace(device, nbytes, workspace, deterministic, kind="wgrad", stream=None):
+    torch = _torch()
     if workspace is False:   # explicitly none (the data gradient's direct program)
         return None, 0
+    s = stream if stream is not None else torch.cuda.current_stream(device)
     if workspace is not None:
-        buf = workspace.get(nbytes) if isinstance(workspace, Workspace) else workspace
+        buf = workspace.get(nbytes, s) if isinstance(workspace, Workspace) else workspace
         if buf is not None and buf.device != device:
             raise ValueError(f"the workspace is on {buf.device}, the operands on {device}")
     else:
@@ -332,10 +361,11 @@ def _workspace(device, nbytes, workspace, deterministic, kind="wgrad"):
         # deterministic program runs): a non-deterministic call routed to it
         # shares its buffer of partials, the split program has its own,
         # zeroed one; the data gradient's W^T has its own
-        key = (str(device), "dgrad") if kind == "dgrad" else (str(device), bool(deterministic))
+        prog = "dgrad" if kind == "dgrad" else bool(deterministic)
+        key = (str(device), s.cuda_stream, prog)
         if key not in _default_ws:
             _default_ws[key] = Workspace(device)
-        buf = _default_ws[key].get(nbytes)
+        buf = _default_ws[key].get(nbytes, s)
     if buf is None:
         return None, 0
     return ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size()
@@ -393,7 +423,7 @@ def grouped_gemm_dgrad(G, W, group_offsets, out_dtype=None, deterministic=True, 
             raise ValueError("out has the wrong shape")
     nbytes = workspace_size(OP_DGRAD, E, M, N, K, code, deterministic)
     with _on_one_device(stream, G, W, group_offsets, out):
-        ws_ptr, ws_bytes = _workspace(G.device, nbytes, workspace, deterministic, kind="dgrad")
+        ws_ptr, ws_bytes = _workspace(G.device, nbytes, workspace, deterministic, kind="dgrad", stream=stream)
         st = lib.grouped_gemm_dgrad(G.data_ptr(), W.data_ptr(), group_offsets.data_ptr(), E, M, N, K, code,
                                     int(bool(deterministic)), out.data_ptr(), ws_ptr, ws_bytes,
                                     _stream(G.device, stream))
@@ -422,7 +452,7 @@ def grouped_gemm_wgrad(X, G, group_offsets, out_dtype=None, deterministic=True, 
     nbytes = workspace_size(OP_WGRAD, E, M, N, K, code, deterministic)
     with _on_one_device(stream, X, G, group_offsets, out):
         ws_ptr, ws_bytes = _workspace(X.device, nbytes, workspace,
-                                      wgrad_runs_deterministic(E, M, N, K, code, deterministic))
+                                      wgrad_runs_deterministic(E, M, N, K, code, deterministic), stream=stream)
         st = lib.grouped_gemm_wgrad(X.data_ptr(), G.data_ptr(), group_offsets.data_ptr(), E, M, N, K, code,
                                     int(bool(deterministic)), out.data_ptr(), ws_ptr, ws_bytes,
                                     _stream(X.device, stream))
@@ -495,7 +525,7 @@ def batched_gemm_dgrad(G, W, out_dtype=None, out=None, workspace=None, stream=No
     nbytes = workspace_size(OP_DGRAD, B, B * T, N, K, code, True)
     b = Batched(B, T, N, K, G.stride(1), G.stride(0), 0, 0, out.stride(1), out.stride(0))
     with _on_one_device(stream, G, W, out):
-        ws_ptr, ws_bytes = _workspace(G.device, nbytes, workspace, True, kind="dgrad")
+        ws_ptr, ws_bytes = _workspace(G.device, nbytes, workspace, True, kind="dgrad", stream=stream)
         st = lib.batched_gemm_dgrad(G.data_ptr(), W.data_ptr(), ctypes.byref(b), code, out.data_ptr(), ws_ptr,
                                     ws_bytes, _stream(G.device, stream))
     _check(st, "batched_gemm_dgrad")
@@ -526,7 +556,7 @@ def batched_gemm_wgrad(X, G, out_dtype=None, deterministic=True, out=None, works
     b = Batched(B, T, N, K, X.stride(1), X.stride(0), G.stride(1), G.stride(0), 0, 0)
     with _on_one_device(stream, X, G, out):
         ws_ptr, ws_bytes = _workspace(X.device, nbytes, workspace,
-                                      wgrad_runs_deterministic(B, B * T, N, K, code, deterministic))
+                                      wgrad_runs_deterministic(B, B * T, N, K, code, deterministic), stream=stream)
         st = lib.batched_gemm_wgrad(X.data_ptr(), G.data_ptr(), ctypes.byref(b), code, int(bool(deterministic)),
                                     out.data_ptr(), ws_ptr, ws_bytes, _stream(X.device, stream))
     _check(st, "batched_gemm_wgrad")

@@ -3,10 +3,11 @@ mixture-of-experts block, Y[t] = X[t] W[e(t)]^T for the tokens of each
 expert's contiguous range, with the backward dX = G W and dW = G^T X.
 
 Every product runs in the library's kernels (forward, data gradient, weight
-gradient); this module only wires them into torch.autograd.  It is what the
-checkpointed step of "ckpt" and "ckpt ES" times on PR #8258 ("Operations and
-shapes": one grouped GEMM in a non-reentrant checkpoint, forward + backward,
-with checkpoint early stop off and on).
+gradient); this module only wires them into torch.autograd.  It is the layer
+behind the checkpointed training step that PR #8258 times ("Operations and
+shapes", its ckpt and ckpt ES rows): the layer wrapped in activation
+checkpointing without re-entry, run forward and backward, once with the
+early-stop option of the checkpoint disabled and once enabled.
 
 Checkpoint early stop.  A custom autograd Function saves its tensors only
 after its forward has returned, so a non-reentrant checkpoint recomputing it
@@ -20,17 +21,26 @@ the kernel is not launched; with early stop off, or when a later operation of
 the checkpointed region needs Y, the forward runs as usual.  Outside any hook
 it uses save_for_backward.
 """
+import warnings
+
 import torch
 
 from . import grouped_gemm_dgrad, grouped_gemm_fwd, grouped_gemm_wgrad
+
+# torch's accessor for the innermost active saved-tensor hooks (internal API)
+_TOP_HOOKS = getattr(torch._C._autograd, "_top_saved_tensors_default_hooks", None)
+if _TOP_HOOKS is None:
+    warnings.warn("torch has no _top_saved_tensors_default_hooks: grouped_linear saves its tensors after the "
+                  "forward kernel, so a checkpoint with early stop still recomputes the forward", RuntimeWarning)
 
 
 def save_before_compute(ctx, *tensors):
     """Record `tensors` for the backward now, through the innermost
     saved-tensor hooks if any are active (a checkpoint, CPU offloading), else
-    with save_for_backward."""
-    top = getattr(torch._C._autograd, "_top_saved_tensors_default_hooks", None)
-    hooks = top(False) if top is not None else None
+    with save_for_backward.  Without torch's accessor for those hooks (warned
+    at import) the tensors are saved with save_for_backward, which is
+    correct but lets an early-stopping checkpoint run the forward kernel."""
+    hooks = _TOP_HOOKS(False) if _TOP_HOOKS is not None else None
     if hooks is None:
         ctx.packed = None
         ctx.save_for_backward(*tensors)

@@ -2,14 +2,17 @@
 //
 // Host-side argument checks in checked 64-bit arithmetic, planning (plan.hpp)
 // and kernel launches (kernels.hip) on the caller's stream.  Nothing here
-// allocates device memory or synchronises.
+// allocates device memory, and nothing synchronises except the two opt-in
+// debug checks (group offsets, split-program workspace).
 #include <hip/hip_runtime.h>
 
 #include <atomic>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <vector>
 
 #include "../../include/drgg.h"
 #include "internal.hpp"
@@ -20,6 +23,17 @@ namespace drgg {
 namespace {
 
 std::atomic<int64_t> g_knob_tile{0}, g_knob_grid{0}, g_knob_reverse{0}, g_knob_nondet{0};
+// Debug checks (DRGG_KNOB_CHECK_OFFSETS / DRGG_KNOB_CHECK_WORKSPACE): 1 = on,
+// 0 = the environment's setting (DRGG_CHECK_OFFSETS / DRGG_CHECK_WORKSPACE
+// set to anything but "0"), off when unset.
+std::atomic<int64_t> g_knob_check_offsets{0}, g_knob_check_ws{0};
+
+bool env_flag(const char* name) {
+    const char* v = std::getenv(name);
+    return v && *v && std::strcmp(v, "0") != 0;
+}
+bool checks_offsets() { return g_knob_check_offsets.load() != 0 || env_flag("DRGG_CHECK_OFFSETS"); }
+bool checks_workspace() { return g_knob_check_ws.load() != 0 || env_flag("DRGG_CHECK_WORKSPACE"); }
 
 constexpr int64_t kMaxBytes = (int64_t)1 << 62;
 constexpr int kMaxDevices = 64;
@@ -213,6 +227,34 @@ drgg_status make_plan(drgg_op op, int32_t E, int64_t M, int64_t N, int64_t K, in
 
 drgg_status launch_status(hipError_t e) { return e == hipSuccess ? DRGG_OK : device_error(e); }
 
+// Debug check of the group offsets (DRGG_CHECK_OFFSETS): a synchronous copy
+// to the host, then o[0] = 0, non-decreasing, o[E] = M, else DRGG_ESHAPE.
+// Nothing of the computation has been enqueued when it fails.
+drgg_status check_offsets_sync(const int32_t* offs, int32_t E, int64_t M, hipStream_t s) {
+    std::vector<int32_t> h((size_t)E + 1);
+    hipError_t e = hipMemcpyAsync(h.data(), offs, h.size() * sizeof(int32_t), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return device_error(e);
+    if (h[0] != 0 || (int64_t)h[(size_t)E] != M) return DRGG_ESHAPE;
+    for (int32_t i = 0; i < E; ++i)
+        if (h[(size_t)i + 1] < h[(size_t)i]) return DRGG_ESHAPE;
+    return DRGG_OK;
+}
+
+// Debug check of the split program's workspace (DRGG_CHECK_WORKSPACE): its
+// tile sums and tickets must be zero before a call (a buffer that served a
+// deterministic call holds partials); a synchronous copy to the host,
+// DRGG_EWORKSPACE if any byte is set.
+drgg_status check_workspace_zero(const void* ws, size_t bytes, hipStream_t s) {
+    std::vector<uint8_t> h(bytes);
+    hipError_t e = hipMemcpyAsync(h.data(), ws, bytes, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return device_error(e);
+    for (size_t i = 0; i < bytes; ++i)
+        if (h[i] != 0) return DRGG_EWORKSPACE;
+    return DRGG_OK;
+}
+
 // ---- timing marks (DRGG_KNOB_TIMING) ----------------------------------------
 constexpr int kMaxMarks = 8;
 std::atomic<int> g_timing_on{0};
@@ -261,6 +303,10 @@ drgg_status run_fwd_dgrad(drgg_op op, const void* A, const void* W, const int32_
     if (!W || (!offs && L.T == 0 && M > 0) || (M > 0 && (!A || !out))) return DRGG_EINVAL;
     if (!aligned16(A) || !aligned16(W) || !aligned16(out) || (reinterpret_cast<uintptr_t>(offs) & 3u))
         return DRGG_EALIGN;
+    if (offs && checks_offsets()) {
+        st = check_offsets_sync(offs, E, M, s);
+        if (st != DRGG_OK) return st;
+    }
     if (M == 0) return DRGG_OK;   // no rows to write
     int cus = 0;
     st = current_cu_count(&cus);
@@ -314,6 +360,14 @@ drgg_status run_wgrad(const void* X, const void* G, const int32_t* group_offsets
     // the route table changed in between: the workspace was checked (and
     // may have been prepared) for the other program
     if (p.ws_bytes != checked || p.det != checked_det) return DRGG_EWORKSPACE;
+    if (group_offsets && checks_offsets()) {
+        st = check_offsets_sync(group_offsets, E, M, stream);
+        if (st != DRGG_OK) return st;
+    }
+    if (!p.det && p.ws_bytes > 0 && checks_workspace()) {
+        st = check_workspace_zero(workspace, p.ws_bytes, stream);
+        if (st != DRGG_OK) return st;
+    }
     GemmArgs a{};
     a.A = static_cast<const uint16_t*>(G);   // A rows: output rows n of dW (from G)
     a.B = static_cast<const uint16_t*>(X);   // B rows: output cols k of dW (from X)
@@ -450,15 +504,16 @@ drgg_status batched_gemm_wgrad(const void* X, const void* G, const drgg_batched*
 drgg_status router_gemm_fp32_bf16x3(const float* X, const float* Wr, int64_t M, int64_t N, int64_t K,
                                     float* out, hipStream_t stream) {
     if (!X || !Wr || !out) return DRGG_EINVAL;
-    if (M < 0 || N < 1 || K < 8 || M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return DRGG_ESHAPE;
+    // N, K <= 2^22 keep every per-lane byte offset inside a 128-row block of
+    // the operands and of the output below 2^31
+    if (M < 0 || N < 1 || K < 8 || M > INT32_MAX || N > (int64_t(1) << 22) || K > (int64_t(1) << 22))
+        return DRGG_ESHAPE;
     if (K % 8 != 0 || N % 4 != 0) return DRGG_EALIGN;
     if (!aligned16(X) || !aligned16(Wr) || !aligned16(out)) return DRGG_EALIGN;
     int64_t t;
     if (!mul_ok(M, K, &t) || !mul_ok(t, 4, &t) || !mul_ok(M, N, &t) || !mul_ok(t, 4, &t) ||
         !mul_ok(N, K, &t) || !mul_ok(t, 4, &t))
         return DRGG_EOVERFLOW;
-    // per-lane byte offsets within a 128-row tile stay below 2^31
-    if (K > (int64_t(1) << 22)) return DRGG_ESHAPE;
     if (M == 0) return DRGG_OK;
     return launch_status(launch_router(X, Wr, out, M, N, K, stream));
 }
@@ -518,6 +573,16 @@ drgg_status drgg_wgrad_chunking(int64_t T, int64_t chunk_max, int64_t* chunk_len
     return DRGG_OK;
 }
 
+drgg_status drgg_tailsplit_units(int64_t tiles, int64_t workers, int64_t* out) {
+    if (!out || tiles < 0 || workers < 1) return DRGG_EINVAL;
+    const TailSplit t = tailsplit_units(tiles, workers);
+    out[0] = t.tiles;
+    out[1] = t.units;
+    out[2] = t.full;
+    out[3] = t.split;
+    return DRGG_OK;
+}
+
 drgg_status drgg_route_split(int32_t E, int64_t M, int64_t N, int64_t K, drgg_dtype out_dtype) {
     drgg_status st = check_problem(E, M, N, K, out_dtype);
     if (st != DRGG_OK) return st;
@@ -566,6 +631,12 @@ drgg_status drgg_set_knob(int knob, int64_t value) {
         case DRGG_KNOB_NONDET:
             g_knob_nondet.store(value != 0);
             return DRGG_OK;
+        case DRGG_KNOB_CHECK_OFFSETS:
+            g_knob_check_offsets.store(value != 0);
+            return DRGG_OK;
+        case DRGG_KNOB_CHECK_WORKSPACE:
+            g_knob_check_ws.store(value != 0);
+            return DRGG_OK;
         default:
             return DRGG_EINVAL;
     }
@@ -590,10 +661,10 @@ const char* drgg_status_string(drgg_status s) {
     switch (s) {
         case DRGG_OK: return "ok";
         case DRGG_EINVAL: return "invalid argument (null pointer, bad enum value or E outside 1..1024)";
-        case DRGG_ESHAPE: return "invalid shape (negative or too large dimension)";
+        case DRGG_ESHAPE: return "invalid shape (negative or too large dimension, or group offsets that fail the debug check)";
         case DRGG_EALIGN: return "misaligned (pointers must be 16-byte aligned, N and K multiples of 8)";
         case DRGG_EOVERFLOW: return "size overflow in 64-bit arithmetic";
-        case DRGG_EWORKSPACE: return "workspace missing or too small";
+        case DRGG_EWORKSPACE: return "workspace missing or too small (or, with the debug check on, not zero for the split program)";
         case DRGG_EUNSUPPORTED: return "unsupported on this device or combination";
         case DRGG_EDEVICE: {
             thread_local char msg[256];

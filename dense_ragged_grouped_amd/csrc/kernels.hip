@@ -7,10 +7,13 @@
 //   weight gradient  dW[e,n,k] = sum_{t of e} G[t,n] X[t,k]
 // with FP32 accumulation on v_mfma_f32_32x32x16_bf16 and one rounding.
 //
-// One workgroup = 4 waves (256 lanes, one per SIMD) computes one BMxBN output
-// tile at a time and walks a list of tiles (persistent); the waves form a 2x2
-// grid, each wave a (BM/2)x(BN/2) block of 32x32 MFMA tiles whose FP32
-// accumulators stay in registers for the whole reduction.
+// One workgroup computes one BMxBN output tile at a time and walks a list of
+// tiles (persistent).  The 256x256 forward, data-gradient and deterministic
+// weight-gradient kernels run 8 waves (two per SIMD) in a 4x2 wave grid, each
+// wave a 64x128 block; every other kernel runs 4 waves (one per SIMD) in a
+// 2x2 grid, each wave a (BM/2)x(BN/2) block.  A wave's block is made of
+// 32x32 MFMA tiles whose FP32 accumulators stay in registers for the whole
+// reduction.
 //
 // Operand staging.  The reduction runs in stages of 32 values through four
 // LDS stage slots per operand, filled straight from HBM by 16-byte buffer

@@ -110,6 +110,23 @@ inline int64_t wgrad_max_partials(int64_t M, int64_t chunk_max) {
     return M <= 0 ? 0 : (2 * M) / chunk_max + 1;
 }
 
+// The tail-split rule of a persistent schedule (flashinfer PR #7516, the
+// #7632 commit body, its tail-split routing test): `tiles` equal output
+// tiles run on `workers` persistent workers in full waves plus a partial
+// last wave of tail = tiles mod workers tiles.  When 2 * tail <= workers the
+// tail tiles are cut in two along the reduction, giving 2 * tail half units
+// next to the `full` whole tiles; otherwise every tile stays whole.
+// Returns (tiles, units, full, split): units = work units handed out,
+// full = tiles that run whole, split = pieces per tail tile (1 or 2).
+struct TailSplit {
+    int64_t tiles, units, full, split;
+};
+inline TailSplit tailsplit_units(int64_t tiles, int64_t workers) {
+    const int64_t tail = workers > 0 ? tiles % workers : 0;
+    if (tail > 0 && 2 * tail <= workers) return {tiles, tiles - tail + 2 * tail, tiles - tail, 2};
+    return {tiles, tiles, tiles, 1};
+}
+
 // Rows per round of the staged epilogue of the forward and data-gradient
 // kernels (kernels.hip): its LDS scratch is that many 128-byte rows per
 // wave.  Tiles below 256x128 share a CU and get the smaller scratch.

@@ -59,10 +59,18 @@
  *     capturable into a HIP graph.
  *   * Argument checks run on the host before anything is enqueued; on any
  *     error nothing is enqueued and the status says why
- *     (drgg_status_string).  Offsets are not checked on the host (they live
- *     on the device); the kernels clamp every offset into [0, M] so that no
- *     access leaves the buffers, and the result for invalid offsets is
- *     unspecified.
+ *     (drgg_status_string).  By default the offsets are not checked on the
+ *     host (they live on the device and the call does not synchronise); the
+ *     kernels clamp every offset into [0, M] so that no access leaves the
+ *     buffers, and the result for invalid offsets is unspecified.  With the
+ *     debug check on (environment DRGG_CHECK_OFFSETS=1, or
+ *     DRGG_KNOB_CHECK_OFFSETS), a grouped call first copies the offsets to
+ *     the host synchronously and returns DRGG_ESHAPE unless o[0] = 0, they
+ *     are non-decreasing and o[E] = M; nothing of the computation is
+ *     enqueued then.  The check cannot be graph-captured (it synchronises),
+ *     which is why it is off by default; this follows the fail-closed
+ *     precedent of flashinfer PR #7516 (#7632 commit body: a program that
+ *     cannot run raises and says why rather than launching).
  *   * Alignment: every pointer 16-byte aligned; N and K multiples of 8.
  *   * Limits: 1 <= E <= 1024, 0 <= M < 2^31, 8 <= N, K <= 2^22, and every
  *     buffer size below 2^62 bytes (checked in 64-bit arithmetic).
@@ -95,10 +103,13 @@ typedef enum {
 typedef enum {
     DRGG_OK = 0,
     DRGG_EINVAL = 1,        /* null pointer, bad enum value, E out of range   */
-    DRGG_ESHAPE = 2,        /* negative or too large dimension                */
+    DRGG_ESHAPE = 2,        /* negative or too large dimension; offsets that
+                               fail the debug check                           */
     DRGG_EALIGN = 3,        /* pointer not 16-byte aligned, N or K not % 8    */
     DRGG_EOVERFLOW = 4,     /* a size product overflows 64-bit arithmetic     */
-    DRGG_EWORKSPACE = 5,    /* workspace missing or smaller than required     */
+    DRGG_EWORKSPACE = 5,    /* workspace missing or smaller than required; a
+                               split-program workspace that is not zero (debug
+                               check)                                         */
     DRGG_EUNSUPPORTED = 6,  /* no program for this device or combination      */
     DRGG_EDEVICE = 7        /* HIP error while querying the device or launching */
 } drgg_status;
@@ -143,7 +154,10 @@ drgg_status grouped_gemm_dgrad(const void *G, const void *W, const int32_t *grou
  *     and tickets that must be zero before the first call
  *     (drgg_workspace_init); every call leaves them zero again.  A buffer
  *     that served a deterministic (or routed) call holds partials afterwards
- *     and must be zeroed again before a split-program call.
+ *     and must be zeroed again before a split-program call; with the debug
+ *     check on (environment DRGG_CHECK_WORKSPACE=1, or
+ *     DRGG_KNOB_CHECK_WORKSPACE) a split-program call copies the workspace to
+ *     the host first and returns DRGG_EWORKSPACE if any byte is set.
  *   Two calls in flight at once must not share a workspace.
  */
 drgg_status grouped_gemm_wgrad(const void *X, const void *G, const int32_t *group_offsets,
@@ -198,9 +212,9 @@ drgg_status batched_gemm_wgrad(const void *X, const void *G, const drgg_batched 
  * value v is split into
  * hi = bf16(v), lo = bf16(v - hi) (round to nearest even) and every product
  * is taken as hi*hi + hi*lo + lo*hi with FP32 accumulation.
- * X [M,K] FP32, Wr [N,K] FP32, out [M,N] FP32.  K must be a multiple of 8
- * and at most 2^22 (DRGG_ESHAPE otherwise), N a multiple of 4
- * (DRGG_EALIGN otherwise).  Deterministic (one fixed order).
+ * X [M,K] FP32, Wr [N,K] FP32, out [M,N] FP32.  K must be a multiple of 8,
+ * N a multiple of 4 (DRGG_EALIGN otherwise), both at most 2^22 and
+ * M < 2^31 (DRGG_ESHAPE otherwise).  Deterministic (one fixed order).
  */
 drgg_status router_gemm_fp32_bf16x3(const float *X, const float *Wr, int64_t M, int64_t N,
                                     int64_t K, float *out, hipStream_t stream);
@@ -209,14 +223,21 @@ drgg_status router_gemm_fp32_bf16x3(const float *X, const float *Wr, int64_t M, 
  * Workspace bytes (written to *bytes, a HOST pointer) that a call with these
  * arguments needs; they do not depend on the CU count (cu_count is accepted
  * for symmetry with drgg_plan and ignored).  0 bytes for fwd; for dgrad the
- * optional W^T buffer.
+ * optional W^T buffer; for wgrad the buffers of the variant's reduction:
+ * the deterministic variant's per-chunk FP32 partials, folded in a fixed
+ * order, or the split program's shared FP32 tile sums and per-tile tickets
+ * (flashinfer PR #8258, Summary: the split tail adds FP32 partial tiles into
+ * a shared sum, and a per-tile ticket picks the last arrival).  The caller
+ * allocates it (the library allocates nothing).
  */
 drgg_status grouped_gemm_workspace_size(drgg_op op, int32_t E, int64_t M, int64_t N, int64_t K,
                                         drgg_dtype out_dtype, int deterministic, int cu_count,
                                         size_t *bytes);
 
-/* Zero a workspace on `stream` (needed once before its first
- * non-deterministic weight-gradient call). */
+/* Zero a workspace on `stream` with a fill kernel (capturable): needed once
+ * before its first split-program weight-gradient call, because the tile
+ * sums and tickets of PR #8258's split tail (Summary) start at zero and the
+ * last arrival on each tile clears them again. */
 drgg_status drgg_workspace_init(void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
@@ -258,10 +279,14 @@ drgg_status drgg_wgrad_chunking(int64_t T, int64_t chunk_max, int64_t *chunk_len
  *   DRGG_KNOB_TIMING      1 = record a HIP event on the stream before every
  *                         kernel launch of a call and after its last launch
  *                         (read back with drgg_timing_read)
+ *   DRGG_KNOB_CHECK_OFFSETS    1 = the synchronous offsets check described
+ *                         above (0 = as the environment says)
+ *   DRGG_KNOB_CHECK_WORKSPACE  1 = the split program's zero-workspace check
+ *                         (0 = as the environment says)
  * None of them changes the arithmetic of the deterministic variant.
  */
 enum { DRGG_KNOB_TILE = 1, DRGG_KNOB_GRID = 2, DRGG_KNOB_REVERSE = 3, DRGG_KNOB_TIMING = 4,
-       DRGG_KNOB_NONDET = 5 };
+       DRGG_KNOB_NONDET = 5, DRGG_KNOB_CHECK_OFFSETS = 6, DRGG_KNOB_CHECK_WORKSPACE = 7 };
 drgg_status drgg_set_knob(int knob, int64_t value);
 
 /*
@@ -302,6 +327,22 @@ int drgg_route_count(void);
 int drgg_timing_count(void);
 drgg_status drgg_timing_read(int i, const char **kernel, float *ms);
 
+/*
+ * The tail-split rule of a persistent schedule (HOST only; flashinfer
+ * PR #7516, #7632 commit body, its tail-split routing test): `tiles` equal
+ * output tiles on `workers` persistent workers run in full waves plus a
+ * partial last wave of tail = tiles mod workers tiles; when
+ * 2 * tail <= workers each tail tile is cut in two along the reduction
+ * (2 * tail half units), otherwise every tile stays whole.  Writes
+ * out[0..3] = (tiles, units handed out, tiles run whole, pieces per tail
+ * tile) to a HOST array of four.  DRGG_EINVAL for a null out, tiles < 0 or
+ * workers < 1.
+ */
+drgg_status drgg_tailsplit_units(int64_t tiles, int64_t workers, int64_t *out);
+
+/* Text of a status code, with the HIP error name and text appended for
+ * DRGG_EDEVICE (the fail-closed precedent of PR #7516, #7632 commit body:
+ * an error names what failed and why). */
 const char *drgg_status_string(drgg_status status);
 int drgg_abi_version(void);
 

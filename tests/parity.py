@@ -14,8 +14,15 @@ Tolerances (written here, used by every parity test):
   the floor for outputs that nearly cancel: FP32 accumulation (which the
   method prescribes) has an error of order 2^-24 sqrt(K_red) q that no
   rounding of the result can undo, so a pure ulp bound cannot hold where
-  |ref| is far below that.  The number of elements that needed the floor is
-  reported.
+  |ref| is far below that.  The elements that needed the floor must be rare.
+  An element needs it when |ref| is within a few hundred times its
+  accumulation error of zero; relative to the spread of the outputs that
+  error grows like sqrt(K_red), and so does the chance.  The bound is
+  1 per million times sqrt(K_red) per element checked, plus 3 (so that a
+  sample of a few thousand elements is not failed by one near-zero output):
+  128 per million at K_red = 16384, where the kernels measured 23-30, and
+  45 per million at K_red = 2048.  The worst error in BF16 ulps of the
+  elements that passed the ulp clause is reported.
 * Integer-valued inputs: every partial sum is exact in FP32, so the GPU must
   equal the oracle bit for bit, in every mode.
 """
@@ -73,8 +80,14 @@ def check_fp32(gpu, ref, kred, amax_a, amax_b, what=""):
         assert np.all(gpu == 0), f"{what}: reference is zero but the GPU result is not"
 
 
+FLOOR_PPM_PER_SQRT_K = 1.0   # elements allowed to need the floor, per million, times sqrt(K_red)
+FLOOR_SLACK = 3              # ... plus this many
+
+
 def check_bf16(gpu_u16, ref, q, kred, what=""):
-    """Returns the number of elements that needed the accumulation floor."""
+    """Returns the number of elements that needed the accumulation floor
+    (bounded by FLOOR_PPM_PER_SQRT_K per million times sqrt(K_red), summed
+    over the elements, + FLOOR_SLACK)."""
     g = bf16_to_f64(np.asarray(gpu_u16).ravel())
     ref = np.asarray(ref, dtype=np.float64).ravel()
     q = np.asarray(q, dtype=np.float64).ravel()
@@ -87,7 +100,17 @@ def check_bf16(gpu_u16, ref, q, kred, what=""):
     bad = ~(ok_ulp | ok_floor)
     assert not np.any(bad), (f"{what}: {bad.sum()} of {bad.size} BF16 elements out of tolerance; "
                              f"first at {np.flatnonzero(bad)[:5]}: gpu {g[bad][:5]} ref {ref[bad][:5]}")
-    return int(np.sum(~ok_ulp))
+    n_floor = int(np.sum(~ok_ulp))
+    limit = FLOOR_PPM_PER_SQRT_K * 1e-6 * float(np.sum(np.sqrt(kred))) + FLOOR_SLACK
+    assert n_floor <= limit, (f"{what}: {n_floor} of {g.size} elements needed the FP32-accumulation floor "
+                              f"(limit {limit:.1f})")
+    if g.size:
+        worst = float(np.max(np.where(ok_ulp, np.abs(g - r16) / ulp, 0.0)))
+        check_bf16.last_worst_ulp = worst
+    return n_floor
+
+
+check_bf16.last_worst_ulp = 0.0
 
 
 def expert_of_rows(offs, M):
@@ -169,6 +192,48 @@ def sample_indices(prob, program, n_random=3000, seed=0):
         return np.zeros(0, dtype=np.int64)
     rand = rng.integers(0, size, n_random)
     return np.unique(np.concatenate([struct, rand]).astype(np.int64))
+
+
+def tile_indices(prob, program, tile=256, seed=0):
+    """Flat output indices of four whole tile x tile output blocks (every
+    element of each, clipped to the output): the first block, the last one,
+    one that straddles an expert boundary (forward and data gradient: rows
+    across the start of the second non-empty expert; weight gradient: a block
+    of the expert with the most tokens) and a random one."""
+    rng = np.random.default_rng(seed + 17)
+    offs = prob.offs.astype(np.int64)
+    E, M, N, K = prob.E, prob.M, prob.N, prob.K
+    blocks = []   # (expert or -1, row0, col0)
+    if program in ("fwd", "dgrad"):
+        cols = N if program == "fwd" else K
+        rows = M
+        nonempty = [e for e in range(E) if offs[e + 1] > offs[e]]
+        boundary = offs[nonempty[1]] - tile // 2 if len(nonempty) > 1 else rows // 2
+        starts = [(0, 0), (max(rows - tile, 0), max(cols - tile, 0)),
+                  (min(max(boundary, 0), max(rows - tile, 0)), int(rng.integers(0, max(cols - tile, 0) + 1))),
+                  (int(rng.integers(0, max(rows - tile, 0) + 1)), int(rng.integers(0, max(cols - tile, 0) + 1)))]
+        idx = []
+        for r0, c0 in starts:
+            r = np.arange(r0, min(r0 + tile, rows))
+            c = np.arange(c0, min(c0 + tile, cols))
+            idx.append((r[:, None] * cols + c[None, :]).ravel())
+        return np.unique(np.concatenate(idx)).astype(np.int64)
+    counts = offs[1:] - offs[:-1]
+    nonempty = np.flatnonzero(counts > 0)
+    if nonempty.size == 0:
+        return np.zeros(0, dtype=np.int64)
+    big = int(np.argmax(counts))
+    re = int(rng.choice(nonempty))
+    starts = [(int(nonempty[0]), 0, 0),
+              (int(nonempty[-1]), max(N - tile, 0), max(K - tile, 0)),
+              (big, int(rng.integers(0, max(N - tile, 0) + 1)), int(rng.integers(0, max(K - tile, 0) + 1))),
+              (re, int(rng.integers(0, max(N - tile, 0) + 1)), int(rng.integers(0, max(K - tile, 0) + 1)))]
+    idx = []
+    for e, r0, c0 in starts:
+        r = np.arange(r0, min(r0 + tile, N))
+        c = np.arange(c0, min(c0 + tile, K))
+        idx.append((e * N * K + r[:, None] * K + c[None, :]).ravel())
+    return np.unique(np.concatenate(idx)).astype(np.int64)
 
 
 def oracle_program(prob, program, idx=None):

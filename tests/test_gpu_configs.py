@@ -2,10 +2,12 @@
 configuration the benchmark times.
 
 Every output element at these sizes would take the CPU oracle minutes, so
-each program is checked on sampled elements the oracle computes one by one
-(random elements plus every expert's and every 256-row tile's first and last
-row, the last column, every expert's output corners), at the tolerances of
-tests/parity.py.  Integer-valued inputs of the same shapes are compared bit
+each program is checked on the elements the oracle computes one by one:
+every element of four whole 256x256 output blocks (the first, the last, one
+across an expert boundary -- for the weight gradient one of the longest
+expert -- and a random one) plus scattered samples (random elements, every
+expert's and every 256-row tile's first and last row, the last column, every
+expert's output corners), at the tolerances of tests/parity.py.  Integer-valued inputs of the same shapes are compared bit
 for bit on the same samples, empty experts are checked in full, and the
 deterministic variant is re-run and compared bit for bit.
 """
@@ -38,9 +40,11 @@ def bits(t):
 
 
 def sampled_check(prob, program, out, out_bf16, integer=False, what=""):
-    idx = parity.sample_indices(prob, program)
+    idx = np.union1d(parity.sample_indices(prob, program), parity.tile_indices(prob, program))
     n = parity.compare(prob, program, parity.from_dev(out), out_bf16, idx=idx, integer=integer, what=what)
-    print(f"{what}: {idx.size} sampled elements ok; {n} needed the FP32-accumulation floor", flush=True)
+    worst = f"; worst {parity.check_bf16.last_worst_ulp:.2f} ulp" if out_bf16 and not integer else ""
+    print(f"{what}: {idx.size} elements (4 whole tiles + samples) ok; {n} needed the FP32-accumulation "
+          f"floor{worst}", flush=True)
 
 
 def empty_experts_zero(prob, out):
@@ -146,11 +150,18 @@ def test_router_full_size(drgg):
     out = drgg.router_gemm_fp32_bf16x3(parity.to_dev(X), parity.to_dev(Wr))
     o = parity.from_dev(out).ravel().astype(np.float64)
     rng = np.random.default_rng(0)
-    idx = np.unique(np.concatenate([rng.integers(0, o.size, 4000), [0, o.size - 1]]))
+    M, N = out.shape
+    # every element of three whole 128 x 128 output tiles (first, last, one
+    # random) plus scattered samples
+    blocks = []
+    for r0, c0 in ((0, 0), (M - 128, N - 128), (int(rng.integers(0, M // 128)) * 128, 128)):
+        r = np.arange(r0, r0 + 128)
+        c = np.arange(c0, c0 + 128)
+        blocks.append((r[:, None] * N + c[None, :]).ravel())
+    idx = np.unique(np.concatenate([rng.integers(0, o.size, 4000), [0, o.size - 1], *blocks]))
     emul = oracle.router_bf16x3(X, Wr, idx)
     exact = oracle.router_exact(X, Wr, idx)
     assert np.linalg.norm(o[idx] - emul) <= 1e-6 * np.linalg.norm(emul)
-    M, N = out.shape
     ax = np.abs(X).max(axis=1)[idx // N]
     aw = np.abs(Wr).max(axis=1)[idx % N]
     parity.check_fp32(o[idx], exact, np.full(idx.size, X.shape[1]), ax, aw, what="router full size")

@@ -1,15 +1,18 @@
 """GPU tests of the variants' contracts and of the boundary's behaviour.
 
 * deterministic variant: bitwise identical over 20 runs, across output tile
-  shapes, across the order the work items are walked in, and on a stream
-  restricted to a subset of the CUs (fewer CUs, same bits);
+  shapes, across the order the work items are walked in, on streams
+  restricted to 16, 64 and 128 of the CUs (fewer CUs, same bits), and next to
+  a kernel that holds 8, 16 or 32 CUs;
 * non-deterministic variant: the tile sums and tickets are zero again after
   every call; every stream-K partition (grid sizes from 1 to more workgroups
   than units) matches the oracle;
 * the router's BF16x3 split against both oracles;
 * edge cases: no tokens, one token per expert, 1024 experts, the smallest N
   and K, all tokens on one expert;
-* error paths: misaligned pointers, a short workspace, bad dtypes.
+* error paths: misaligned pointers, a short workspace, bad dtypes; the
+  debug checks of the group offsets and of the split program's workspace;
+* a split-program call on a stream other than the current one.
 """
 import ctypes
 
@@ -115,39 +118,82 @@ def test_deterministic_across_grid_sizes(drgg, program):
 
 
 def _hip():
+    # torch's own HIP runtime: torch loads it under this name, so the dynamic
+    # loader returns the copy already in the process
     return ctypes.CDLL("libamdhip64.so")
 
 
-def test_deterministic_on_fewer_cus(drgg):
-    """Run on a stream whose CU mask enables a quarter of the CUs: the
-    deterministic results must equal those on the full device."""
-    hip = _hip()
-    props = torch.cuda.get_device_properties(0)
-    ncu = props.multi_processor_count
+def _cu_mask_stream(hip, n):
+    """A stream restricted to the CUs of the first n bits of the CU mask.  The
+    mask's bits go round the XCDs (bit i on XCD i mod 8), so the first n bits
+    leave n/8 CUs on every XCD; a mask that leaves an XCD without CUs is
+    refused (the runtime returns hipErrorOutOfMemory for it)."""
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
     words = (ncu + 31) // 32
     mask = (ctypes.c_uint32 * words)()
-    for cu in range(0, ncu, 4):
+    for cu in range(n):
         mask[cu // 32] |= 1 << (cu % 32)
     stream = ctypes.c_void_p()
     hip.hipExtStreamCreateWithCUMask.restype = ctypes.c_int
     rc = hip.hipExtStreamCreateWithCUMask(ctypes.byref(stream), ctypes.c_uint32(words), mask)
     if rc != 0:
         hip.hipGetLastError()      # clear the error so that later calls do not report it
-        pytest.skip(f"hipExtStreamCreateWithCUMask returned {rc}: CU masks unavailable here")
+        return None, rc
+    return stream, 0
+
+
+FEWER_CU_CASES = [DET_CASE, (306, 3, 4000, 264, 520, (1,))]
+
+
+@pytest.mark.parametrize("n_cus", [16, 64, 128])
+def test_deterministic_on_fewer_cus(drgg, n_cus):
+    """Run on a stream whose CU mask enables n_cus of the CUs, with the
+    default persistent grid (sized for the whole device, so workgroups queue
+    for the CUs left) and with a grid of n_cus workgroups: the deterministic
+    results must equal those on the full device."""
+    hip = _hip()
+    stream, rc = _cu_mask_stream(hip, n_cus)
+    if stream is None:
+        pytest.skip(f"hipExtStreamCreateWithCUMask({n_cus} CUs) returned {rc}: CU masks unavailable here")
     try:
         ext = torch.cuda.ExternalStream(stream.value)
-        prob = ragged_problem(*DET_CASE)
+        for case in FEWER_CU_CASES:
+            prob = ragged_problem(*case)
+            dv = dev_inputs(prob)
+            for program in ("fwd", "dgrad", "wgrad"):
+                print(f"fewer CUs: {n_cus} CUs, case {case[0]}, {program}", flush=True)
+                ref = bits(run_program(drgg, program, dv, torch.bfloat16, True))
+                torch.cuda.synchronize()
+                for grid in (0, n_cus):
+                    drgg.set_knob(drgg.KNOB_GRID, grid)
+                    try:
+                        with torch.cuda.stream(ext):
+                            out = run_program(drgg, program, dv, torch.bfloat16, True)
+                        ext.synchronize()
+                    finally:
+                        drgg.set_knob(drgg.KNOB_GRID, 0)
+                    assert np.array_equal(bits(out), ref), f"{program}: {n_cus} CUs (grid {grid}) changed the bits"
+    finally:
+        torch.cuda.synchronize()
+        hip.hipStreamDestroy(stream)
+
+
+@pytest.mark.parametrize("held", [8, 16, 32])
+def test_deterministic_next_to_cu_holder(drgg, held):
+    """A kernel on another stream holds `held` CUs while the programs run
+    (their persistent workgroups then share the device unevenly): the
+    deterministic results must not change."""
+    other = torch.cuda.Stream()
+    for case in FEWER_CU_CASES:
+        prob = ragged_problem(*case)
         dv = dev_inputs(prob)
         for program in ("fwd", "dgrad", "wgrad"):
             ref = bits(run_program(drgg, program, dv, torch.bfloat16, True))
             torch.cuda.synchronize()
-            with torch.cuda.stream(ext):
-                out = run_program(drgg, program, dv, torch.bfloat16, True)
-            ext.synchronize()
-            assert np.array_equal(bits(out), ref), f"{program}: CU mask changed the bits"
-    finally:
-        torch.cuda.synchronize()
-        hip.hipStreamDestroy(stream)
+            drgg.hold_cus(held, 3000, stream=other)
+            out = run_program(drgg, program, dv, torch.bfloat16, True)
+            torch.cuda.synchronize()
+            assert np.array_equal(bits(out), ref), f"{program}: holding {held} CUs changed the bits"
 
 
 def _nondet_ws(drgg, prob, out_code):
@@ -279,6 +325,95 @@ def test_one_hot_routing_equals_dense_call(drgg, det):
 
 
 # ---- errors ------------------------------------------------------------------
+
+def _raw_call(drgg, program, dv, prob, out, ws=None, det=1, code=None):
+    """A call straight through the C ABI (no Python-side checks)."""
+    code = drgg.FP32 if code is None else code
+    ws_ptr = ws.data_ptr() if ws is not None else None
+    ws_bytes = ws.numel() if ws is not None else 0
+    s = torch.cuda.current_stream().cuda_stream
+    f = {"fwd": drgg.lib.grouped_gemm_fwd, "dgrad": drgg.lib.grouped_gemm_dgrad,
+         "wgrad": drgg.lib.grouped_gemm_wgrad}[program]
+    a, b = {"fwd": ("X", "W"), "dgrad": ("G", "W"), "wgrad": ("X", "G")}[program]
+    return f(dv[a].data_ptr(), dv[b].data_ptr(), dv["offs"].data_ptr(), prob.E, prob.M, prob.N, prob.K, code,
+             det, out.data_ptr(), ws_ptr, ws_bytes, s)
+
+
+def test_offsets_debug_check(drgg):
+    """With the offsets check on, offsets that do not start at 0, decrease or
+    do not end at M are refused with DRGG_ESHAPE and nothing is written;
+    valid offsets still run."""
+    prob = ragged_problem(332, 4, 900, 64, 72, (2,))
+    dv = dev_inputs(prob)
+    good = prob.offs.copy()
+    bad_sets = []
+    b = good.copy(); b[0] = 5; bad_sets.append(b)                      # o[0] != 0
+    b = good.copy(); b[2] = b[1] - 1; bad_sets.append(b)               # decreasing
+    b = good.copy(); b[-1] = prob.M - 8; bad_sets.append(b)            # o[E] != M
+    shapes = {"fwd": (prob.M, prob.N), "dgrad": (prob.M, prob.K), "wgrad": (prob.E, prob.N, prob.K)}
+    ws = torch.zeros(drgg.workspace_size(drgg.OP_WGRAD, prob.E, prob.M, prob.N, prob.K, drgg.FP32, True),
+                     dtype=torch.uint8, device="cuda")
+    drgg.set_knob(drgg.KNOB_CHECK_OFFSETS, 1)
+    try:
+        for program in ("fwd", "dgrad", "wgrad"):
+            for bad in bad_sets:
+                d = dict(dv, offs=parity.to_dev(bad))
+                out = torch.full(shapes[program], 7.0, dtype=torch.float32, device="cuda")
+                st = _raw_call(drgg, program, d, prob, out, ws)
+                torch.cuda.synchronize()
+                assert st == 2, f"{program}: bad offsets {bad.tolist()} gave status {st}"
+                assert bool(torch.all(out == 7.0)), f"{program}: a refused call wrote its output"
+            out = torch.empty(shapes[program], dtype=torch.float32, device="cuda")
+            assert _raw_call(drgg, program, dv, prob, out, ws) == 0
+            torch.cuda.synchronize()
+            parity.compare(prob, program, parity.from_dev(out), False, what=f"checked offsets {program}")
+    finally:
+        drgg.set_knob(drgg.KNOB_CHECK_OFFSETS, 0)
+
+
+def test_split_workspace_debug_check(drgg):
+    """With the workspace check on, a split-program call whose workspace
+    still holds a deterministic call's partials is refused with
+    DRGG_EWORKSPACE; after drgg_workspace_init it runs and leaves the
+    workspace zero."""
+    prob = ragged_problem(333, 3, 3000, 256, 264, ())
+    dv = dev_inputs(prob)
+    n_det = drgg.workspace_size(drgg.OP_WGRAD, prob.E, prob.M, prob.N, prob.K, drgg.FP32, True)
+    n_split = drgg.workspace_size(drgg.OP_WGRAD, prob.E, prob.M, prob.N, prob.K, drgg.FP32, False)
+    ws = torch.zeros(max(n_det, n_split), dtype=torch.uint8, device="cuda")
+    out = torch.empty((prob.E, prob.N, prob.K), dtype=torch.float32, device="cuda")
+    assert _raw_call(drgg, "wgrad", dv, prob, out, ws, det=1) == 0     # leaves partials behind
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(ws[:n_split])) > 0
+    drgg.set_knob(drgg.KNOB_CHECK_WORKSPACE, 1)
+    try:
+        out.fill_(7.0)
+        assert _raw_call(drgg, "wgrad", dv, prob, out, ws, det=0) == 5
+        torch.cuda.synchronize()
+        assert bool(torch.all(out == 7.0))
+        drgg.workspace_init(ws)
+        assert _raw_call(drgg, "wgrad", dv, prob, out, ws, det=0) == 0
+        torch.cuda.synchronize()
+        assert int(torch.count_nonzero(ws)) == 0
+        parity.compare(prob, "wgrad", parity.from_dev(out), False, what="split after workspace check")
+    finally:
+        drgg.set_knob(drgg.KNOB_CHECK_WORKSPACE, 0)
+
+
+def test_split_program_on_another_stream(drgg):
+    """The split program with the default workspace on a stream that is not
+    the current one: the workspace is allocated and zeroed on that stream and
+    the result matches the oracle, twice in a row (the second call reuses the
+    buffer, which the first left zero)."""
+    prob = ragged_problem(334, 4, 3000, 264, 392, (1,))
+    dv = dev_inputs(prob)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    for _ in range(2):
+        out = drgg.grouped_gemm_wgrad(dv["X"], dv["G"], dv["offs"], out_dtype=torch.float32, deterministic=False,
+                                      stream=side)
+        side.synchronize()
+        parity.compare(prob, "wgrad", parity.from_dev(out), False, what="split program on a side stream")
 
 def test_error_paths(drgg):
     prob = ragged_problem(331, 2, 100, 64, 64, ())

@@ -109,13 +109,34 @@ def test_integer_inputs_bitwise(drgg, program, det, tile):
         drgg.set_knob(drgg.KNOB_TILE, 0)
 
 
-def test_wgrad_det_multi_chunk_case_is_split(drgg):
-    """The medium weight-gradient cases above really exercise the chunked
-    (partials + ordered fold) path."""
-    plan = drgg.plan(drgg.OP_WGRAD, 3, 1000, 520, 392, drgg.FP32, True)
-    counts = synth.ragged_counts(101, 1000, 3, (1,))
-    chunks = [drgg.wgrad_chunking(int(t), plan["chunk_max"])[1] for t in counts]
-    assert max(chunks) > 1 or plan["chunk_max"] >= 1000
+SPLIT_CASE = (106, 3, 4000, 264, 520, (1,))   # two experts of about 2000 tokens: cut into chunks
+MEDIUM_SPLIT = [SPLIT_CASE, (107, 1, 9000, 64, 392, ())]
+
+
+def test_wgrad_det_split_cases_are_split(drgg):
+    """The cases below really exercise the chunked (partials + ordered fold)
+    path: some expert is cut into more than one chunk."""
+    for seed, E, M, N, K, empty in MEDIUM_SPLIT:
+        plan = drgg.plan(drgg.OP_WGRAD, E, M, N, K, drgg.FP32, True)
+        counts = synth.ragged_counts(seed, M, E, empty)
+        chunks = [drgg.wgrad_chunking(int(t), plan["chunk_max"])[1] for t in counts]
+        assert max(chunks) > 1, (seed, plan["chunk_max"], counts.tolist(), chunks)
+
+
+@pytest.mark.parametrize("out_bf16", [False, True])
+@pytest.mark.parametrize("det", [True, False])
+@pytest.mark.parametrize("case", MEDIUM_SPLIT, ids=lambda c: f"s{c[0]}_E{c[1]}_M{c[2]}_N{c[3]}_K{c[4]}")
+def test_medium_split_wgrad(drgg, case, det, out_bf16):
+    """Every element of weight gradients whose experts are cut into several
+    chunks (deterministic: partials and ordered fold; split program: atomic
+    tile sums and tickets)."""
+    seed, E, M, N, K, empty = case
+    prob = ragged_problem(seed, E, M, N, K, empty)
+    print(f"medium split {case} det={det} bf16={out_bf16}", flush=True)
+    dv = dev_inputs(prob)
+    out = run_program(drgg, "wgrad", dv, torch.bfloat16 if out_bf16 else torch.float32, det)
+    torch.cuda.synchronize()
+    parity.compare(prob, "wgrad", parity.from_dev(out), out_bf16, what=f"split {case}")
 
 
 @pytest.mark.parametrize("shape", [(302, 3, 1000, 264, 520, (1,)), (303, 8, 4096, 1536, 2048, ()),

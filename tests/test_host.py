@@ -139,13 +139,51 @@ def test_router_argument_checks(drgg):
     assert r(A16, A16, 16, 16, 16, A16 + 4, None) == 3
     assert r(A16, A16, 16, 10, 16, A16, None) == 3          # N must be a multiple of 4
     assert r(A16, A16, 16, 16, 2 ** 22 + 8, A16, None) == 2
-    assert r(A16, A16, 2 ** 31 - 1, 16, 2 ** 31 - 8, A16, None) == 4
+    assert r(A16, A16, 16, 2 ** 22 + 4, 16, A16, None) == 2   # output offsets stay below 2^31
+    assert r(A16, A16, 2 ** 31, 16, 16, A16, None) == 2
+    assert r(A16, A16, 2 ** 31 - 1, 16, 2 ** 31 - 8, A16, None) == 2
 
 
 def test_knob_checks(drgg):
     assert drgg.lib.drgg_set_knob(99, 1) == 1
     assert drgg.lib.drgg_set_knob(drgg.KNOB_TILE, 42) == 1
     assert drgg.lib.drgg_set_knob(drgg.KNOB_TILE, 0) == 0
+    for knob in (drgg.KNOB_CHECK_OFFSETS, drgg.KNOB_CHECK_WORKSPACE):
+        assert drgg.lib.drgg_set_knob(knob, 1) == 0
+        assert drgg.lib.drgg_set_knob(knob, 0) == 0
+
+
+# ---- the tail-split rule ---------------------------------------------------------
+
+def test_tailsplit_units_pages_tuples(drgg):
+    """flashinfer PR #7516, #7632 commit body: the row M 6889, N 12288 has
+    27 x 48 = 1296 tiles of 256 x 256 on SM pairs; on 148 SMs (74 pairs) the
+    38-tile tail does not fit as 76 half units, so every tile stays whole; on
+    152 SMs (76 pairs) the 4-tile tail becomes 8 half units."""
+    def units(m, n, sm_count):
+        return drgg.tailsplit_units(-(-m // 256) * -(-n // 256), sm_count // 2)
+    assert units(6889, 12288, 148) == (1296, 1296, 1296, 1)
+    assert units(6889, 12288, 152) == (1296, 1300, 1292, 2)
+
+
+def test_tailsplit_units_closed_form(drgg):
+    rng = np.random.default_rng(3)
+    for _ in range(500):
+        tiles, workers = int(rng.integers(0, 5000)), int(rng.integers(1, 600))
+        t, units, full, split = drgg.tailsplit_units(tiles, workers)
+        tail = tiles % workers
+        assert t == tiles
+        if tail and 2 * tail <= workers:
+            # the full waves whole, the tail in halves: one more wave of units
+            assert (units, full, split) == (tiles + tail, tiles - tail, 2)
+            assert (units - full) <= workers
+        else:
+            assert (units, full, split) == (tiles, tiles, 1)
+    assert drgg.tailsplit_units(256, 256) == (256, 256, 256, 1)      # no tail
+    assert drgg.tailsplit_units(384, 256) == (384, 512, 256, 2)      # gate_up: 128 tail tiles in halves
+    assert drgg.tailsplit_units(0, 256) == (0, 0, 0, 1)
+    with pytest.raises(drgg.DrggError):
+        drgg.tailsplit_units(10, 0)
 
 
 # ---- planner -------------------------------------------------------------------
