@@ -35,7 +35,7 @@ EXPORTS = (
     "batched_gemm_fwd", "batched_gemm_dgrad", "batched_gemm_wgrad",
     "drgg_route_split", "drgg_route_clear", "drgg_route_count", "drgg_hold_cus",
     "grouped_gemm_workspace_size", "drgg_workspace_init", "drgg_plan", "drgg_wgrad_chunking",
-    "drgg_tailsplit_units",
+    "drgg_tailsplit_units", "grouped_gemm_wgrad_noalloc",
     "drgg_set_knob", "drgg_timing_count", "drgg_timing_read", "drgg_status_string", "drgg_abi_version",
 )
 
@@ -90,6 +90,8 @@ def _load(path=LIB_PATH):
     for name in ("grouped_gemm_fwd", "grouped_gemm_dgrad", "grouped_gemm_wgrad"):
         getattr(lib, name).argtypes = gemm
         getattr(lib, name).restype = c_int
+    lib.grouped_gemm_wgrad_noalloc.argtypes = [vp, vp, vp, i32, i64, i64, i64, c_int, c_int, vp, vp]
+    lib.grouped_gemm_wgrad_noalloc.restype = c_int
     pb = ctypes.POINTER(Batched)
     lib.batched_gemm_fwd.argtypes = [vp, vp, pb, c_int, vp, vp]
     lib.batched_gemm_dgrad.argtypes = [vp, vp, pb, c_int, vp, vp, sz, vp]
@@ -457,6 +459,31 @@ def grouped_gemm_wgrad(X, G, group_offsets, out_dtype=None, deterministic=True, 
                                     int(bool(deterministic)), out.data_ptr(), ws_ptr, ws_bytes,
                                     _stream(X.device, stream))
     _check(st, "grouped_gemm_wgrad")
+    return out
+
+
+def grouped_gemm_wgrad_noalloc(X, G, group_offsets, out, deterministic=True, stream=None):
+    """grouped_gemm_wgrad into a caller-given `out` [E, N, K] (BF16 or FP32)
+    with the library's fixed per-device workspace: the call allocates
+    nothing (for code that must not, e.g. under graph capture).  Problems
+    whose workspace exceeds that array (64 MiB) are refused; calls that
+    overlap on one device race on it."""
+    torch = _torch()
+    _need(X, torch.bfloat16, "X", 2)
+    _need(G, torch.bfloat16, "G", 2)
+    E = _offsets(group_offsets)
+    M, K = X.shape
+    Mg, N = G.shape
+    if Mg != M:
+        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, G {tuple(G.shape)}")
+    code = _dtype_code(out.dtype)
+    _need(out, _torch_dtype(code), "out", 3)
+    if tuple(out.shape) != (E, N, K):
+        raise ValueError("out has the wrong shape")
+    with _on_one_device(stream, X, G, group_offsets, out):
+        st = lib.grouped_gemm_wgrad_noalloc(X.data_ptr(), G.data_ptr(), group_offsets.data_ptr(), E, M, N, K, code,
+                                            int(bool(deterministic)), out.data_ptr(), _stream(X.device, stream))
+    _check(st, "grouped_gemm_wgrad_noalloc")
     return out
 
 

@@ -332,9 +332,12 @@ drgg_status run_fwd_dgrad(drgg_op op, const void* A, const void* W, const int32_
     return launch_status(launch_fwd_dgrad((int)op, p.tile, a, dt == DRGG_BF16, s));
 }
 
+// validate_only: run the argument checks (and the offsets debug check) and
+// stop before the first launch; the split program's workspace check is left
+// to the call that follows.
 drgg_status run_wgrad(const void* X, const void* G, const int32_t* group_offsets, int32_t E, int64_t M, int64_t N,
                       int64_t K, drgg_dtype out_dtype, int deterministic, void* dW, void* workspace,
-                      size_t workspace_bytes, hipStream_t stream, const Layout& L) {
+                      size_t workspace_bytes, hipStream_t stream, const Layout& L, bool validate_only = false) {
     drgg_status st = check_problem(E, M, N, K, out_dtype);
     if (st != DRGG_OK) return st;
     if (!dW || (M > 0 && (!X || !G))) return DRGG_EINVAL;
@@ -364,10 +367,11 @@ drgg_status run_wgrad(const void* X, const void* G, const int32_t* group_offsets
         st = check_offsets_sync(group_offsets, E, M, stream);
         if (st != DRGG_OK) return st;
     }
-    if (!p.det && p.ws_bytes > 0 && checks_workspace()) {
+    if (!p.det && p.ws_bytes > 0 && checks_workspace() && !validate_only) {
         st = check_workspace_zero(workspace, p.ws_bytes, stream);
         if (st != DRGG_OK) return st;
     }
+    if (validate_only) return DRGG_OK;
     GemmArgs a{};
     a.A = static_cast<const uint16_t*>(G);   // A rows: output rows n of dW (from G)
     a.B = static_cast<const uint16_t*>(X);   // B rows: output cols k of dW (from X)
@@ -466,6 +470,37 @@ drgg_status grouped_gemm_wgrad(const void* X, const void* G, const int32_t* grou
                                void* dW, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (!group_offsets) return DRGG_EINVAL;
     return run_wgrad(X, G, group_offsets, E, M, N, K, out_dtype, deterministic, dW, workspace, workspace_bytes,
+                     stream, grouped_layout(DRGG_OP_WGRAD, N, K));
+}
+
+drgg_status grouped_gemm_wgrad_noalloc(const void* X, const void* G, const int32_t* group_offsets, int32_t E,
+                                       int64_t M, int64_t N, int64_t K, drgg_dtype out_dtype, int deterministic,
+                                       void* dW, hipStream_t stream) {
+    if (!group_offsets) return DRGG_EINVAL;
+    drgg_status st = check_problem(E, M, N, K, out_dtype);
+    if (st != DRGG_OK) return st;
+    Plan p;   // the workspace size does not depend on the CU count
+    st = make_plan(DRGG_OP_WGRAD, E, M, N, K, deterministic, 1, &p, out_dtype);
+    if (st != DRGG_OK) return st;
+    if (p.ws_bytes > kScratchBytes) return DRGG_EWORKSPACE;
+    void* ws = nullptr;
+    if (p.ws_bytes > 0) {
+        hipError_t e = scratch_buffer(&ws);
+        if (e != hipSuccess) return device_error(e);
+    }
+    // The split program needs zero tile sums and tickets; the array may
+    // hold a deterministic call's partials, so clear that much first (a fill
+    // kernel on the stream: capturable, allocates nothing).  The plain
+    // argument checks of run_wgrad come first, so nothing is enqueued for a
+    // call they refuse.
+    if (!p.det && p.ws_bytes > 0) {
+        st = run_wgrad(X, G, group_offsets, E, M, N, K, out_dtype, deterministic, dW, ws, kScratchBytes, stream,
+                       grouped_layout(DRGG_OP_WGRAD, N, K), /*validate_only=*/true);
+        if (st != DRGG_OK) return st;
+        hipError_t e = launch_zero(ws, p.ws_bytes, stream);
+        if (e != hipSuccess) return device_error(e);
+    }
+    return run_wgrad(X, G, group_offsets, E, M, N, K, out_dtype, deterministic, dW, ws, ws ? kScratchBytes : 0,
                      stream, grouped_layout(DRGG_OP_WGRAD, N, K));
 }
 

@@ -42,6 +42,11 @@ hipError_t launch_wgrad_atomic(int tile, const GemmArgs& a, int64_t grid_n, bool
 hipError_t launch_router(const float* X, const float* Wr, float* out, int64_t M, int64_t N, int64_t K,
                          hipStream_t s);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
+
+// The fixed device workspace of grouped_gemm_wgrad_noalloc: its size, and the
+// device address of the current device's copy (looked up once per device).
+constexpr size_t kScratchBytes = size_t(64) << 20;
+hipError_t scratch_buffer(void** ptr);
 hipError_t launch_hold_cus(int n, uint64_t ticks, hipStream_t s);
 
 // Per-launch timing marks (a measurement knob, off by default): when on, an

@@ -34,6 +34,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -1880,6 +1881,35 @@ __global__ void zero_kernel(uint8_t* p, size_t bytes) {
             for (size_t j = i; j < i + 16 && j < bytes; ++j) p[j] = 0;
         }
     }
+}
+
+// Workspace of the entry point that allocates nothing
+// (grouped_gemm_wgrad_noalloc): a fixed array in device memory, one copy per
+// device that runs the library's kernels, held until the process ends.  In
+// host code `scratch` names a host-side stand-in, not the device array, so
+// it is never passed to a kernel: scratch_buffer looks up the device address
+// of the current device's copy once (hipGetSymbolAddress, with that device
+// current) and every later use goes through that address.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+hipError_t scratch_buffer(void** ptr) {
+    constexpr int kDevices = 64;
+    static std::mutex mu;
+    static void* addr[kDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {

@@ -166,6 +166,28 @@ drgg_status grouped_gemm_wgrad(const void *X, const void *G, const int32_t *grou
                                void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * The weight gradient for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): grouped_gemm_wgrad with the same arguments minus the
+ * workspace, which comes from a fixed array in device memory that the
+ * library holds per device (64 MiB, allocated when the library's kernels are
+ * loaded on that device and held until the process ends).  Same programs,
+ * same results: the deterministic variant is bitwise that of
+ * grouped_gemm_wgrad.  A problem whose workspace
+ * (grouped_gemm_workspace_size) exceeds 64 MiB gets DRGG_EWORKSPACE with
+ * nothing enqueued.  The call allocates nothing: before a split-program call
+ * it clears the part of the array the tile sums and tickets use with a fill
+ * kernel on `stream`.  Every call on one device shares that device's array,
+ * and it keeps the last call's contents: calls that overlap on one device
+ * (on different streams, or from different threads) race on it and must be
+ * serialised by the caller.
+ */
+drgg_status grouped_gemm_wgrad_noalloc(const void *X, const void *G, const int32_t *group_offsets,
+                                       int32_t E, int64_t M, int64_t N, int64_t K,
+                                       drgg_dtype out_dtype, int deterministic, void *dW,
+                                       hipStream_t stream);
+
+/*
  * Batched projection GEMM: the projection family also covers batched
  * products (PR #8363, Summary; its #8438 commit body names batched "MLA head
  * rows"), read here as B independent products of one shape -- batch b has

@@ -27,6 +27,7 @@ hipError_t launch_router(const float*, const float*, float*, int64_t, int64_t, i
 }
 hipError_t launch_zero(void*, size_t, hipStream_t) { no_gpu("zero"); }
 hipError_t launch_hold_cus(int, uint64_t, hipStream_t) { no_gpu("hold"); }
+hipError_t scratch_buffer(void**) { no_gpu("scratch"); }
 }  // namespace drgg
 
 static int fails = 0;
@@ -58,6 +59,10 @@ int main() {
     EXPECT(grouped_gemm_wgrad(A, A, O, 2, 100000, 256, 256, DRGG_FP32, 1, A, nullptr, 0, nullptr), DRGG_EWORKSPACE);
     EXPECT(grouped_gemm_wgrad(A, A, nullptr, 2, 64, 64, 64, DRGG_FP32, 1, A, A, 1 << 20, nullptr), DRGG_EINVAL);
     EXPECT(grouped_gemm_wgrad(A, A, O, 2, 64, 64, 64, (drgg_dtype)5, 1, A, A, 1 << 20, nullptr), DRGG_EINVAL);
+    // the no-allocation weight gradient: refused on the host
+    EXPECT(grouped_gemm_wgrad_noalloc(A, A, nullptr, 2, 64, 64, 64, DRGG_FP32, 1, A, nullptr), DRGG_EINVAL);
+    EXPECT(grouped_gemm_wgrad_noalloc(A, A, O, 8, 131072, 1536, 2048, DRGG_BF16, 1, A, nullptr), DRGG_EWORKSPACE);
+    EXPECT(grouped_gemm_wgrad_noalloc(A, A, O, 2, 64, 12, 64, DRGG_FP32, 1, A, nullptr), DRGG_EALIGN);
     // batched
     drgg_batched b{4, 64, 64, 64, 64, 64 * 64, 64, 64 * 64, 64, 64 * 64};
     drgg_batched bad = b;
