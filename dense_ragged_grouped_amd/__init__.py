@@ -35,7 +35,7 @@ EXPORTS = (
     "batched_gemm_fwd", "batched_gemm_dgrad", "batched_gemm_wgrad",
     "drgg_route_split", "drgg_route_clear", "drgg_route_count", "drgg_hold_cus",
     "grouped_gemm_workspace_size", "drgg_workspace_init", "drgg_plan", "drgg_wgrad_chunking",
-    "drgg_tailsplit_units", "grouped_gemm_wgrad_noalloc",
+    "drgg_tailsplit_units", "drgg_wgrad_tail_plan", "grouped_gemm_wgrad_noalloc",
     "drgg_set_knob", "drgg_timing_count", "drgg_timing_read", "drgg_status_string", "drgg_abi_version",
 )
 
@@ -109,6 +109,8 @@ def _load(path=LIB_PATH):
     lib.drgg_plan.restype = c_int
     lib.drgg_wgrad_chunking.argtypes = [i64, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
     lib.drgg_wgrad_chunking.restype = c_int
+    lib.drgg_wgrad_tail_plan.argtypes = [vp, i32, i64, i64, ctypes.POINTER(c_int), vp]
+    lib.drgg_wgrad_tail_plan.restype = c_int
     lib.drgg_tailsplit_units.argtypes = [i64, i64, ctypes.POINTER(i64)]
     lib.drgg_tailsplit_units.restype = c_int
     lib.drgg_route_split.argtypes = [i32, i64, i64, i64, c_int]
@@ -174,6 +176,21 @@ def tailsplit_units(tiles: int, workers: int):
     out = (ctypes.c_int64 * 4)()
     _check(lib.drgg_tailsplit_units(int(tiles), int(workers), out), "drgg_tailsplit_units")
     return tuple(int(v) for v in out)
+
+
+def wgrad_tail_plan(offsets, N: int, K: int):
+    """(tail_only, row0) of the deterministic weight gradient's plan for host
+    group offsets (a sequence of E + 1 ints): whether the kernel runs the
+    tail-only plan, and per expert the first dW row that comes from folded
+    partials (the rows above it are whole tiles, stored directly)."""
+    import numpy as np
+    o = np.ascontiguousarray(np.asarray(offsets, dtype=np.int32))
+    E = o.size - 1
+    tail = ctypes.c_int()
+    row0 = np.zeros(max(E, 1), dtype=np.int32)
+    _check(lib.drgg_wgrad_tail_plan(o.ctypes.data, E, N, K, ctypes.byref(tail), row0.ctypes.data),
+           "drgg_wgrad_tail_plan")
+    return bool(tail.value), row0[:E]
 
 
 def wgrad_runs_deterministic(E: int, M: int, N: int, K: int, out_dtype: int = BF16,

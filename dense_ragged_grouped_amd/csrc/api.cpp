@@ -608,6 +608,15 @@ drgg_status drgg_wgrad_chunking(int64_t T, int64_t chunk_max, int64_t* chunk_len
     return DRGG_OK;
 }
 
+drgg_status drgg_wgrad_tail_plan(const int32_t* group_offsets, int32_t E, int64_t N, int64_t K, int* tail_only,
+                                 int32_t* row0) {
+    if (!group_offsets || !tail_only || E < 1 || E > kMaxExperts || N < 8 || K < 8 || N > (1 << 22) ||
+        K > (1 << 22))
+        return DRGG_EINVAL;
+    *tail_only = wgrad_tail_plan(group_offsets, E, N, K, row0) ? 1 : 0;
+    return DRGG_OK;
+}
+
 drgg_status drgg_tailsplit_units(int64_t tiles, int64_t workers, int64_t* out) {
     if (!out || tiles < 0 || workers < 1) return DRGG_EINVAL;
     const TailSplit t = tailsplit_units(tiles, workers);

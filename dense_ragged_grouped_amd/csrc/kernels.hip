@@ -147,28 +147,27 @@ __device__ void build_schedule(Sched& s, const int32_t* __restrict__ offs, int E
 // index) and, for the persistent walk below, the rounds alternate direction
 // ("snake"): the longest items of round r and the shortest of round r+1 land
 // on the same workgroup.  On the Zipf-routed E=32 workload that balances the
-// workgroups to 96 % of the mean load, against 81 % in expert order.  After
-// this, s.prefix[p] is the exclusive prefix of work in the new order and
-// expert_at(s, p) the expert at position p (stored as 16-bit values over
-// s.scan, which build_schedule no longer needs).  `scr` is 8 KB of LDS
-// that is free until the first stage load; `clen(T)` is an expert's chunk
-// length and `work(T)` its item count.  Must be called by all threads after
-// build_schedule; ends with a barrier.
+// workgroups to 96 % of the mean load, against 81 % in expert order.
+//
+// rank_experts writes that order as 16-bit expert ids over s.scan (which
+// build_schedule no longer needs): expert_at(s, p) is the expert at position
+// p.  position_prefix then rebuilds s.prefix[0..npos] as the exclusive
+// prefix of work(p) over positions p < npos (a plan may give an expert more
+// than one position: the tail-only plan of the deterministic weight
+// gradient has its whole tiles at p and its chunks at E + p).  `scr` is
+// 8 KB of LDS that is free until the first stage load; `clen(T)` is an
+// expert's chunk length.  Both must be called by all threads and end with a
+// barrier; rank_experts after build_schedule.
 static_assert(kMaxExperts <= 2 * kMaxGemmThreads && kMaxExperts <= 32767, "16-bit expert order in Sched::scan");
 __device__ __forceinline__ int expert_at(const Sched& s, int p) {
     return reinterpret_cast<const int16_t*>(s.scan)[p];
 }
-template <class LenFn, class WorkFn>
-__device__ void order_longest_first(Sched& s, lds_t* scr, int E, LenFn clen, WorkFn work) {
+template <class LenFn>
+__device__ void rank_experts(Sched& s, lds_t* scr, int E, LenFn clen) {
     static_assert(kMaxExperts <= 4 * kGemmThreads, "at most four experts per thread");
     const int tid = threadIdx.x, nthr = blockDim.x;
     auto* key = reinterpret_cast<__attribute__((address_space(3))) int32_t*>(scr);
-    auto* wk = key + kMaxExperts;
-    for (int e = tid; e < E; e += nthr) {
-        const int32_t T = s.offs[e + 1] - s.offs[e];
-        key[e] = clen(T);
-        wk[e] = work(T);
-    }
+    for (int e = tid; e < E; e += nthr) key[e] = clen(s.offs[e + 1] - s.offs[e]);
     __syncthreads();
     // rank of expert e: experts with a longer chunk, or as long and a lower
     // index, go first; each thread ranks its (up to four) experts in one
@@ -185,35 +184,66 @@ __device__ void order_longest_first(Sched& s, lds_t* scr, int E, LenFn clen, Wor
 #pragma unroll
         for (int u = 0; u < 4; ++u) r4[u] += kf > k4[u] || (kf == k4[u] && f < tid + u * nthr);
     }
+    __syncthreads();   // the keys are read; s.scan may be overwritten
     int16_t* perm = reinterpret_cast<int16_t*>(s.scan);
 #pragma unroll
     for (int u = 0; u < 4; ++u)
         if (tid + u * nthr < E) perm[r4[u]] = (int16_t)(tid + u * nthr);
     __syncthreads();
-    // exclusive prefix of the item counts in the new order: per-thread runs,
-    // then a serial scan of the run sums (in key[], no longer needed)
-    const int per = (E + nthr - 1) / nthr;
-    const int lo = min(tid * per, E), hi = min(lo + per, E);
-    int32_t run = 0;
-    for (int q = lo; q < hi; ++q) run += wk[perm[q]];
-    key[tid] = run;
+}
+// Exclusive prefix sum of v over the workgroup's threads (in thread order);
+// *total gets the sum.  Inclusive scans within each wave by lane shuffles,
+// then one pass over the (at most 8) wave sums in `tmp` (LDS, one word per
+// wave plus one).  A serial pass over every thread's value costs tens of
+// microseconds at kernel start; this costs a few hundred cycles.  Must be
+// called by all threads; ends with a barrier.
+__device__ int32_t block_exclusive_scan(int32_t v, __attribute__((address_space(3))) int32_t* tmp, int32_t* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    int32_t x = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int32_t y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+    }
+    if (lane == 63) tmp[wave] = x;
     __syncthreads();
-    if (tid == 0) {
+    if (threadIdx.x == 0) {
         int32_t acc = 0;
-        for (int t = 0; t < nthr; ++t) {
-            const int32_t v = key[t];
-            key[t] = acc;
-            acc += v;
+        for (int w = 0; w < nw; ++w) {
+            const int32_t t = tmp[w];
+            tmp[w] = acc;
+            acc += t;
         }
-        s.prefix[E] = acc;
+        tmp[nw] = acc;
     }
     __syncthreads();
-    int32_t acc = key[tid];
+    const int32_t r = tmp[wave] + x - v;
+    *total = tmp[nw];
+    __syncthreads();
+    return r;
+}
+
+template <class WorkFn>
+__device__ void position_prefix(Sched& s, lds_t* scr, int npos, WorkFn work) {
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    // per-thread runs of positions, then a scan of the run sums
+    const int per = (npos + nthr - 1) / nthr;
+    const int lo = min(tid * per, npos), hi = min(lo + per, npos);
+    int32_t run = 0;
+    for (int q = lo; q < hi; ++q) run += work(q);
+    int32_t total;
+    int32_t acc = block_exclusive_scan(run, reinterpret_cast<__attribute__((address_space(3))) int32_t*>(scr), &total);
     for (int q = lo; q < hi; ++q) {
         s.prefix[q] = acc;
-        acc += wk[perm[q]];
+        acc += work(q);
     }
+    if (tid == 0) s.prefix[npos] = total;
     __syncthreads();
+}
+template <class LenFn, class WorkFn>
+__device__ void order_longest_first(Sched& s, lds_t* scr, int E, LenFn clen, WorkFn work) {
+    rank_experts(s, scr, E, clen);
+    position_prefix(s, scr, E, [&](int q) { return work(s.offs[expert_at(s, q) + 1] - s.offs[expert_at(s, q)]); });
 }
 
 // Work item of round r for the workgroup at (XCD-remapped) index wb of G:
@@ -227,9 +257,11 @@ __device__ __forceinline__ int64_t snake_item(int64_t r, int64_t wb, int64_t G) 
 // registers (keeps the per-tile state out of the VGPR budget).
 __device__ __forceinline__ int32_t uni(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// Largest e with prefix[e] <= w (so that prefix[e] <= w < prefix[e+1]).
-__device__ __forceinline__ int find_expert(const Sched& s, int E, int32_t w) {
-    int lo = 0, hi = E;   // answer in [0, E)
+// Largest e < n with prefix[e] <= w (so that prefix[e] <= w < prefix[e+1]
+// when w < prefix[n]); n is the number of experts, or of positions of a
+// plan's walk.
+__device__ __forceinline__ int find_expert(const Sched& s, int n, int32_t w) {
+    int lo = 0, hi = n;   // answer in [0, n)
     while (lo < hi) {
         int mid = (lo + hi + 1) >> 1;
         if (s.prefix[mid] <= w) lo = mid; else hi = mid - 1;
@@ -248,6 +280,35 @@ __device__ __forceinline__ int32_t chunk_len_dev(int32_t T, int64_t chunk_max) {
 __device__ __forceinline__ int32_t chunks_dev(int32_t T, int64_t chunk_max) {
     int32_t l = chunk_len_dev(T, chunk_max);
     return l ? (T + l - 1) / l : 0;
+}
+
+// Estimated time of a planned walk on the kRuleCUs reference workgroups: the
+// items 0 .. prefix[npos]-1 handed out in snake rounds, as the persistent
+// kernels hand them out, each costing len(its position) plus
+// kItemOverheadTokens tokens; returns the largest per-workgroup load.  It
+// chooses between the two plans of the deterministic weight gradient and is
+// a function of the plan only, never of the device.  `red` is an LDS word.
+// Must be called by all threads (at least kRuleCUs of them); ends with a
+// barrier.
+template <class LenFn>
+__device__ uint64_t walk_makespan(const Sched& s, int npos, LenFn len, unsigned long long* red) {
+    if (threadIdx.x == 0) *red = 0;
+    __syncthreads();
+    const int64_t total = s.prefix[npos];
+    if (threadIdx.x < kRuleCUs) {
+        const int64_t b = threadIdx.x;
+        uint64_t load = 0;
+        for (int64_t r = 0;; ++r) {
+            const int64_t i = snake_item(r, b, kRuleCUs);
+            if (i >= total) break;   // later rounds hold only larger indices
+            load += (uint64_t)len(find_expert(s, npos, (int32_t)i)) + (uint64_t)kItemOverheadTokens;
+        }
+        atomicMax(red, (unsigned long long)load);
+    }
+    __syncthreads();
+    const uint64_t m = *red;
+    __syncthreads();
+    return m;
 }
 
 // Workgroup b of G -> logical work index.  Workgroups are dispatched to the
@@ -1226,6 +1287,23 @@ __global__ __launch_bounds__(64 * WAVES) void gg_fwd_dgrad_kernel(GemmArgs a) {
 template <int BM, int BN>
 constexpr int wgrad_det_waves() { return BM == 256 && BN == 256 ? 8 : 4; }
 
+// The deterministic weight gradient's two plans (chunk rule parts 1-3 in
+// plan.hpp).  Both cut expert e into S_e chunks of L_e tokens.  The
+// all-split plan runs every tile of an expert with S_e > 1 as S_e chunk
+// items; the tail-only plan runs the tiles of its first h_e 256-row bands
+// (wgrad_whole_rows) as whole items and only the others as chunk items.
+// Every workgroup estimates both planned walks on the kRuleCUs reference
+// workgroups with the 256x256 reference tile (walk_makespan) and takes the
+// tail-only plan when it is not slower: with equal experts its whole tiles
+// fill full waves and the plan writes a third of the partials or fewer;
+// with ragged experts whole tiles of different lengths balance badly and the
+// all-split plan is kept.  The choice depends on the offsets and (E, M, N,
+// K) only: not on the CU count, the grid or the kernel's tile shape.
+//
+// Walk positions: all-split plan, position p < E = the p-th expert of the
+// longest-chunk-first order with all its items; tail-only plan, position
+// p < E = that expert's whole tiles (none unless S_e > 1) and E + p = its
+// chunk items (or, for S_e = 1, its whole tiles, which are as short).
 template <int BM, int BN, bool OUT_BF16>
 __global__ __launch_bounds__((64 * wgrad_det_waves<BM, BN>())) void gg_wgrad_det_kernel(GemmArgs a) {
     constexpr int WV = wgrad_det_waves<BM, BN>();
@@ -1234,56 +1312,124 @@ __global__ __launch_bounds__((64 * wgrad_det_waves<BM, BN>())) void gg_wgrad_det
     __shared__ Sched sch;
     __shared__ int32_t slot_base[kMaxExperts + 1];
     __shared__ __attribute__((aligned(16))) char ep[kStaged ? WV * ep_rows(BM, BN) * 128 : 16];
+    __shared__ unsigned long long s_red;
     const int32_t tn = (int32_t)((a.N + BM - 1) / BM), tk = (int32_t)((a.K + BN - 1) / BN);
     const int32_t P = tn * tk;
+    const int32_t tn0 = (int32_t)((a.N + 255) / 256), tk0 = (int32_t)((a.K + 255) / 256);
+    const int32_t P0 = tn0 * tk0;   // reference tiles per expert
     const int64_t cmax = a.chunk_max;
-    build_schedule(sch, a.offs, a.E, a.M, a.T,
-                   [=](int, int32_t T) { return P * chunks_dev(T, cmax); });
+    const int E = a.E;
+    build_schedule(sch, a.offs, E, a.M, a.T, [=](int, int32_t T) { return P * chunks_dev(T, cmax); });
     // partial slots: experts cut into more than one chunk, in expert order
-    if (threadIdx.x == 0) {
-        int32_t sb = 0;
-        for (int x = 0; x < a.E; ++x) {
-            slot_base[x] = sb;
+    {
+        const int nthr = blockDim.x, per = (E + nthr - 1) / nthr;
+        const int lo = min((int)threadIdx.x * per, E), hi = min(lo + per, E);
+        auto slots = [&](int x) {
             const int32_t c = chunks_dev(sch.offs[x + 1] - sch.offs[x], cmax);
-            if (c > 1) sb += c;
+            return c > 1 ? c : 0;
+        };
+        int32_t run = 0;
+        for (int x = lo; x < hi; ++x) run += slots(x);
+        int32_t total;
+        int32_t acc = block_exclusive_scan(run, reinterpret_cast<__attribute__((address_space(3))) int32_t*>(stg.b[0]),
+                                           &total);
+        for (int x = lo; x < hi; ++x) {
+            slot_base[x] = acc;
+            acc += slots(x);
         }
-        slot_base[a.E] = sb;
+        if (threadIdx.x == 0) slot_base[E] = total;
     }
-    __syncthreads();
+    rank_experts(sch, stg.b[0], E, [=](int32_t T) { return chunk_len_dev(T, cmax); });
+    auto T_at = [&](int q) { const int e = expert_at(sch, q); return sch.offs[e + 1] - sch.offs[e]; };
+    // whole 256-row bands of an expert with T tokens in the tail-only plan
+    auto bands = [&](int32_t T) { return (int32_t)wgrad_whole_rows(T, a.M, a.N, a.K, chunks_dev(T, cmax)); };
+    // plan choice on the reference tile (only when some split expert keeps
+    // whole bands, else the two plans are the same)
+    int tail = 0;
+    int keeps_whole = 0;
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        const int32_t T = sch.offs[e + 1] - sch.offs[e];
+        keeps_whole |= chunks_dev(T, cmax) > 1 && bands(T) > 0;
+    }
+    if (E <= kTailPlanMaxExperts && __syncthreads_or(keeps_whole)) {
+        const uint64_t mk_split = [&] {
+            position_prefix(sch, stg.b[0], E, [&](int q) { return P0 * chunks_dev(T_at(q), cmax); });
+            return walk_makespan(sch, E, [&](int q) {
+                const int32_t T = T_at(q);
+                return chunks_dev(T, cmax) > 1 ? chunk_len_dev(T, cmax) : T;
+            }, &s_red);
+        }();
+        position_prefix(sch, stg.b[0], 2 * E, [&](int q) {
+            const int32_t T = T_at(q < E ? q : q - E), S = chunks_dev(T, cmax);
+            if (S <= 1) return q < E ? 0 : P0;
+            const int32_t w0 = bands(T) * tk0;   // whole reference tiles
+            return q < E ? w0 : (P0 - w0) * S;
+        });
+        const uint64_t mk_tail = walk_makespan(sch, 2 * E, [&](int q) {
+            const int32_t T = T_at(q < E ? q : q - E);
+            return q < E || chunks_dev(T, cmax) <= 1 ? T : chunk_len_dev(T, cmax);
+        }, &s_red);
+        tail = mk_tail <= mk_split;
+    }
     // the fold kernel's per-expert table (the same values from every
-    // workgroup; workgroup 0 writes it)
+    // workgroup; workgroup 0 writes it): T_e, chunks, first partial slot,
+    // first row of the partials (rows above it were stored directly)
     if (blockIdx.x == 0)
-        for (int e = threadIdx.x; e < a.E; e += blockDim.x) {
-            const int32_t T = sch.offs[e + 1] - sch.offs[e];
-            *reinterpret_cast<int4*>(a.fold_info + 4 * e) = int4{T, chunks_dev(T, cmax), slot_base[e], 0};
+        for (int e = threadIdx.x; e < E; e += blockDim.x) {
+            const int32_t T = sch.offs[e + 1] - sch.offs[e], S = chunks_dev(T, cmax);
+            const int32_t row0 = tail && S > 1 ? (int32_t)min<int64_t>(a.N, (int64_t)bands(T) * 256) : 0;
+            *reinterpret_cast<int4*>(a.fold_info + 4 * e) = int4{T, S, slot_base[e], row0};
         }
-    order_longest_first(sch, stg.b[0], a.E, [=](int32_t T) { return chunk_len_dev(T, cmax); },
-                        [=](int32_t T) { return P * chunks_dev(T, cmax); });
-    const int64_t total = uni(sch.prefix[a.E]);
+    // whole kernel tiles of an expert (a prefix of its row-major tiles)
+    auto nwhole = [&](int32_t T) {
+        return tail && chunks_dev(T, cmax) > 1 ? (int32_t)min<int64_t>(tn, (int64_t)bands(T) * (256 / BM)) * tk : 0;
+    };
+    const int npos = tail ? 2 * E : E;
+    position_prefix(sch, stg.b[0], npos, [&](int q) {
+        const int32_t T = T_at(q < E ? q : q - E), S = chunks_dev(T, cmax);
+        if (!tail) return P * S;
+        if (S <= 1) return q < E ? 0 : P;
+        const int32_t nw = nwhole(T);
+        return q < E ? nw : (P - nw) * S;
+    });
+    const int64_t total = uni(sch.prefix[npos]);
     const int64_t G = gridDim.x;
     int64_t wb = xcd_remap(blockIdx.x, G), round = 0;
     if (a.reverse) wb = G - 1 - wb;
     int64_t w = snake_item(0, wb, G);
     auto more = [&]() { return w < total; };
     auto next = [&](TileInfo& t) {
-        const int pos = uni(find_expert(sch, a.E, (int32_t)w));
-        const int e = uni(expert_at(sch, pos));
+        const int pos = uni(find_expert(sch, npos, (int32_t)w));
+        const int e = uni(expert_at(sch, pos < E ? pos : pos - E));
         const int32_t oe = uni(sch.offs[e]), oe1 = uni(sch.offs[e + 1]);
         const int32_t T = oe1 - oe;
         const int32_t clen = chunk_len_dev(T, cmax);
         const int32_t nch = (T + clen - 1) / clen;
         const int32_t local = (int32_t)w - uni(sch.prefix[pos]);
-        const int32_t chunk = local / P, tile = local % P;   // chunk-major: tiles of a chunk adjacent
+        int32_t tile, chunk = 0;
+        bool whole;
+        if (tail && pos < E) {          // a whole tile of a split expert
+            tile = local;
+            whole = true;
+        } else if (nch > 1) {           // a chunk item: chunk-major, tiles of a chunk adjacent
+            const int32_t nw = nwhole(T), ps = P - nw;
+            chunk = local / ps;
+            tile = nw + local % ps;
+            whole = false;
+        } else {
+            tile = local;
+            whole = true;
+        }
         const int32_t ti = tile / tk, tj = tile % tk;
         const int64_t n0 = (int64_t)ti * BM, k0 = (int64_t)tj * BN;
-        const int64_t tb = oe + (int64_t)chunk * clen;
-        const int32_t len = (int32_t)min<int64_t>(clen, oe1 - tb);
+        const int64_t tb = oe + (whole ? 0 : (int64_t)chunk * clen);
+        const int32_t len = whole ? T : (int32_t)min<int64_t>(clen, oe1 - tb);
         t.o0 = n0;
         t.o1 = k0;
         t.rows = (int32_t)min<int64_t>(BM, a.N - n0);
         t.cols = (int32_t)min<int64_t>(BN, a.K - k0);
         t.e = e;
-        t.aux = nch == 1 ? -1 : uni(slot_base[e]) + chunk;   // -1: store the output directly
+        t.aux = whole ? -1 : uni(slot_base[e]) + chunk;   // -1: store the output directly
         // dW[n][k] = sum_t G[t][n] X[t][k]: both operands token-major (MN-major)
         t.A = Operand{a.A + tb * a.a_rs + e * a.a_gs + n0, a.a_rs, t.rows, len};
         t.B = Operand{a.B + tb * a.b_rs + e * a.b_gs + k0, a.b_rs, t.cols, len};
@@ -1291,7 +1437,7 @@ __global__ __launch_bounds__((64 * wgrad_det_waves<BM, BN>())) void gg_wgrad_det
     };
     auto finish = [&](const TileInfo& t, const TileMma<BM, BN, false, false, WV>& mma) {
         const int64_t ld = a.K;
-        if (t.aux < 0) {   // one chunk: round and store the output directly
+        if (t.aux < 0) {   // a whole tile: round and store the output directly
             const int64_t off = (int64_t)t.e * a.N * a.K + t.o0 * a.K + t.o1;
             void* base = OUT_BF16 ? (void*)(reinterpret_cast<uint16_t*>(a.out) + off)
                                   : (void*)(reinterpret_cast<float*>(a.out) + off);
@@ -1309,24 +1455,28 @@ __global__ __launch_bounds__((64 * wgrad_det_waves<BM, BN>())) void gg_wgrad_det
 }
 
 // Fold the partials of every expert cut into more than one chunk, in chunk
-// order, in FP32, then round once; zero-fill experts without tokens.
+// order, in FP32, then round once (only rows from the expert's first
+// partial row on: the rows of its whole tiles were stored directly);
+// zero-fill experts without tokens.
 // Grid: (ceil(N*K / 2048), E); 256 threads x 8 consecutive elements.
 template <bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void gg_wgrad_fold_kernel(GemmArgs a) {
     const int e = blockIdx.y;
     // T_e, chunks_e and the first partial slot, from the chunk kernel's
     // table; with M = 0 that kernel does not run and every expert is empty
-    int32_t Te = 0, ce = 0, sb = 0;
+    int32_t Te = 0, ce = 0, sb = 0, row0 = 0;
     if (a.M > 0) {
         const int4 info = *reinterpret_cast<const int4*>(a.fold_info + 4 * e);
         Te = info.x;
         ce = info.y;
         sb = info.z;
+        row0 = info.w;
     }
     if (Te > 0 && ce <= 1) return;   // written directly by the chunk kernel
     const int64_t nk = a.N * a.K;
     const int64_t i0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 8;
     if (i0 >= nk) return;            // nk is a multiple of 8
+    if (i0 < (int64_t)row0 * a.K) return;   // a row of whole tiles, written directly
     float s[8];
     if (Te == 0) {
 #pragma unroll

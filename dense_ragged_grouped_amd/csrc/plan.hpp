@@ -5,7 +5,17 @@
 // kernel launchers (kernels.hip); nothing here touches the GPU.
 #pragma once
 
+#include <algorithm>
 #include <cstdint>
+#include <vector>
+
+// Functions the kernels evaluate too are host-and-device when hipcc compiles
+// this header, plain host functions otherwise.
+#if defined(__HIPCC__)
+#define DRGG_HD __host__ __device__
+#else
+#define DRGG_HD
+#endif
 
 namespace drgg {
 
@@ -51,14 +61,14 @@ inline TileShape tile_shape(int id) {
     }
 }
 
-inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
-inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+DRGG_HD inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+DRGG_HD inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
 // Chunk rule part 2 (host mirror of the device function): an expert with T
 // tokens is cut into chunks of `len` tokens (the last one shorter), starting
 // at its first token.  S = ceil(T / chunk_max), len = ceil(T / S) rounded up
 // to a multiple of 64, chunks = ceil(T / len).
-inline void wgrad_chunking(int64_t T, int64_t chunk_max, int64_t* len, int64_t* chunks) {
+DRGG_HD inline void wgrad_chunking(int64_t T, int64_t chunk_max, int64_t* len, int64_t* chunks) {
     if (T <= 0) { *len = 0; *chunks = 0; return; }
     const int64_t s = ceil_div(T, chunk_max);
     const int64_t l = round_up(ceil_div(T, s), kTileK);
@@ -100,6 +110,95 @@ inline int64_t wgrad_chunk_max(int32_t E, int64_t M, int64_t N, int64_t K) {
         }
     }
     return best;
+}
+
+// Deterministic weight gradient, chunk rule part 3: the tail-only plan.
+// Whole output tiles in full waves, only the tail split (flashinfer PR
+// #8258, Summary: the last output tiles, the "tail", are the ones whose K
+// range is split).  An expert cut into S > 1 chunks (part 2) has P0 output
+// tiles of 256 x 256 (the reference tile, as in part 1) and a share
+// R_e = kRuleCUs * T / M of the kRuleCUs reference workgroups (its share of
+// the work).  Its whole tiles fill the F = floor(P0 / R_e) full waves on
+// that share, floor(F * R_e) tiles, rounded down to whole rows of reference
+// tiles; every other tile is cut into the S chunks.  Returns the number of
+// 256-row reference rows of the expert's output (dW rows n < 256 * result)
+// that run as whole tiles: all of them (ceil(N / 256)) when S <= 1.  A pure
+// function of the problem, never of the device; the result does not depend
+// on the kernel's tile shape either (its tiles nest in the 256-row bands).
+DRGG_HD inline int64_t wgrad_whole_rows(int64_t T, int64_t M, int64_t N, int64_t K, int64_t S) {
+    const int64_t tn0 = ceil_div(N, 256), tk0 = ceil_div(K, 256);
+    if (S <= 1 || T <= 0 || M <= 0) return tn0;
+    const int64_t F = (tn0 * tk0 * M) / (kRuleCUs * T);
+    const int64_t full = (F * kRuleCUs * T) / M;
+    const int64_t h = full / tk0;
+    return h < tn0 ? h : tn0;
+}
+
+// Experts above this count always run the all-split plan: the tail-only
+// plan's walk has two positions per expert (whole tiles first, then the
+// chunks), and the kernels' schedule tables hold kMaxExperts + 1 entries.
+constexpr int kTailPlanMaxExperts = kMaxExperts / 2;
+
+// Host mirror of the deterministic weight gradient's plan choice, which the
+// chunk kernel makes on the device from the group offsets (same integer
+// arithmetic): the estimated time of each plan's walk on kRuleCUs reference
+// workgroups, in tokens (snake rounds over the walk positions, each item
+// costing its token count plus kItemOverheadTokens), with 256x256 reference
+// tiles; the tail-only plan when it differs and is not slower.  `offs` are
+// valid host offsets [E + 1] (o[0] = 0, non-decreasing, o[E] = M).  Fills row0[e] (if
+// given) with the first dW row of expert e that the fold writes (0 in the
+// all-split plan, and for experts not cut into chunks).  For tests and
+// inspection only.
+inline bool wgrad_tail_plan(const int32_t* offs, int32_t E, int64_t N, int64_t K, int32_t* row0) {
+    std::vector<int64_t> T(E > 0 ? E : 0);
+    int64_t M = 0, prev = 0;
+    const int64_t last = E > 0 ? std::max<int64_t>(offs[E], 0) : 0;
+    for (int32_t e = 0; e < E; ++e) {   // clamp into [0, M], non-decreasing
+        const int64_t lo = std::max(prev, std::min<int64_t>(std::max<int64_t>(offs[e], 0), last));
+        const int64_t hi = std::max(lo, std::min<int64_t>(std::max<int64_t>(offs[e + 1], 0), last));
+        T[e] = hi - lo;
+        prev = hi;
+    }
+    M = last;
+    for (int32_t e = 0; e < E && row0; ++e) row0[e] = 0;
+    if (E > kTailPlanMaxExperts || M <= 0) return false;
+    const int64_t cmax = wgrad_chunk_max(E, M, N, K);
+    std::vector<int64_t> L(E), S(E), band(E);
+    for (int32_t e = 0; e < E; ++e) {
+        wgrad_chunking(T[e], cmax, &L[e], &S[e]);
+        band[e] = wgrad_whole_rows(T[e], M, N, K, S[e]);
+    }
+    std::vector<int32_t> perm(E);
+    for (int32_t e = 0; e < E; ++e) perm[e] = e;
+    std::stable_sort(perm.begin(), perm.end(), [&](int32_t x, int32_t y) { return L[x] > L[y]; });
+    const int64_t tk0 = ceil_div(K, 256), P0 = ceil_div(N, 256) * tk0;
+    auto makespan = [&](const std::vector<int64_t>& work, const std::vector<int64_t>& len) {
+        std::vector<uint64_t> load(kRuleCUs, 0);
+        int64_t i = 0;
+        for (size_t q = 0; q < work.size(); ++q)
+            for (int64_t j = 0; j < work[q]; ++j, ++i) {
+                const int64_t r = i / kRuleCUs, b = i % kRuleCUs;
+                load[(r & 1) ? kRuleCUs - 1 - b : b] += (uint64_t)(len[q] + kItemOverheadTokens);
+            }
+        return *std::max_element(load.begin(), load.end());
+    };
+    std::vector<int64_t> w1(E), l1(E), w2(2 * E), l2(2 * E);
+    int64_t whole_tiles = 0;
+    for (int32_t q = 0; q < E; ++q) {
+        const int32_t e = perm[q];
+        w1[q] = P0 * S[e];
+        l1[q] = S[e] > 1 ? L[e] : T[e];
+        const int64_t w0 = S[e] > 1 ? band[e] * tk0 : 0;
+        whole_tiles += w0;
+        w2[q] = w0;
+        l2[q] = T[e];
+        w2[E + q] = S[e] > 1 ? (P0 - w0) * S[e] : P0;
+        l2[E + q] = S[e] > 1 ? L[e] : T[e];
+    }
+    const bool tail = whole_tiles > 0 && makespan(w2, l2) <= makespan(w1, l1);
+    for (int32_t e = 0; e < E && row0 && tail; ++e)
+        row0[e] = S[e] > 1 ? (int32_t)std::min<int64_t>(N, band[e] * 256) : 0;
+    return tail;
 }
 
 // Partial slots the deterministic weight gradient may need: only experts cut

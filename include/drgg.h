@@ -350,6 +350,24 @@ int drgg_timing_count(void);
 drgg_status drgg_timing_read(int i, const char **kernel, float *ms);
 
 /*
+ * The deterministic weight gradient's plan for these group offsets (HOST
+ * only; group_offsets is a HOST array [E + 1]; the kernel makes the same
+ * choice on the device).  Experts cut into chunks run either every output
+ * tile as chunk items ("all-split"), or the tiles of their first 256-row
+ * bands whole, in full waves on their share of 256 reference workgroups,
+ * and only the remaining tiles -- the tail -- as chunk items ("tail-only";
+ * flashinfer PR #8258, Summary: only the tail's K range is split).  The
+ * kernel takes the tail-only plan when its planned walk is not slower on 256
+ * reference workgroups; the choice depends on the problem only.  Writes
+ * *tail_only (HOST) = 1 for the tail-only plan, and, if row0 (HOST, E
+ * entries) is given, the first dW row of each expert that comes from folded
+ * partials (0 for all rows).  DRGG_EINVAL for null pointers or E, N, K out
+ * of range.
+ */
+drgg_status drgg_wgrad_tail_plan(const int32_t *group_offsets, int32_t E, int64_t N, int64_t K,
+                                 int *tail_only, int32_t *row0);
+
+/*
  * The tail-split rule of a persistent schedule (HOST only; flashinfer
  * PR #7516, #7632 commit body, its tail-split routing test): `tiles` equal
  * output tiles on `workers` persistent workers run in full waves plus a

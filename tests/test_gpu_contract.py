@@ -440,3 +440,76 @@ def test_error_paths(drgg):
         drgg.router_gemm_fp32_bf16x3(Xr, Wr, out=torch.empty(39, 24, device="cuda"))
     with pytest.raises(ValueError):
         drgg.router_gemm_fp32_bf16x3(Xr, Wr, out=torch.empty(24, 40, device="cuda"))
+
+
+# ---- the deterministic weight gradient's tail-only plan ------------------------
+
+def _tail_problem(integer=False):
+    """32 equal experts of 768 tokens, N = 768, K = 1024: the kernel runs the
+    first two 256-row bands of every expert as whole tiles and cuts only the
+    third band into chunks."""
+    return synth.make_problem("tail_plan", 341, np.full(32, 768), N=768, K=1024, w_std=0.02, integer=integer)
+
+
+def _fold_table(drgg, prob, ws):
+    p = drgg.plan(drgg.OP_WGRAD, prob.E, prob.M, prob.N, prob.K, drgg.FP32, True)
+    off = p["max_partials"] * prob.N * prob.K * 4
+    return ws[off:off + 16 * prob.E].view(torch.int32).reshape(prob.E, 4).cpu().numpy()
+
+
+@pytest.mark.parametrize("case", ["tail", "zipf_small", "dense"])
+def test_wgrad_plan_on_device_matches_host_rule(drgg, case):
+    """The chunk kernel writes, for the fold, each expert's token count,
+    chunk count and first folded row; that row must be the one the host
+    mirror of the plan rule gives (tail-only: the whole bands' end; all-split:
+    0), and the result must match the oracle."""
+    if case == "tail":
+        prob = _tail_problem()
+    elif case == "zipf_small":
+        prob = synth.make_problem("zipf_small", 342, synth.zipf_counts(342, 24576, 16, 2), N=768, K=1024,
+                                  w_std=0.02)
+    else:
+        prob = synth.make_problem("dense_plan", 343, np.array([8192]), N=512, K=1024, w_std=0.02)
+    dv = dev_inputs(prob)
+    n = drgg.workspace_size(drgg.OP_WGRAD, prob.E, prob.M, prob.N, prob.K, drgg.FP32, True)
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    out = drgg.grouped_gemm_wgrad(dv["X"], dv["G"], dv["offs"], out_dtype=torch.float32, deterministic=True,
+                                  workspace=ws)
+    torch.cuda.synchronize()
+    tail, row0 = drgg.wgrad_tail_plan(prob.offs, prob.N, prob.K)
+    assert tail == (case == "tail")
+    table = _fold_table(drgg, prob, ws)
+    cm = drgg.plan(drgg.OP_WGRAD, prob.E, prob.M, prob.N, prob.K, drgg.FP32, True)["chunk_max"]
+    assert table[:, 0].tolist() == prob.counts.tolist()
+    assert table[:, 1].tolist() == [drgg.wgrad_chunking(int(t), cm)[1] for t in prob.counts]
+    assert table[:, 3].tolist() == row0.tolist()
+    idx = np.union1d(parity.sample_indices(prob, "wgrad"), parity.tile_indices(prob, "wgrad"))
+    parity.compare(prob, "wgrad", parity.from_dev(out), False, idx=idx, what=f"plan {case}")
+
+
+@pytest.mark.parametrize("integer", [False, True])
+def test_tail_plan_bitwise_across_tiles_grids_and_order(drgg, integer):
+    """In the tail-only plan the whole bands are 256-row bands whatever the
+    kernel's tile: every tile shape, grid size and walk order gives the same
+    bits (and, on integer inputs, the oracle's)."""
+    prob = _tail_problem(integer=integer)
+    dv = dev_inputs(prob)
+    for out_dtype in (torch.float32, torch.bfloat16):
+        ref = bits(run_program(drgg, "wgrad", dv, out_dtype, True))
+        try:
+            for tile in (1, 2, 3, 4, 5):
+                drgg.set_knob(drgg.KNOB_TILE, tile)
+                for grid, rev in ((0, 0), (0, 1), (17, 0), (255, 1)):
+                    drgg.set_knob(drgg.KNOB_GRID, grid)
+                    drgg.set_knob(drgg.KNOB_REVERSE, rev)
+                    got = bits(run_program(drgg, "wgrad", dv, out_dtype, True))
+                    assert np.array_equal(got, ref), f"tile {tile} grid {grid} reverse {rev} changed the bits"
+        finally:
+            drgg.set_knob(drgg.KNOB_TILE, 0)
+            drgg.set_knob(drgg.KNOB_GRID, 0)
+            drgg.set_knob(drgg.KNOB_REVERSE, 0)
+        out = run_program(drgg, "wgrad", dv, out_dtype, True)
+        torch.cuda.synchronize()
+        idx = np.union1d(parity.sample_indices(prob, "wgrad"), parity.tile_indices(prob, "wgrad"))
+        parity.compare(prob, "wgrad", parity.from_dev(out), out_dtype == torch.bfloat16, idx=idx,
+                       integer=integer, what=f"tail plan integer={integer}")

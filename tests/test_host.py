@@ -308,3 +308,54 @@ def test_nondet_routes_to_the_det_program_by_default(drgg):
         assert drgg.plan(drgg.OP_WGRAD, 32, 131072, 2048, 768, drgg.FP32, False, 256)["grid"] == 7
     finally:
         drgg.set_knob(drgg.KNOB_GRID, 0)
+
+
+# ---- the deterministic weight gradient's tail-only plan ----------------------------
+
+def _offs(counts):
+    import synth
+    return synth.offsets_from_counts(np.asarray(counts))
+
+
+def test_tail_plan_choices(drgg):
+    """The plan the kernel picks for the measured workloads: balanced gate_up
+    runs 4 of its 6 row bands as whole tiles (256 whole tiles, one full wave
+    on 256 reference workgroups, and 128 tail tiles in 2 chunks); the
+    Zipf-routed down workload, the dense and the square shapes keep the
+    all-split plan."""
+    import synth
+    tail, row0 = drgg.wgrad_tail_plan(_offs(np.full(8, 16384)), 1536, 2048)
+    assert tail and row0.tolist() == [1024] * 8
+    tail, row0 = drgg.wgrad_tail_plan(_offs(synth.zipf_counts(4004, 131072, 32, 2)), 2048, 768)
+    assert not tail and not row0.any()
+    for n in (48, 64, 512, 1024, 4096):
+        assert drgg.wgrad_tail_plan(_offs([16384]), n, 4096)[0] is False
+    tail, row0 = drgg.wgrad_tail_plan(_offs(np.full(32, 768)), 768, 1024)
+    assert tail and row0.tolist() == [512] * 32
+
+
+def test_tail_plan_properties(drgg):
+    rng = np.random.default_rng(11)
+    for _ in range(60):
+        E = int(rng.choice([1, 2, 4, 8, 16, 32]))
+        M = int(rng.choice([4096, 32768, 131072]))
+        N = int(rng.choice([64, 512, 768, 1536, 2048]))
+        K = int(rng.choice([256, 768, 1024, 2048]))
+        w = rng.lognormal(0, float(rng.choice([0.0, 0.1, 0.35, 1.0])), E)
+        counts = rng.multinomial(M, w / w.sum())
+        tail, row0 = drgg.wgrad_tail_plan(_offs(counts), N, K)
+        cm = drgg.plan(drgg.OP_WGRAD, E, M, N, K, drgg.FP32, True)["chunk_max"]
+        for e in range(E):
+            chunks = drgg.wgrad_chunking(int(counts[e]), cm)[1]
+            if not tail or chunks <= 1:
+                assert row0[e] == 0
+            else:
+                assert row0[e] % 256 == 0 or row0[e] == N
+                assert 0 <= row0[e] <= N
+        if tail:
+            assert row0.any()
+    # more experts than the tail-only walk has positions for: always all-split
+    assert drgg.wgrad_tail_plan(_offs(np.full(600, 2048)), 4096, 4096)[0] is False
+    assert drgg.wgrad_tail_plan(_offs(np.full(512, 2048)), 4096, 4096)[0] in (True, False)
+    with pytest.raises(drgg.DrggError):
+        drgg.wgrad_tail_plan([0], 64, 64)
