@@ -26,7 +26,7 @@ LIB_PATH = os.path.join(_HERE, "libdrgg.so")
 BF16, FP32 = 0, 1
 OP_FWD, OP_DGRAD, OP_WGRAD = 0, 1, 2
 KNOB_TILE, KNOB_GRID, KNOB_REVERSE, KNOB_TIMING, KNOB_NONDET = 1, 2, 3, 4, 5
-KNOB_CHECK_OFFSETS, KNOB_CHECK_WORKSPACE = 6, 7
+KNOB_CHECK_OFFSETS, KNOB_CHECK_WORKSPACE, KNOB_DELAY_SEED, KNOB_SPLIT_REPORT = 6, 7, 8, 9
 TILE_AUTO, TILE_256x256, TILE_128x128, TILE_256x128, TILE_128x256, TILE_64x256 = range(6)
 
 # the symbols include/drgg.h declares
@@ -35,7 +35,7 @@ EXPORTS = (
     "batched_gemm_fwd", "batched_gemm_dgrad", "batched_gemm_wgrad",
     "drgg_route_split", "drgg_route_clear", "drgg_route_count", "drgg_hold_cus",
     "grouped_gemm_workspace_size", "drgg_workspace_init", "drgg_plan", "drgg_wgrad_chunking",
-    "drgg_tailsplit_units", "drgg_wgrad_tail_plan", "grouped_gemm_wgrad_noalloc",
+    "drgg_tailsplit_units", "drgg_wgrad_tail_plan", "drgg_wgrad_split_plan", "grouped_gemm_wgrad_noalloc",
     "drgg_set_knob", "drgg_timing_count", "drgg_timing_read", "drgg_status_string", "drgg_abi_version",
 )
 
@@ -111,6 +111,9 @@ def _load(path=LIB_PATH):
     lib.drgg_wgrad_chunking.restype = c_int
     lib.drgg_wgrad_tail_plan.argtypes = [vp, i32, i64, i64, ctypes.POINTER(c_int), vp]
     lib.drgg_wgrad_tail_plan.restype = c_int
+    lib.drgg_wgrad_split_plan.argtypes = [vp, i32, i64, i64, c_int, i64, ctypes.POINTER(c_int), ctypes.POINTER(i64),
+                                          ctypes.POINTER(c_int)]
+    lib.drgg_wgrad_split_plan.restype = c_int
     lib.drgg_tailsplit_units.argtypes = [i64, i64, ctypes.POINTER(i64)]
     lib.drgg_tailsplit_units.restype = c_int
     lib.drgg_route_split.argtypes = [i32, i64, i64, i64, c_int]
@@ -191,6 +194,21 @@ def wgrad_tail_plan(offsets, N: int, K: int):
     _check(lib.drgg_wgrad_tail_plan(o.ctypes.data, E, N, K, ctypes.byref(tail), row0.ctypes.data),
            "drgg_wgrad_tail_plan")
     return bool(tail.value), row0[:E]
+
+
+def wgrad_split_plan(offsets, N: int, K: int, grid: int = 256, tile: int = 0, banded: bool = False):
+    """(slack, tail_tiles) of the split program's walk for host group offsets
+    on `grid` workgroups: whether its tail tiles run whole on the
+    least-loaded workgroups (slack placement), and how many tail tiles the
+    banded walk has; with banded=True also whether the banded walk runs."""
+    import numpy as np
+    o = np.ascontiguousarray(np.asarray(offsets, dtype=np.int32))
+    slack, tail, band = ctypes.c_int(), ctypes.c_int64(), ctypes.c_int()
+    _check(lib.drgg_wgrad_split_plan(o.ctypes.data, o.size - 1, N, K, tile, grid, ctypes.byref(slack),
+                                     ctypes.byref(tail), ctypes.byref(band)), "drgg_wgrad_split_plan")
+    if banded:
+        return bool(slack.value), int(tail.value), bool(band.value)
+    return bool(slack.value), int(tail.value)
 
 
 def wgrad_runs_deterministic(E: int, M: int, N: int, K: int, out_dtype: int = BF16,

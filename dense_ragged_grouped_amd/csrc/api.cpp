@@ -27,6 +27,9 @@ std::atomic<int64_t> g_knob_tile{0}, g_knob_grid{0}, g_knob_reverse{0}, g_knob_n
 // 0 = the environment's setting (DRGG_CHECK_OFFSETS / DRGG_CHECK_WORKSPACE
 // set to anything but "0"), off when unset.
 std::atomic<int64_t> g_knob_check_offsets{0}, g_knob_check_ws{0};
+// Split-program test aids: seeded delays before tail arrivals, and a device
+// address (4 int32) where the kernel reports its tail decision.
+std::atomic<int64_t> g_knob_delay{0}, g_knob_report{0};
 
 bool env_flag(const char* name) {
     const char* v = std::getenv(name);
@@ -392,6 +395,8 @@ drgg_status run_wgrad(const void* X, const void* G, const int32_t* group_offsets
     const int64_t sums = round_up(P * E * p.ts.bm * p.ts.bn * 4, 256);
     a.chunk_max = wgrad_chunk_max(E, M, N, K);   // chunks in whole 512-token units on the device
     a.tilesum = static_cast<float*>(workspace);
+    a.delay_seed = (int32_t)g_knob_delay.load();
+    a.report = reinterpret_cast<int32_t*>(g_knob_report.load());
     a.tickets = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + sums);
     return launch_status(launch_wgrad_atomic(p.tile, a, p.grid, bf16, stream));
 }
@@ -617,6 +622,19 @@ drgg_status drgg_wgrad_tail_plan(const int32_t* group_offsets, int32_t E, int64_
     return DRGG_OK;
 }
 
+drgg_status drgg_wgrad_split_plan(const int32_t* group_offsets, int32_t E, int64_t N, int64_t K, int tile,
+                                  int64_t grid, int* slack, int64_t* tail_tiles, int* banded_walk) {
+    if (!group_offsets || !slack || !tail_tiles || E < 1 || E > kMaxExperts || N < 8 || K < 8 || grid < 1 ||
+        tile < kTileAuto || tile > kTile64x256)
+        return DRGG_EINVAL;
+    const TileShape ts = tile_shape(tile == kTileAuto ? default_tile(DRGG_OP_WGRAD, N, K) : tile);
+    int64_t out[2];
+    *slack = wgrad_split_plan(group_offsets, E, N, K, ts.bm, ts.bn, grid, out) ? 1 : 0;
+    *tail_tiles = out[0];
+    if (banded_walk) *banded_walk = (int)out[1];
+    return DRGG_OK;
+}
+
 drgg_status drgg_tailsplit_units(int64_t tiles, int64_t workers, int64_t* out) {
     if (!out || tiles < 0 || workers < 1) return DRGG_EINVAL;
     const TailSplit t = tailsplit_units(tiles, workers);
@@ -680,6 +698,14 @@ drgg_status drgg_set_knob(int knob, int64_t value) {
             return DRGG_OK;
         case DRGG_KNOB_CHECK_WORKSPACE:
             g_knob_check_ws.store(value != 0);
+            return DRGG_OK;
+        case DRGG_KNOB_DELAY_SEED:
+            if (value < 0 || value > INT32_MAX) return DRGG_EINVAL;
+            g_knob_delay.store(value);
+            return DRGG_OK;
+        case DRGG_KNOB_SPLIT_REPORT:
+            if (value < 0 || (value & 15) != 0) return DRGG_EINVAL;
+            g_knob_report.store(value);
             return DRGG_OK;
         default:
             return DRGG_EINVAL;

@@ -32,6 +32,8 @@ struct GemmArgs {
     int64_t items_max;     // workgroups launched (fwd/dgrad/det wgrad)
     int32_t E;
     int32_t reverse;       // walk work items in reverse (test knob)
+    int32_t delay_seed;    // split program: seeded delays before tail arrivals (test knob; 0 = off)
+    int32_t* report;       // split program: if set, workgroup 0 writes its tail decision here (test aid)
 };
 
 // op 0: forward; 1: data gradient; 2: data gradient with a.B = W^T [E][K][N]

@@ -282,29 +282,31 @@ __device__ __forceinline__ int32_t chunks_dev(int32_t T, int64_t chunk_max) {
     return l ? (T + l - 1) / l : 0;
 }
 
-// Estimated time of a planned walk on the kRuleCUs reference workgroups: the
-// items 0 .. prefix[npos]-1 handed out in snake rounds, as the persistent
-// kernels hand them out, each costing len(its position) plus
-// kItemOverheadTokens tokens; returns the largest per-workgroup load.  It
-// chooses between the two plans of the deterministic weight gradient and is
-// a function of the plan only, never of the device.  `red` is an LDS word.
-// Must be called by all threads (at least kRuleCUs of them); ends with a
-// barrier.
+// Estimated time of a planned walk on `workers` workgroups: the items
+// 0 .. prefix[npos]-1 handed out in snake rounds, as the persistent kernels
+// hand them out, each costing len(its position) plus kItemOverheadTokens
+// tokens; returns the largest per-workgroup load.  The deterministic weight
+// gradient chooses between its two plans with it on kRuleCUs reference
+// workgroups (a function of the plan only, never of the device); the split
+// program on its live grid.  `red` is an LDS word.  Must be called by all
+// threads; ends with a barrier.
 template <class LenFn>
-__device__ uint64_t walk_makespan(const Sched& s, int npos, LenFn len, unsigned long long* red) {
+__device__ uint64_t walk_makespan(const Sched& s, int npos, LenFn len, unsigned long long* red,
+                                  int64_t workers = kRuleCUs) {
     if (threadIdx.x == 0) *red = 0;
     __syncthreads();
     const int64_t total = s.prefix[npos];
-    if (threadIdx.x < kRuleCUs) {
-        const int64_t b = threadIdx.x;
+    uint64_t worst = 0;
+    for (int64_t b = threadIdx.x; b < workers; b += blockDim.x) {
         uint64_t load = 0;
         for (int64_t r = 0;; ++r) {
-            const int64_t i = snake_item(r, b, kRuleCUs);
+            const int64_t i = snake_item(r, b, workers);
             if (i >= total) break;   // later rounds hold only larger indices
             load += (uint64_t)len(find_expert(s, npos, (int32_t)i)) + (uint64_t)kItemOverheadTokens;
         }
-        atomicMax(red, (unsigned long long)load);
+        worst = load > worst ? load : worst;
     }
+    atomicMax(red, (unsigned long long)worst);
     __syncthreads();
     const uint64_t m = *red;
     __syncthreads();
@@ -947,7 +949,11 @@ struct TileRunner {
         return (t.A.klen + kStageK - 1) / kStageK;
     }
     // steps run for a tile of n stages: whole groups of kStages (the stages
-    // past n load zeros), at least the peeled group
+    // past n load zeros), at least the peeled group.  The next tile is
+    // decoded inside a group's steps, so every tile must have at least one
+    // reduction value: a tile of none would never hand over to the next one
+    // (the callers' walks hold no item of zero length).  Forcing a group
+    // here instead makes the compiler spill the 4-wave kernels' accumulators.
     static __device__ __forceinline__ int round4(int n) {
         const int r = (n + kStages - 1) & ~(kStages - 1);
         return kPeel && r < kStages ? kStages : r;
@@ -1361,7 +1367,8 @@ __global__ __launch_bounds__((64 * wgrad_det_waves<BM, BN>())) void gg_wgrad_det
         }();
         position_prefix(sch, stg.b[0], 2 * E, [&](int q) {
             const int32_t T = T_at(q < E ? q : q - E), S = chunks_dev(T, cmax);
-            if (S <= 1) return q < E ? 0 : P0;
+            if (S == 0) return 0;                // no tokens: no items
+            if (S == 1) return q < E ? 0 : P0;
             const int32_t w0 = bands(T) * tk0;   // whole reference tiles
             return q < E ? w0 : (P0 - w0) * S;
         });
@@ -1387,8 +1394,8 @@ __global__ __launch_bounds__((64 * wgrad_det_waves<BM, BN>())) void gg_wgrad_det
     const int npos = tail ? 2 * E : E;
     position_prefix(sch, stg.b[0], npos, [&](int q) {
         const int32_t T = T_at(q < E ? q : q - E), S = chunks_dev(T, cmax);
-        if (!tail) return P * S;
-        if (S <= 1) return q < E ? 0 : P;
+        if (!tail || S == 0) return P * S;   // (no tokens: no items)
+        if (S == 1) return q < E ? 0 : P;
         const int32_t nw = nwhole(T);
         return q < E ? nw : (P - nw) * S;
     });
@@ -1526,10 +1533,11 @@ __global__ __launch_bounds__(kThreads) void gg_wgrad_fold_kernel(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// non-deterministic weight gradient: the deterministic kernel's chunk-major
-// items, with token chunks of whole 512-token units; the partials of an
-// expert cut into several chunks are added into an FP32 tile sum by atomics,
-// and a per-tile ticket picks the last arrival, which writes the tile
+// non-deterministic weight gradient: whole tiles in full waves, the tail
+// either placed whole on the least-loaded workgroups or cut into chunks of
+// whole 512-token units whose partials are added into an FP32 tile sum by
+// atomics, a per-tile ticket picking the last arrival, which writes the tile
+// (flashinfer PR #8258, Summary)
 
 // the deterministic chunk length rounded up to whole 512-token units
 __device__ __forceinline__ int32_t unit_chunk_len(int32_t T, int64_t chunk_max) {
@@ -1541,47 +1549,266 @@ __device__ __forceinline__ int32_t unit_chunks(int32_t T, int64_t chunk_max) {
     return l ? (T + l - 1) / l : 0;
 }
 
+// Test aid (DRGG_KNOB_DELAY_SEED): a bounded sleep, a different length for
+// every (seed, workgroup, tile, expert), before a tail piece adds its
+// partial (the pieces of a tile run on different workgroups), so that the
+// arrivals at a tile's ticket come in other orders.  At most 47 x 16 x 64
+// cycles.
+__device__ __forceinline__ void arrival_delay(int32_t seed, int32_t tile, int32_t expert) {
+    uint32_t h = (uint32_t)seed * 2654435761u ^ (uint32_t)blockIdx.x * 40503u ^ (uint32_t)tile * 977u ^
+                 (uint32_t)expert * 131u;
+    h ^= h >> 15;
+    h *= 2246822519u;
+    h ^= h >> 13;
+    const int n = (int)(h % 48u);
+    for (int i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(16);
+}
+
+// Walks (experts in decreasing order of unit chunk length).  Banded walk:
+// position p < E holds the whole tiles of the p-th expert (split_whole_rows:
+// full waves on its share of the grid; all of an expert not cut into
+// chunks), position E + p its tail tiles, whole (slack placement) or as chunk
+// items.  All-split walk: position p holds every tile of the p-th expert,
+// as chunk items if it is cut into chunks.  Like the deterministic program,
+// the kernel estimates both walks (walk_makespan, here on the live grid) and
+// runs the banded one when it is not slower: with ragged experts, whole
+// tiles of different lengths balance worse than chunk items.  With more
+// than kTailPlanMaxExperts experts only the all-split walk exists.
+//
+// Slack placement: at the start every workgroup computes the load of every
+// workgroup from the first pass (the whole tiles, in snake rounds over the
+// grid), ranks them and checks whether the i-th tail tile fits whole on the
+// i-th least-loaded workgroup within the largest load plus one tail share
+// (a chunk of that expert).  All the workgroups reach the same answer; if
+// every tail tile fits, the workgroup of rank i runs tail tile i whole after
+// its first pass, otherwise the tail runs as chunk items after the first
+// pass.  (The pages rank the clusters while the first tiles run; here the
+// ranking is recomputed by every workgroup from the plan, so no workgroup
+// waits for another.)
 template <int BM, int BN, bool OUT_BF16>
 __global__ __launch_bounds__(kGemmThreads) void gg_wgrad_atomic_kernel(GemmArgs a) {
     DRGG_STAGES(BM, BN, false, false, stg);
     __shared__ Sched sch;
+    __shared__ int32_t nw_tab[kMaxExperts];   // whole tiles of each expert (the decode reads it)
     __shared__ int32_t s_last;
+    __shared__ int32_t s_rank;
+    __shared__ unsigned long long s_red, s_min;
     const int32_t tn = (int32_t)((a.N + BM - 1) / BM), tk = (int32_t)((a.K + BN - 1) / BN);
     const int32_t P = tn * tk;
     const int64_t cmax = a.chunk_max;
-    build_schedule(sch, a.offs, a.E, a.M, a.T, [=](int, int32_t T) { return P * unit_chunks(T, cmax); });
-    order_longest_first(sch, stg.b[0], a.E, [=](int32_t T) { return unit_chunk_len(T, cmax); },
-                        [=](int32_t T) { return P * unit_chunks(T, cmax); });
-    const int64_t total = uni(sch.prefix[a.E]);
+    const int E = a.E;
     const int64_t G = gridDim.x;
-    const int64_t b = blockIdx.x;
-    int64_t wb = xcd_remap(blockIdx.x, G), round = 0;
-    if (a.reverse) wb = G - 1 - wb;
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    build_schedule(sch, a.offs, E, a.M, a.T, [=](int, int32_t) { return 0; });
+    rank_experts(sch, stg.b[0], E, [=](int32_t T) { return unit_chunk_len(T, cmax); });
+    auto T_at = [&](int q) { const int e = expert_at(sch, q); return sch.offs[e + 1] - sch.offs[e]; };
+    const bool banded = E <= kTailPlanMaxExperts;
+    // whole tiles of each expert: a prefix of its row-major tiles (none for
+    // an expert without tokens, which has no items at all); computed once,
+    // so that the per-tile decode is a table read
+    for (int e = tid; e < E; e += nthr) {
+        const int32_t T = sch.offs[e + 1] - sch.offs[e], S = unit_chunks(T, cmax);
+        int32_t nw = 0;
+        if (S == 1) nw = P;
+        else if (S > 1 && banded)
+            nw = (int32_t)min<int64_t>(tn, split_whole_rows(T, a.M, a.N, a.K, S, G) * (256 / BM)) * tk;
+        nw_tab[e] = nw;
+    }
+    __syncthreads();
+    auto nw_at = [&](int q) { return nw_tab[expert_at(sch, q)]; };
+    const int64_t wb0 = a.reverse ? G - 1 - xcd_remap(blockIdx.x, G) : xcd_remap(blockIdx.x, G);
+    auto S_at = [&](int q) { return unit_chunks(T_at(q), cmax); };
+    auto L_at = [&](int q) { return unit_chunk_len(T_at(q), cmax); };
+    // the all-split walk: every tile of an expert cut into chunks as chunk
+    // items, the others whole (one position per expert)
+    auto split_walk = [&] {
+        position_prefix(sch, stg.b[0], E, [&](int q) {
+            const int32_t S = S_at(q);
+            return S > 1 ? P * S : S == 1 ? P : 0;
+        });
+    };
+    // the banded walk with its tail as chunk items
+    auto band_walk = [&] {
+        position_prefix(sch, stg.b[0], 2 * E, [&](int q) {
+            const int qe = q < E ? q : q - E;
+            const int32_t T = T_at(qe), nw = nw_at(qe);
+            return T == 0 ? 0 : q < E ? nw : (P - nw) * unit_chunks(T, cmax);
+        });
+    };
+    int use_band = 0, slack = 0;
+    int64_t total1 = 0, ntail = 0;
+    if (banded) {
+        // the banded walk's first pass (whole tiles) and its tail tile counts
+        position_prefix(sch, stg.b[0], 2 * E, [&](int q) {
+            const int qe = q < E ? q : q - E;
+            const int32_t T = T_at(qe), nw = nw_at(qe);
+            return T == 0 ? 0 : q < E ? nw : P - nw;
+        });
+        total1 = sch.prefix[E];
+        ntail = sch.prefix[2 * E] - total1;
+        // with no whole tiles the banded walk is the all-split walk
+        if (total1 > 0) {
+            // every workgroup's load from the first pass
+            const bool rank = ntail > 0 && ntail <= G && G <= kSlackMaxGrid;
+            auto* load = reinterpret_cast<__attribute__((address_space(3))) uint64_t*>(stg.b[1]);
+            auto* sorted = reinterpret_cast<__attribute__((address_space(3))) uint64_t*>(stg.b[2]);
+            if (tid == 0) {
+                s_red = 0;
+                s_min = ~0ull;
+            }
+            __syncthreads();
+            uint64_t hi = 0, lo = ~0ull;
+            for (int64_t b = tid; b < G; b += nthr) {
+                uint64_t l = 0;
+                for (int64_t r = 0;; ++r) {
+                    const int64_t i = snake_item(r, b, G);
+                    if (i >= total1) break;   // later rounds hold only larger indices
+                    l += (uint64_t)T_at(find_expert(sch, E, (int32_t)i)) + (uint64_t)kItemOverheadTokens;
+                }
+                if (rank) load[b] = l;
+                hi = l > hi ? l : hi;
+                lo = l < lo ? l : lo;
+            }
+            atomicMax(&s_red, (unsigned long long)hi);
+            atomicMin(&s_min, (unsigned long long)lo);
+            __syncthreads();
+            const uint64_t lmax = s_red, lmin = s_min;
+            // slack placement needs at least the longest tail tile to fit
+            // whole on the least-loaded workgroup; only then rank them all
+            const int32_t T0 = ntail > 0 ? T_at(find_expert(sch, 2 * E, (int32_t)total1) - E) : 0;
+            if (rank && lmin + (uint64_t)T0 <= lmax + (uint64_t)unit_chunk_len(T0, cmax)) {
+                for (int64_t b = tid; b < G; b += nthr) {
+                    const uint64_t lb = load[b];
+                    int64_t r = 0;
+                    for (int64_t c = 0; c < G; ++c) r += load[c] < lb || (load[c] == lb && c < b);
+                    sorted[r] = lb;
+                    if (b == wb0) s_rank = (int32_t)r;
+                }
+                __syncthreads();
+                int fits = 1;
+                uint64_t top = 0;   // the placed tail's largest load
+                for (int64_t i = tid; i < ntail; i += nthr) {
+                    const int32_t T = T_at(find_expert(sch, 2 * E, (int32_t)(total1 + i)) - E);
+                    fits &= sorted[i] + (uint64_t)T <= lmax + (uint64_t)unit_chunk_len(T, cmax);
+                    const uint64_t t = sorted[i] + (uint64_t)T + (uint64_t)kItemOverheadTokens;
+                    top = t > top ? t : top;
+                }
+                slack = __syncthreads_and(fits);
+                if (slack) {
+                    if (tid == 0) s_red = lmax;
+                    __syncthreads();
+                    atomicMax(&s_red, (unsigned long long)top);
+                    __syncthreads();
+                }
+            }
+            // estimated times of the banded walk (slack placement, or its
+            // tail as chunk items) and of the all-split walk; without slack
+            // placement and with no expert cut into chunks keeping whole
+            // tiles, both walks hold the same items and the all-split one
+            // runs
+            int keeps = 0;
+            for (int q = tid; q < E; q += nthr) keeps |= S_at(q) > 1 && nw_at(q) > 0;
+            if (__syncthreads_or(keeps) || slack) {
+                uint64_t mk_band;
+                if (slack) {
+                    mk_band = s_red;
+                    __syncthreads();
+                } else {
+                    band_walk();
+                    mk_band = walk_makespan(sch, 2 * E, [&](int q) { return q < E ? T_at(q) : L_at(q - E); }, &s_red,
+                                            G);
+                }
+                split_walk();
+                const uint64_t mk_split = walk_makespan(sch, E, [&](int q) {
+                    return S_at(q) > 1 ? L_at(q) : T_at(q);
+                }, &s_red, G);
+                use_band = mk_band <= mk_split;
+            }
+            slack = slack && use_band;
+        }
+    }
+    if (a.report && blockIdx.x == 0 && tid == 0) {
+        a.report[0] = slack;
+        a.report[1] = (int32_t)ntail;
+        a.report[2] = use_band;
+        a.report[3] = (int32_t)G;
+    }
+    // the walk that runs: first pass and placed tail; first pass and chunked
+    // tail; or all split
+    int npos = E;
+    if (use_band) {
+        npos = 2 * E;
+        if (slack) {
+            position_prefix(sch, stg.b[0], 2 * E, [&](int q) {
+                const int qe = q < E ? q : q - E;
+                const int32_t T = T_at(qe), nw = nw_at(qe);
+                return T == 0 ? 0 : q < E ? nw : P - nw;
+            });
+        } else {
+            band_walk();
+        }
+    } else {
+        split_walk();
+    }
+    const int64_t total = uni(sch.prefix[npos]);
+    const int64_t wb = wb0;
+    int64_t round = 0;
     int64_t w = snake_item(0, wb, G);
-    auto more = [&]() { return w < total; };
+    // with slack placement the walk ends with this workgroup's tail tile
+    slack = uni(slack);
+    use_band = uni(use_band);
+    total1 = uni((int32_t)total1);
+    const int64_t first_end = slack ? total1 : total;
+    const int64_t tail_item = slack && uni(s_rank) < total - total1 ? total1 + uni(s_rank) : -1;
+    bool tail_done = tail_item < 0;
+    auto more = [&]() {
+        if (w < first_end) return true;
+        if (!tail_done) {
+            w = tail_item;
+            tail_done = true;
+            return true;
+        }
+        return false;
+    };
     auto next = [&](TileInfo& t) {
-        const int pos = uni(find_expert(sch, a.E, (int32_t)w));
-        const int e = uni(expert_at(sch, pos));
+        const int pos = uni(find_expert(sch, npos, (int32_t)w));
+        const int e = uni(expert_at(sch, pos < E ? pos : pos - E));
         const int32_t oe = uni(sch.offs[e]), oe1 = uni(sch.offs[e + 1]);
         const int32_t T = oe1 - oe;
         const int32_t clen = unit_chunk_len(T, cmax);
         const int32_t nch = (T + clen - 1) / clen;
         const int32_t local = (int32_t)w - uni(sch.prefix[pos]);
-        const int32_t chunk = local / P, tile = local % P;   // chunk-major: tiles of a chunk adjacent
+        int32_t tile, chunk = 0;
+        bool whole;
+        if (use_band && pos < E) {                // first pass: a whole tile
+            tile = local;
+            whole = true;
+        } else if (use_band && slack) {          // a tail tile placed whole
+            tile = uni(nw_tab[e]) + local;
+            whole = true;
+        } else if (nch > 1) {                    // a chunk item (of the tail, or of every tile)
+            const int32_t nw = use_band ? uni(nw_tab[e]) : 0, ps = P - nw;
+            chunk = local / ps;
+            tile = nw + local % ps;
+            whole = false;
+        } else {
+            tile = local;
+            whole = true;
+        }
         const int32_t ti = tile / tk, tj = tile % tk;
         const int64_t n0 = (int64_t)ti * BM, k0 = (int64_t)tj * BN;
-        const int64_t tb = oe + (int64_t)chunk * clen;
-        const int32_t len = (int32_t)min<int64_t>(clen, oe1 - tb);
+        const int64_t tb = oe + (whole ? 0 : (int64_t)chunk * clen);
+        const int32_t len = whole ? T : (int32_t)min<int64_t>(clen, oe1 - tb);
         t.o0 = n0;
         t.o1 = k0;
         t.rows = (int32_t)min<int64_t>(BM, a.N - n0);
         t.cols = (int32_t)min<int64_t>(BN, a.K - k0);
         t.e = e;
-        t.aux = nch == 1 ? -1 : tile;   // -1: the whole tile in this item, store directly
-        t.aux2 = nch;                   // pieces of a split tile
+        t.aux = whole ? -1 : tile;   // -1: the whole tile in this item, store directly
+        t.aux2 = nch;                // pieces of a split tile
         t.A = Operand{a.A + tb * a.a_rs + e * a.a_gs + n0, a.a_rs, t.rows, len};
         t.B = Operand{a.B + tb * a.b_rs + e * a.b_gs + k0, a.b_rs, t.cols, len};
-        w = snake_item(++round, wb, G);
+        w = w < first_end ? snake_item(++round, wb, G) : first_end;
     };
     auto finish = [&](const TileInfo& t, const TileMma<BM, BN, false, false>& mma) {
         const int64_t base = (int64_t)t.e * a.N * a.K + t.o0 * a.K + t.o1;
@@ -1592,6 +1819,7 @@ __global__ __launch_bounds__(kGemmThreads) void gg_wgrad_atomic_kernel(GemmArgs 
             store_tile<OUT_BF16>(mma, ob, a.K, t.rows, t.cols);
             return;
         }
+        if (a.delay_seed) arrival_delay(a.delay_seed, t.aux, t.e);
         const int64_t slot = (int64_t)t.e * P + t.aux;
         float* ts = a.tilesum + slot * (BM * BN);
         const uint32_t parts = (uint32_t)t.aux2;
@@ -1633,7 +1861,8 @@ __global__ __launch_bounds__(kGemmThreads) void gg_wgrad_atomic_kernel(GemmArgs 
     runner.run(more, next, finish);
     // experts without tokens: dW[e] = +0, shared out over the grid
     const int64_t nk = a.N * a.K;
-    for (int e = 0; e < a.E; ++e) {
+    const int64_t b = blockIdx.x;
+    for (int e = 0; e < E; ++e) {
         if (sch.offs[e + 1] != sch.offs[e]) continue;
         for (int64_t i = (b * kGemmThreads + threadIdx.x) * 8; i < nk; i += (int64_t)gridDim.x * kGemmThreads * 8) {
             const int64_t o = (int64_t)e * nk + i;

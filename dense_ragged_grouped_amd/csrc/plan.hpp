@@ -125,19 +125,64 @@ inline int64_t wgrad_chunk_max(int32_t E, int64_t M, int64_t N, int64_t K) {
 // that run as whole tiles: all of them (ceil(N / 256)) when S <= 1.  A pure
 // function of the problem, never of the device; the result does not depend
 // on the kernel's tile shape either (its tiles nest in the 256-row bands).
-DRGG_HD inline int64_t wgrad_whole_rows(int64_t T, int64_t M, int64_t N, int64_t K, int64_t S) {
+// (The split program uses the same rule on the live grid: `workers`.)
+DRGG_HD inline int64_t wgrad_whole_rows(int64_t T, int64_t M, int64_t N, int64_t K, int64_t S,
+                                        int64_t workers = kRuleCUs) {
     const int64_t tn0 = ceil_div(N, 256), tk0 = ceil_div(K, 256);
-    if (S <= 1 || T <= 0 || M <= 0) return tn0;
-    const int64_t F = (tn0 * tk0 * M) / (kRuleCUs * T);
-    const int64_t full = (F * kRuleCUs * T) / M;
+    if (S <= 1 || T <= 0 || M <= 0 || workers <= 0) return tn0;
+    const int64_t F = (tn0 * tk0 * M) / (workers * T);
+    const int64_t full = (F * workers * T) / M;
     const int64_t h = full / tk0;
     return h < tn0 ? h : tn0;
 }
+
+// The non-deterministic split program's whole bands: full waves on the
+// expert's share of the live grid (`workers` persistent workgroups), as
+// wgrad_whole_rows, and then the tail-split rule below (tailsplit_units) on
+// that share: the tail tiles are cut into chunks only when twice their
+// number fits in the share, R_e = workers * T / M (2 * tail <= R_e);
+// otherwise every tile of the expert stays whole (returns all bands).
+DRGG_HD inline int64_t split_whole_rows(int64_t T, int64_t M, int64_t N, int64_t K, int64_t S, int64_t workers) {
+    const int64_t tn0 = ceil_div(N, 256), tk0 = ceil_div(K, 256);
+    const int64_t h = wgrad_whole_rows(T, M, N, K, S, workers);
+    if (h >= tn0) return tn0;
+    const int64_t tail = (tn0 - h) * tk0;
+    return 2 * tail * M <= workers * T ? h : tn0;
+}
+
+// The split program's token unit: its chunks are the deterministic chunk
+// lengths rounded up to whole kStreamKUnit-token units.
+DRGG_HD inline void split_chunking(int64_t T, int64_t chunk_max, int64_t* len, int64_t* chunks) {
+    int64_t l, c;
+    wgrad_chunking(T, chunk_max, &l, &c);
+    l = round_up(l, kStreamKUnit);
+    *len = T > 0 ? l : 0;
+    *chunks = T > 0 ? ceil_div(T, l) : 0;
+}
+
+// Slack placement of the split program's tail needs every workgroup's load
+// at kernel start; grids above this size skip it (the tail is split).
+constexpr int64_t kSlackMaxGrid = 1024;
 
 // Experts above this count always run the all-split plan: the tail-only
 // plan's walk has two positions per expert (whole tiles first, then the
 // chunks), and the kernels' schedule tables hold kMaxExperts + 1 entries.
 constexpr int kTailPlanMaxExperts = kMaxExperts / 2;
+
+// Estimated time of a walk (host mirror of the kernels' walk_makespan):
+// position q holds work[q] items of len[q] tokens each, handed out in snake
+// rounds over `workers` workgroups; every item costs len + kItemOverheadTokens.
+inline uint64_t walk_makespan_host(const std::vector<int64_t>& work, const std::vector<int64_t>& len,
+                                   int64_t workers) {
+    std::vector<uint64_t> load(workers, 0);
+    int64_t i = 0;
+    for (size_t q = 0; q < work.size(); ++q)
+        for (int64_t j = 0; j < work[q]; ++j, ++i) {
+            const int64_t r = i / workers, b = i % workers;
+            load[(r & 1) ? workers - 1 - b : b] += (uint64_t)(len[q] + kItemOverheadTokens);
+        }
+    return *std::max_element(load.begin(), load.end());
+}
 
 // Host mirror of the deterministic weight gradient's plan choice, which the
 // chunk kernel makes on the device from the group offsets (same integer
@@ -172,16 +217,7 @@ inline bool wgrad_tail_plan(const int32_t* offs, int32_t E, int64_t N, int64_t K
     for (int32_t e = 0; e < E; ++e) perm[e] = e;
     std::stable_sort(perm.begin(), perm.end(), [&](int32_t x, int32_t y) { return L[x] > L[y]; });
     const int64_t tk0 = ceil_div(K, 256), P0 = ceil_div(N, 256) * tk0;
-    auto makespan = [&](const std::vector<int64_t>& work, const std::vector<int64_t>& len) {
-        std::vector<uint64_t> load(kRuleCUs, 0);
-        int64_t i = 0;
-        for (size_t q = 0; q < work.size(); ++q)
-            for (int64_t j = 0; j < work[q]; ++j, ++i) {
-                const int64_t r = i / kRuleCUs, b = i % kRuleCUs;
-                load[(r & 1) ? kRuleCUs - 1 - b : b] += (uint64_t)(len[q] + kItemOverheadTokens);
-            }
-        return *std::max_element(load.begin(), load.end());
-    };
+
     std::vector<int64_t> w1(E), l1(E), w2(2 * E), l2(2 * E);
     int64_t whole_tiles = 0;
     for (int32_t q = 0; q < E; ++q) {
@@ -192,13 +228,101 @@ inline bool wgrad_tail_plan(const int32_t* offs, int32_t E, int64_t N, int64_t K
         whole_tiles += w0;
         w2[q] = w0;
         l2[q] = T[e];
-        w2[E + q] = S[e] > 1 ? (P0 - w0) * S[e] : P0;
+        w2[E + q] = S[e] > 1 ? (P0 - w0) * S[e] : S[e] == 1 ? P0 : 0;   // no tokens: no items
         l2[E + q] = S[e] > 1 ? L[e] : T[e];
     }
-    const bool tail = whole_tiles > 0 && makespan(w2, l2) <= makespan(w1, l1);
+    const bool tail = whole_tiles > 0 && walk_makespan_host(w2, l2, kRuleCUs) <= walk_makespan_host(w1, l1, kRuleCUs);
     for (int32_t e = 0; e < E && row0 && tail; ++e)
         row0[e] = S[e] > 1 ? (int32_t)std::min<int64_t>(N, band[e] * 256) : 0;
     return tail;
+}
+
+// Host mirror of the split program's choice for a grid of G workgroups and
+// kernel tiles of bm x bn (the kernel makes it on the device; same
+// arithmetic).  Experts in decreasing order of chunk length.  Banded walk:
+// a first pass of every expert's whole tiles (split_whole_rows; all of an
+// expert not cut into chunks) in snake rounds over the G workgroups, each
+// item its token count plus kItemOverheadTokens, then the tail tiles.  Slack
+// placement (flashinfer PR #8258, Summary): the workgroups are ranked by
+// their first-pass load; if there are at most G tail tiles and the i-th tail
+// tile (in walk order) fits whole on the i-th least-loaded workgroup without
+// taking it beyond the largest load plus one tail share (one chunk of that
+// expert), every tail tile runs whole there (no tile sum, no ticket);
+// otherwise the tail runs as chunk items.  The banded walk runs if its
+// estimated time is not above the all-split walk's (every tile of an expert
+// cut into chunks as chunk items); without slack placement and with no
+// expert cut into chunks keeping whole tiles both walks hold the same items
+// and the all-split one runs.  Returns true for the slack placement;
+// out[0] = tail tiles, out[1] = 1 if the banded walk runs.  For tests only.
+inline bool wgrad_split_plan(const int32_t* offs, int32_t E, int64_t N, int64_t K, int bm, int bn, int64_t G,
+                             int64_t* out) {
+    out[0] = out[1] = 0;
+    if (E < 1 || G < 1) return false;
+    const int64_t M = offs[E];
+    if (M <= 0) return false;
+    const int64_t cmax = wgrad_chunk_max(E, M, N, K);
+    const int64_t tn = ceil_div(N, bm), tk = ceil_div(K, bn), P = tn * tk;
+    const bool banded = E <= kTailPlanMaxExperts;
+    std::vector<int64_t> T(E), L(E), S(E), nw(E);
+    for (int32_t e = 0; e < E; ++e) {
+        T[e] = (int64_t)offs[e + 1] - offs[e];
+        split_chunking(T[e], cmax, &L[e], &S[e]);
+        if (S[e] == 0) nw[e] = 0;   // no tokens: no items
+        else if (S[e] == 1) nw[e] = P;
+        else if (!banded) nw[e] = 0;
+        else nw[e] = std::min<int64_t>(tn, split_whole_rows(T[e], M, N, K, S[e], G) * (256 / bm)) * tk;
+    }
+    std::vector<int32_t> perm(E);
+    for (int32_t e = 0; e < E; ++e) perm[e] = e;
+    std::stable_sort(perm.begin(), perm.end(), [&](int32_t x, int32_t y) { return L[x] > L[y]; });
+    if (!banded) return false;
+    std::vector<int64_t> w1(E), l1(E), wb(2 * E), lb(2 * E), ws(E), ls(E), tail_T, tail_L;
+    int64_t total1 = 0;
+    for (int32_t q = 0; q < E; ++q) {
+        const int32_t e = perm[q];
+        w1[q] = T[e] > 0 ? nw[e] : 0;
+        l1[q] = T[e];
+        total1 += w1[q];
+        wb[q] = w1[q];
+        lb[q] = T[e];
+        wb[E + q] = T[e] > 0 ? (P - nw[e]) * S[e] : 0;
+        lb[E + q] = L[e];
+        ws[q] = S[e] > 1 ? P * S[e] : S[e] == 1 ? P : 0;
+        ls[q] = S[e] > 1 ? L[e] : T[e];
+        for (int64_t j = nw[e]; j < P && T[e] > 0; ++j) {
+            tail_T.push_back(T[e]);
+            tail_L.push_back(L[e]);
+        }
+    }
+    const int64_t ntail = (int64_t)tail_T.size();
+    out[0] = ntail;
+    if (total1 == 0) return false;   // the banded walk is the all-split walk
+    std::vector<uint64_t> load(G, 0);
+    for (int64_t i = 0, q = 0, j = 0; i < total1; ++i, ++j) {
+        while (j >= w1[q]) { ++q; j = 0; }
+        const int64_t r = i / G, b = i % G;
+        load[(r & 1) ? G - 1 - b : b] += (uint64_t)(l1[q] + kItemOverheadTokens);
+    }
+    const uint64_t lmax = *std::max_element(load.begin(), load.end());
+    const uint64_t lmin = *std::min_element(load.begin(), load.end());
+    bool slack = false;
+    uint64_t top = lmax;
+    if (ntail > 0 && ntail <= G && G <= kSlackMaxGrid && lmin + (uint64_t)tail_T[0] <= lmax + (uint64_t)tail_L[0]) {
+        std::vector<uint64_t> sorted = load;
+        std::sort(sorted.begin(), sorted.end());
+        slack = true;
+        for (int64_t t = 0; t < ntail; ++t) {
+            if (sorted[t] + (uint64_t)tail_T[t] > lmax + (uint64_t)tail_L[t]) slack = false;
+            top = std::max<uint64_t>(top, sorted[t] + (uint64_t)tail_T[t] + kItemOverheadTokens);
+        }
+    }
+    bool keeps = false;   // an expert cut into chunks keeps whole tiles
+    for (int32_t e = 0; e < E; ++e) keeps = keeps || (S[e] > 1 && nw[e] > 0);
+    if (!keeps && !slack) return false;   // both walks hold the same items: the all-split one runs
+    const uint64_t mk_band = slack ? top : walk_makespan_host(wb, lb, G);
+    const bool use_band = mk_band <= walk_makespan_host(ws, ls, G);
+    out[1] = use_band;
+    return slack && use_band;
 }
 
 // Partial slots the deterministic weight gradient may need: only experts cut

@@ -305,10 +305,19 @@ drgg_status drgg_wgrad_chunking(int64_t T, int64_t chunk_max, int64_t *chunk_len
  *                         above (0 = as the environment says)
  *   DRGG_KNOB_CHECK_WORKSPACE  1 = the split program's zero-workspace check
  *                         (0 = as the environment says)
+ *   DRGG_KNOB_DELAY_SEED  n > 0: the split program's tail pieces sleep a
+ *                         bounded, seeded time (under 50 000 cycles) before
+ *                         adding their partial, so that the arrivals at a
+ *                         tile's ticket come in other orders (race testing)
+ *   DRGG_KNOB_SPLIT_REPORT  a 16-byte aligned DEVICE address of four int32
+ *                         where the split program writes {slack placement
+ *                         taken (0/1), tail tiles of the banded walk, banded
+ *                         walk taken (0/1), grid}; 0 = off
  * None of them changes the arithmetic of the deterministic variant.
  */
 enum { DRGG_KNOB_TILE = 1, DRGG_KNOB_GRID = 2, DRGG_KNOB_REVERSE = 3, DRGG_KNOB_TIMING = 4,
-       DRGG_KNOB_NONDET = 5, DRGG_KNOB_CHECK_OFFSETS = 6, DRGG_KNOB_CHECK_WORKSPACE = 7 };
+       DRGG_KNOB_NONDET = 5, DRGG_KNOB_CHECK_OFFSETS = 6, DRGG_KNOB_CHECK_WORKSPACE = 7,
+       DRGG_KNOB_DELAY_SEED = 8, DRGG_KNOB_SPLIT_REPORT = 9 };
 drgg_status drgg_set_knob(int knob, int64_t value);
 
 /*
@@ -366,6 +375,29 @@ drgg_status drgg_timing_read(int i, const char **kernel, float *ms);
  */
 drgg_status drgg_wgrad_tail_plan(const int32_t *group_offsets, int32_t E, int64_t N, int64_t K,
                                  int *tail_only, int32_t *row0);
+
+/*
+ * The split program's walk (HOST only; group_offsets is a HOST array
+ * [E + 1]; the kernel makes the same choice on the device) for a grid of
+ * `grid` workgroups and the output tile `tile` (a DRGG_KNOB_TILE value, 0 =
+ * the default).  Banded walk: each expert's whole tiles first, in full
+ * waves on its share of the grid, then its remaining tiles, the tail, either
+ * whole or cut into chunks of 512-token units (an expert's tail is cut only
+ * when the tail-split rule of drgg_tailsplit_units allows it on its share).
+ * Slack placement (flashinfer PR #8258, Summary): the workgroups are ranked
+ * by the load of their first-pass tiles, and if the i-th tail tile fits
+ * whole on the i-th least-loaded workgroup for every i (within the largest
+ * load plus one tail share, a chunk of that expert) the whole tail runs that
+ * way, with no tile sums and no tickets.  All-split walk: every tile of an
+ * expert cut into chunks runs as chunk items.  The banded walk runs when its
+ * estimated time on the grid is not above the all-split walk's.  Writes
+ * *slack (HOST) = 1 when the tail is placed whole, *tail_tiles (HOST) = the
+ * number of tail tiles of the banded walk, and *banded_walk (HOST, may be
+ * NULL) = 1 when the banded walk runs.  DRGG_EINVAL for null pointers or bad
+ * arguments.
+ */
+drgg_status drgg_wgrad_split_plan(const int32_t *group_offsets, int32_t E, int64_t N, int64_t K, int tile,
+                                  int64_t grid, int *slack, int64_t *tail_tiles, int *banded_walk);
 
 /*
  * The tail-split rule of a persistent schedule (HOST only; flashinfer

@@ -457,7 +457,7 @@ def _fold_table(drgg, prob, ws):
     return ws[off:off + 16 * prob.E].view(torch.int32).reshape(prob.E, 4).cpu().numpy()
 
 
-@pytest.mark.parametrize("case", ["tail", "zipf_small", "dense"])
+@pytest.mark.parametrize("case", ["tail", "tail_empty", "zipf_small", "dense"])
 def test_wgrad_plan_on_device_matches_host_rule(drgg, case):
     """The chunk kernel writes, for the fold, each expert's token count,
     chunk count and first folded row; that row must be the one the host
@@ -465,6 +465,10 @@ def test_wgrad_plan_on_device_matches_host_rule(drgg, case):
     0), and the result must match the oracle."""
     if case == "tail":
         prob = _tail_problem()
+    elif case == "tail_empty":   # the tail-only plan with an expert without tokens
+        counts = np.full(32, 768)
+        counts[15] = 0
+        prob = synth.make_problem("tail_empty", 344, counts, N=768, K=1024, w_std=0.02)
     elif case == "zipf_small":
         prob = synth.make_problem("zipf_small", 342, synth.zipf_counts(342, 24576, 16, 2), N=768, K=1024,
                                   w_std=0.02)
@@ -477,7 +481,7 @@ def test_wgrad_plan_on_device_matches_host_rule(drgg, case):
                                   workspace=ws)
     torch.cuda.synchronize()
     tail, row0 = drgg.wgrad_tail_plan(prob.offs, prob.N, prob.K)
-    assert tail == (case == "tail")
+    assert tail == case.startswith("tail")
     table = _fold_table(drgg, prob, ws)
     cm = drgg.plan(drgg.OP_WGRAD, prob.E, prob.M, prob.N, prob.K, drgg.FP32, True)["chunk_max"]
     assert table[:, 0].tolist() == prob.counts.tolist()
@@ -513,3 +517,96 @@ def test_tail_plan_bitwise_across_tiles_grids_and_order(drgg, integer):
         idx = np.union1d(parity.sample_indices(prob, "wgrad"), parity.tile_indices(prob, "wgrad"))
         parity.compare(prob, "wgrad", parity.from_dev(out), out_dtype == torch.bfloat16, idx=idx,
                        integer=integer, what=f"tail plan integer={integer}")
+
+
+# ---- the split program's tail: slack placement, chunked tails, arrival orders -----
+
+# 64 skewed experts, 4096 tokens: the tail (18 tiles) fits whole on the
+# least-loaded workgroups, and that walk is the faster one
+SLACK_COUNTS = np.array([30, 6, 0, 96, 126, 18, 28, 16, 288, 1, 2, 72, 7, 1, 1, 332, 25, 0, 7, 871, 12, 8, 23, 14, 1, 16, 15, 9, 2, 2, 5, 4,
+              0, 59, 791, 0, 48, 1, 7, 5, 18, 4, 138, 53, 17, 4, 7, 9, 5, 1, 0, 12, 0, 104, 22, 626, 4, 30, 13, 2, 8, 63, 1, 6])
+
+
+def _report(drgg):
+    rep = torch.zeros(4, dtype=torch.int32, device="cuda")
+    drgg.set_knob(drgg.KNOB_SPLIT_REPORT, rep.data_ptr())
+    return rep
+
+
+@pytest.mark.parametrize("integer", [False, True])
+def test_split_slack_placement(drgg, integer):
+    """A ragged problem whose tail tiles fit whole on the least-loaded
+    workgroups: the kernel reports the slack placement the host rule
+    predicts, the tail runs with no tile sums (the workspace stays zero), and
+    the result is the oracle's (bit for bit on integer inputs, like the
+    deterministic program)."""
+    prob = synth.make_problem("slack", 351, SLACK_COUNTS, N=1536, K=256, w_std=0.02, integer=integer)
+    dv = dev_inputs(prob)
+    slack, tail = drgg.wgrad_split_plan(prob.offs, prob.N, prob.K)
+    assert slack and tail == 18
+    ws = _nondet_ws(drgg, prob, drgg.FP32)
+    rep = _report(drgg)
+    try:
+        out = drgg.grouped_gemm_wgrad(dv["X"], dv["G"], dv["offs"], out_dtype=torch.float32, deterministic=False,
+                                      workspace=ws)
+        torch.cuda.synchronize()
+    finally:
+        drgg.set_knob(drgg.KNOB_SPLIT_REPORT, 0)
+    r = rep.cpu().tolist()
+    assert r[0] == 1 and r[1] == tail and r[2] == 1, r
+    assert int(torch.count_nonzero(ws)) == 0
+    parity.compare(prob, "wgrad", parity.from_dev(out), False, integer=integer, what="slack placement")
+    if integer:
+        assert np.array_equal(bits(out), bits(run_program(drgg, "wgrad", dv, torch.float32, True)))
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3, 4])
+def test_split_tail_arrival_orders(drgg, seed):
+    """The chunked tail of a problem whose tail does not fit whole, with
+    seeded delays before each piece adds its partial (other arrival orders
+    at the tickets): always the oracle's result (bit for bit on integer
+    inputs), the workspace zero again after every call, and the reported
+    decision the host rule's."""
+    for integer in (False, True):
+        prob = synth.make_problem("chunked_tail", 352, np.full(8, 2048), N=1536, K=2048, w_std=0.02,
+                                  integer=integer)
+        dv = dev_inputs(prob)
+        slack, tail, banded = drgg.wgrad_split_plan(prob.offs, prob.N, prob.K, banded=True)
+        assert not slack and tail > 0 and banded
+        ws = _nondet_ws(drgg, prob, drgg.FP32)
+        rep = _report(drgg)
+        drgg.set_knob(drgg.KNOB_DELAY_SEED, seed)
+        try:
+            out = drgg.grouped_gemm_wgrad(dv["X"], dv["G"], dv["offs"], out_dtype=torch.float32,
+                                          deterministic=False, workspace=ws)
+            torch.cuda.synchronize()
+        finally:
+            drgg.set_knob(drgg.KNOB_DELAY_SEED, 0)
+            drgg.set_knob(drgg.KNOB_SPLIT_REPORT, 0)
+        r = rep.cpu().tolist()
+        assert r[0] == 0 and r[1] == tail and r[2] == 1, r
+        assert int(torch.count_nonzero(ws)) == 0
+        idx = np.union1d(parity.sample_indices(prob, "wgrad"), parity.tile_indices(prob, "wgrad"))
+        parity.compare(prob, "wgrad", parity.from_dev(out), False, idx=idx, integer=integer,
+                       what=f"arrival orders seed {seed}")
+
+
+def test_split_program_with_an_expert_without_tokens(drgg):
+    """The split program's walk on a problem with an empty expert (the walk
+    has two positions per expert): the empty expert gets no items and a zero
+    gradient, the others the oracle's result, bit for bit on integers."""
+    counts = np.full(32, 768)
+    counts[15] = 0
+    for integer in (False, True):
+        prob = synth.make_problem("split_empty", 345, counts, N=768, K=1024, w_std=0.02, integer=integer)
+        dv = dev_inputs(prob)
+        ws = _nondet_ws(drgg, prob, drgg.FP32)
+        print(f"split program with an empty expert, integer={integer}", flush=True)
+        out = drgg.grouped_gemm_wgrad(dv["X"], dv["G"], dv["offs"], out_dtype=torch.float32, deterministic=False,
+                                      workspace=ws)
+        torch.cuda.synchronize()
+        assert int(torch.count_nonzero(ws)) == 0
+        assert not np.any(bits(out).reshape(prob.E, prob.N, prob.K)[15])
+        idx = np.union1d(parity.sample_indices(prob, "wgrad"), parity.tile_indices(prob, "wgrad"))
+        parity.compare(prob, "wgrad", parity.from_dev(out), False, idx=idx, integer=integer,
+                       what=f"split program, empty expert, integer={integer}")

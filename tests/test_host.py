@@ -359,3 +359,61 @@ def test_tail_plan_properties(drgg):
     assert drgg.wgrad_tail_plan(_offs(np.full(512, 2048)), 4096, 4096)[0] in (True, False)
     with pytest.raises(drgg.DrggError):
         drgg.wgrad_tail_plan([0], 64, 64)
+
+
+# ---- the split program's tail: whole on the least-loaded workgroups or chunked -----
+
+# E=64 skewed experts, 4096 tokens, N=1536, K=256: the tail (18 tiles of the
+# two longest experts) fits whole on the least-loaded workgroups
+SLACK_COUNTS = [30, 6, 0, 96, 126, 18, 28, 16, 288, 1, 2, 72, 7, 1, 1, 332, 25, 0, 7, 871, 12, 8, 23, 14, 1, 16, 15, 9, 2, 2, 5, 4,
+              0, 59, 791, 0, 48, 1, 7, 5, 18, 4, 138, 53, 17, 4, 7, 9, 5, 1, 0, 12, 0, 104, 22, 626, 4, 30, 13, 2, 8, 63, 1, 6]
+SLACK_CASE = (SLACK_COUNTS, 1536, 256)
+
+
+def test_split_plan_decisions(drgg):
+    import synth
+    slack, tail = drgg.wgrad_split_plan(_offs(np.full(8, 16384)), 1536, 2048)
+    assert (slack, tail) == (False, 128)          # balanced: no workgroup has room for a whole tail tile
+    slack, tail = drgg.wgrad_split_plan(_offs(synth.zipf_counts(4004, 131072, 32, 2)), 2048, 768)
+    assert not slack and tail > 0
+    assert drgg.wgrad_split_plan(_offs([16384]), 512, 4096) == (False, 32)
+    counts, n, k = SLACK_CASE
+    assert drgg.wgrad_split_plan(_offs(counts), n, k, banded=True) == (True, 18, True)
+    # more tail tiles than workgroups, or a grid beyond the ranking's limit: chunked
+    assert drgg.wgrad_split_plan(_offs(counts), n, k, grid=1)[0] is False
+    assert drgg.wgrad_split_plan(_offs(counts), n, k, grid=2000)[0] is False
+    # a few idle workgroups: the all-split walk is faster than placing whole
+    # tail tiles, even where they would fit
+    small = [498, 482, 432, 689, 505, 699, 350, 441]
+    assert drgg.wgrad_split_plan(_offs(small), 256, 256, banded=True) == (False, 2, False)
+    # balanced gate_up: the banded walk with its tail in chunks
+    assert drgg.wgrad_split_plan(_offs(np.full(8, 16384)), 1536, 2048, banded=True) == (False, 128, True)
+
+
+def test_split_plan_slack_only_with_room(drgg):
+    """Slack placement is taken only with at most one tail tile per
+    workgroup, and only on the banded walk."""
+    rng = np.random.default_rng(5)
+    checked = 0
+    for _ in range(600):
+        E = int(rng.choice([8, 16, 32, 64]))
+        M = int(rng.choice([4096, 8192, 16384]))
+        N, K = int(rng.choice([256, 512, 768, 1536])), int(rng.choice([256, 512]))
+        w = rng.lognormal(0, 2.0, E)
+        counts = rng.multinomial(M, w / w.sum())
+        slack, tail, banded = drgg.wgrad_split_plan(_offs(counts), N, K, banded=True)
+        if slack:
+            checked += 1
+            assert banded and 0 < tail <= 256
+    assert checked >= 5
+
+
+def test_plans_give_experts_without_tokens_no_items(drgg):
+    """An expert without tokens has no work items in either plan (a whole
+    tile of zero tokens would be a tile with no reduction steps)."""
+    for pos in (0, 15, 31):
+        counts = [768] * 32
+        counts[pos] = 0
+        assert drgg.wgrad_tail_plan(_offs(counts), 768, 1024)[0] is True
+        # 4 tail tiles (one 256-row band of 4 tiles) for each of the 31 experts with tokens
+        assert drgg.wgrad_split_plan(_offs(counts), 768, 1024, banded=True) == (False, 31 * 4, True)
