@@ -610,3 +610,75 @@ def test_split_program_with_an_expert_without_tokens(drgg):
         idx = np.union1d(parity.sample_indices(prob, "wgrad"), parity.tile_indices(prob, "wgrad"))
         parity.compare(prob, "wgrad", parity.from_dev(out), False, idx=idx, integer=integer,
                        what=f"split program, empty expert, integer={integer}")
+
+
+# ---- HIP graph capture ---------------------------------------------------------------
+
+def test_graph_replays_match_eager(drgg):
+    """The deterministic forward, data gradient (W^T workspace), weight
+    gradient and the weight gradient that allocates nothing, captured into one
+    HIP graph: each of three replays, with eager work and synchronisations
+    between them, gives the eager results bit for bit.  The split program in
+    its own graph: every replay matches the oracle and leaves its workspace
+    zero."""
+    prob = _tail_problem()
+    dv = dev_inputs(prob)
+    small = ragged_problem(*DET_CASE)   # within the fixed array of the call that allocates nothing
+    dvs = dev_inputs(small)
+    f32 = torch.float32
+    Y = torch.empty((prob.M, prob.N), dtype=f32, device="cuda")
+    dX = torch.empty((prob.M, prob.K), dtype=f32, device="cuda")
+    dW = torch.empty((prob.E, prob.N, prob.K), dtype=f32, device="cuda")
+    dW2 = torch.empty((small.E, small.N, small.K), dtype=f32, device="cuda")
+    dW3 = torch.empty_like(dW2)
+    wsd = torch.zeros(drgg.workspace_size(drgg.OP_DGRAD, prob.E, prob.M, prob.N, prob.K, drgg.FP32, True),
+                      dtype=torch.uint8, device="cuda")
+    wsw = torch.zeros(drgg.workspace_size(drgg.OP_WGRAD, prob.E, prob.M, prob.N, prob.K, drgg.FP32, True),
+                      dtype=torch.uint8, device="cuda")
+
+    def programs():
+        drgg.grouped_gemm_fwd(dv["X"], dv["W"], dv["offs"], out_dtype=f32, out=Y)
+        drgg.grouped_gemm_dgrad(dv["G"], dv["W"], dv["offs"], out_dtype=f32, out=dX, workspace=wsd)
+        drgg.grouped_gemm_wgrad(dv["X"], dv["G"], dv["offs"], out_dtype=f32, deterministic=True, out=dW,
+                                workspace=wsw)
+        drgg.grouped_gemm_wgrad_noalloc(dvs["X"], dvs["G"], dvs["offs"], dW2, deterministic=True)
+
+    programs()
+    torch.cuda.synchronize()
+    refs = [bits(t) for t in (Y, dX, dW, dW2)]
+    drgg.grouped_gemm_wgrad(dvs["X"], dvs["G"], dvs["offs"], out_dtype=f32, deterministic=True, out=dW3)
+    torch.cuda.synchronize()
+    assert np.array_equal(refs[3], bits(dW3))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        programs()
+    other = ragged_problem(*DET_CASE)
+    dvo = dev_inputs(other)
+    for i in range(3):
+        for t in (Y, dX, dW, dW2):
+            t.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for t, ref in zip((Y, dX, dW, dW2), refs):
+            assert np.array_equal(bits(t), ref), f"replay {i} differs from the eager result"
+        # eager work between the replays
+        run_program(drgg, "wgrad", dvo, f32, True)
+        torch.cuda.synchronize()
+    # the split program (atomic tile sums) in a graph
+    ws = _nondet_ws(drgg, prob, drgg.FP32)
+    out = torch.empty_like(dW)
+    drgg.grouped_gemm_wgrad(dv["X"], dv["G"], dv["offs"], out_dtype=f32, deterministic=False, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    g2 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g2):
+        drgg.grouped_gemm_wgrad(dv["X"], dv["G"], dv["offs"], out_dtype=f32, deterministic=False, out=out,
+                                workspace=ws)
+    idx = np.union1d(parity.sample_indices(prob, "wgrad"), parity.tile_indices(prob, "wgrad"))
+    for i in range(3):
+        out.fill_(float("nan"))
+        g2.replay()
+        torch.cuda.synchronize()
+        assert int(torch.count_nonzero(ws)) == 0
+        parity.compare(prob, "wgrad", parity.from_dev(out), False, idx=idx, what=f"split program replay {i}")
+        run_program(drgg, "fwd", dvo, f32, True)
+        torch.cuda.synchronize()
