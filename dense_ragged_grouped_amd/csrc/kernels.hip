@@ -86,6 +86,43 @@ struct Sched {
     int32_t scan[kMaxGemmThreads];
 };
 
+// Exclusive scan of v over the workgroup's threads (in thread order), with
+// the sum (MAX = false) or the maximum (MAX = true, identity 0: the values
+// are non-negative); *total gets the reduction over all threads.  Inclusive
+// scans within each wave by lane shuffles, then one pass over the (at most
+// 8) wave results in `tmp` (LDS, one word per wave plus one).  A serial pass
+// over every thread's value, or a barrier per doubling step, costs
+// microseconds at kernel start; this costs a few hundred cycles.  Must be
+// called by all threads; ends with a barrier.
+template <bool MAX = false, class Ptr>
+__device__ int32_t block_exclusive_scan(int32_t v, Ptr tmp, int32_t* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    int32_t x = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int32_t y = __shfl_up(x, d, 64);
+        if (lane >= d) x = MAX ? max(x, y) : x + y;
+    }
+    const int32_t excl_in_wave = MAX ? __shfl_up(x, 1, 64) : x - v;
+    if (lane == 63) tmp[wave] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int32_t acc = 0;
+        for (int w = 0; w < nw; ++w) {
+            const int32_t t = tmp[w];
+            tmp[w] = acc;
+            acc = MAX ? max(acc, t) : acc + t;
+        }
+        tmp[nw] = acc;
+    }
+    __syncthreads();
+    const int32_t before = tmp[wave];
+    const int32_t r = MAX ? max(before, lane > 0 ? excl_in_wave : 0) : before + excl_in_wave;
+    *total = tmp[nw];
+    __syncthreads();
+    return r;
+}
+
 // Fills s.offs[0..E] with the offsets clamped into [0, M] (and made
 // non-decreasing), and s.prefix[0..E] with the exclusive prefix of
 // work(e, T_e).  With no offsets array (a batched call) the groups are
@@ -95,28 +132,21 @@ template <class WorkFn>
 __device__ void build_schedule(Sched& s, const int32_t* __restrict__ offs, int E, int64_t M, int64_t T,
                                WorkFn work) {
     const int tid = threadIdx.x, nthr = blockDim.x;
+    int32_t* tmp = s.scan;   // free until the prefix is written
     for (int e = tid; e <= E; e += nthr) {
         int64_t v = offs ? (int64_t)offs[e] : e * T;
         v = v < 0 ? 0 : (v > M ? M : v);
         s.offs[e] = (int32_t)v;
     }
     __syncthreads();
-    // make non-decreasing (a running max); E <= 1024, one pass per thread chunk
+    // make non-decreasing (a running max); E <= 1024, one run per thread
     const int per = (E + nthr) / nthr;   // covers indices 0..E
-    const int lo = tid * per;
+    const int lo = min(tid * per, E + 1);
     const int hi = min(lo + per, E + 1);
     int32_t run = 0;
     for (int i = lo; i < hi; ++i) run = max(run, s.offs[i]);
-    s.scan[tid] = run;
-    __syncthreads();
-    for (int d = 1; d < nthr; d <<= 1) {
-        int32_t v = tid >= d ? s.scan[tid - d] : 0;
-        __syncthreads();
-        s.scan[tid] = max(s.scan[tid], v);
-        __syncthreads();
-    }
-    int32_t carry = tid > 0 ? s.scan[tid - 1] : 0;
-    __syncthreads();
+    int32_t total;
+    int32_t carry = block_exclusive_scan<true>(run, tmp, &total);
     for (int i = lo; i < hi; ++i) {
         carry = max(carry, s.offs[i]);
         s.offs[i] = carry;
@@ -125,15 +155,7 @@ __device__ void build_schedule(Sched& s, const int32_t* __restrict__ offs, int E
     // work counts and their exclusive prefix
     int32_t local = 0;
     for (int e = lo; e < hi && e < E; ++e) local += work(e, s.offs[e + 1] - s.offs[e]);
-    s.scan[tid] = local;
-    __syncthreads();
-    for (int d = 1; d < nthr; d <<= 1) {
-        int32_t v = tid >= d ? s.scan[tid - d] : 0;
-        __syncthreads();
-        s.scan[tid] += v;
-        __syncthreads();
-    }
-    int32_t acc = tid > 0 ? s.scan[tid - 1] : 0;
+    int32_t acc = block_exclusive_scan(local, tmp, &total);
     for (int e = lo; e < hi; ++e) {
         s.prefix[e] = acc;
         if (e < E) acc += work(e, s.offs[e + 1] - s.offs[e]);
@@ -191,38 +213,6 @@ __device__ void rank_experts(Sched& s, lds_t* scr, int E, LenFn clen) {
         if (tid + u * nthr < E) perm[r4[u]] = (int16_t)(tid + u * nthr);
     __syncthreads();
 }
-// Exclusive prefix sum of v over the workgroup's threads (in thread order);
-// *total gets the sum.  Inclusive scans within each wave by lane shuffles,
-// then one pass over the (at most 8) wave sums in `tmp` (LDS, one word per
-// wave plus one).  A serial pass over every thread's value costs tens of
-// microseconds at kernel start; this costs a few hundred cycles.  Must be
-// called by all threads; ends with a barrier.
-__device__ int32_t block_exclusive_scan(int32_t v, __attribute__((address_space(3))) int32_t* tmp, int32_t* total) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    int32_t x = v;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int32_t y = __shfl_up(x, d, 64);
-        if (lane >= d) x += y;
-    }
-    if (lane == 63) tmp[wave] = x;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int32_t acc = 0;
-        for (int w = 0; w < nw; ++w) {
-            const int32_t t = tmp[w];
-            tmp[w] = acc;
-            acc += t;
-        }
-        tmp[nw] = acc;
-    }
-    __syncthreads();
-    const int32_t r = tmp[wave] + x - v;
-    *total = tmp[nw];
-    __syncthreads();
-    return r;
-}
-
 template <class WorkFn>
 __device__ void position_prefix(Sched& s, lds_t* scr, int npos, WorkFn work) {
     const int tid = threadIdx.x, nthr = blockDim.x;
