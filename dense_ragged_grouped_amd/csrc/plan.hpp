@@ -90,6 +90,12 @@ constexpr int64_t kItemOverheadTokens = 256;
 //           minimises the estimated time on kRuleCUs workgroups: the waves
 //           of its P0*E*chunks items times (its chunk length + the item
 //           overhead); the smallest S on ties (fewest partials).
+//   share = one reference CU's share of the token-tile work,
+//           ceil(M * P0 / kRuleCUs) rounded up to 64: when the balanced
+//           expert stays whole (one chunk), only experts longer than the
+//           balanced size are cut, and into chunks of at least one share
+//           (fewer and longer items, fewer partials to fold; measured faster
+//           on skewed routings).
 // Long experts are cut into more chunks; short ones are never cut.
 inline int64_t wgrad_chunk_max(int32_t E, int64_t M, int64_t N, int64_t K) {
     if (M <= 0) return 512;
@@ -109,7 +115,10 @@ inline int64_t wgrad_chunk_max(int32_t E, int64_t M, int64_t N, int64_t K) {
             best_cost = cost;
         }
     }
-    return best;
+    int64_t len, chunks;
+    wgrad_chunking(tb, best, &len, &chunks);
+    const int64_t share = round_up(ceil_div(M * p0, kRuleCUs), kTileK);
+    return chunks <= 1 && share > best ? share : best;
 }
 
 // Deterministic weight gradient, chunk rule part 3: the tail-only plan.

@@ -201,7 +201,9 @@ WORKLOADS = {
 def test_chunk_rule_values(drgg):
     cm = {k: drgg.plan(drgg.OP_WGRAD, *v, drgg.FP32, True)["chunk_max"] for k, v in WORKLOADS.items()}
     assert cm["gate_up"] == 12288 and drgg.wgrad_chunking(16384, cm["gate_up"]) == (8192, 2)
-    assert cm["down"] == 6144 and drgg.wgrad_chunking(42987, cm["down"])[1] == 7
+    # down: the balanced expert (4096 tokens) stays whole, so the long experts
+    # are cut into chunks of at least one reference CU's share (131072 * 24 / 256)
+    assert cm["down"] == 12288 and drgg.wgrad_chunking(42987, cm["down"]) == (10752, 4)
     assert cm["square"] == 16384 and drgg.wgrad_chunking(16384, cm["square"]) == (16384, 1)
     assert drgg.wgrad_chunking(128, cm["tiny"]) == (128, 1)
     # skinny dense: 16 equal chunks, 16 tiles x 16 chunks = one full wave of 256 items
@@ -210,6 +212,26 @@ def test_chunk_rule_values(drgg):
         assert c == 1024 and drgg.wgrad_chunking(16384, c) == (1024, 16)
     for n, want in ((512, 2048), (1024, 4096)):
         assert drgg.plan(drgg.OP_WGRAD, 1, 16384, n, 4096, drgg.FP32, True)["chunk_max"] == want
+
+
+def test_chunk_rule_share_clamp(drgg):
+    """Whenever the rule leaves a balanced expert (ceil(M/E) tokens) whole,
+    its chunk length is at least one reference CU's share of the token-tile
+    work, ceil(M * P0 / 256) rounded up to 64; when it cuts the balanced
+    expert, the chunk count it picked is kept."""
+    rng = np.random.default_rng(5)
+    for _ in range(300):
+        E = int(rng.choice([1, 2, 4, 8, 16, 32, 64, 128]))
+        M = int(rng.integers(1, 1 << 18))
+        N = int(rng.choice([48, 64, 512, 768, 1536, 2048, 4096]))
+        K = int(rng.choice([256, 768, 1024, 2048, 4096]))
+        cm = drgg.plan(drgg.OP_WGRAD, E, M, N, K, drgg.FP32, True)["chunk_max"]
+        p0 = -(-N // 256) * -(-K // 256)
+        share = -(-(-(-M * p0 // 256)) // 64) * 64
+        tb = -(-M // E)
+        assert cm % 64 == 0 and cm >= 512
+        if drgg.wgrad_chunking(tb, cm)[1] <= 1:
+            assert cm >= share, (E, M, N, K, cm, share)
 
 
 @pytest.mark.parametrize("chunk_max", [512, 1152, 6144, 12288, 16384])
