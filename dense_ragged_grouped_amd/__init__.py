@@ -32,6 +32,7 @@ TILE_AUTO, TILE_256x256, TILE_128x128, TILE_256x128, TILE_128x256, TILE_64x256 =
 # the symbols include/drgg.h declares
 EXPORTS = (
     "grouped_gemm_fwd", "grouped_gemm_dgrad", "grouped_gemm_wgrad", "router_gemm_fp32_bf16x3",
+    "router_gemm_fp32_bf16x3_ws", "router_workspace_size", "drgg_router_split",
     "batched_gemm_fwd", "batched_gemm_dgrad", "batched_gemm_wgrad",
     "drgg_route_split", "drgg_route_clear", "drgg_route_count", "drgg_hold_cus",
     "grouped_gemm_workspace_size", "drgg_workspace_init", "drgg_plan", "drgg_wgrad_chunking",
@@ -100,6 +101,12 @@ def _load(path=LIB_PATH):
         getattr(lib, name).restype = c_int
     lib.router_gemm_fp32_bf16x3.argtypes = [vp, vp, i64, i64, i64, vp, vp]
     lib.router_gemm_fp32_bf16x3.restype = c_int
+    lib.router_gemm_fp32_bf16x3_ws.argtypes = [vp, vp, i64, i64, i64, vp, vp, sz, vp]
+    lib.router_gemm_fp32_bf16x3_ws.restype = c_int
+    lib.router_workspace_size.argtypes = [i64, i64, i64, ctypes.POINTER(sz)]
+    lib.router_workspace_size.restype = c_int
+    lib.drgg_router_split.argtypes = [i64, i64, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    lib.drgg_router_split.restype = c_int
     lib.grouped_gemm_workspace_size.argtypes = [c_int, i32, i64, i64, i64, c_int, c_int, c_int,
                                                 ctypes.POINTER(sz)]
     lib.grouped_gemm_workspace_size.restype = c_int
@@ -397,8 +404,9 @@ def _workspace(device, nbytes, workspace, deterministic, kind="wgrad", stream=No
         # keyed by the program that runs (`deterministic` here: whether the
         # deterministic program runs): a non-deterministic call routed to it
         # shares its buffer of partials, the split program has its own,
-        # zeroed one; the data gradient's W^T has its own
-        prog = "dgrad" if kind == "dgrad" else bool(deterministic)
+        # zeroed one; the data gradient's W^T and the router's reduction
+        # slices have their own
+        prog = kind if kind in ("dgrad", "router") else bool(deterministic)
         key = (str(device), s.cuda_stream, prog)
         if key not in _default_ws:
             _default_ws[key] = Workspace(device)
@@ -625,8 +633,25 @@ def batched_gemm_wgrad(X, G, out_dtype=None, deterministic=True, out=None, works
     return out
 
 
-def router_gemm_fp32_bf16x3(X, Wr, out=None, stream=None):
-    """FP32 router GEMM out = X Wr^T on BF16 MFMA via the BF16x3 split."""
+def router_split(M: int, N: int, K: int):
+    """(slices, values per slice) of the sliced router call."""
+    ks, kq = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib.drgg_router_split(M, N, K, ctypes.byref(ks), ctypes.byref(kq)), "drgg_router_split")
+    return ks.value, kq.value
+
+
+def router_workspace_size(M: int, N: int, K: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib.router_workspace_size(M, N, K, ctypes.byref(n)), "router_workspace_size")
+    return n.value
+
+
+def router_gemm_fp32_bf16x3(X, Wr, out=None, stream=None, workspace=None):
+    """FP32 router GEMM out = X Wr^T on BF16 MFMA via the BF16x3 split.
+    `workspace` (a Workspace, a device tensor, or None for the default
+    buffer) holds the reduction slices of the sliced program; False runs the
+    single-pass program (no workspace; a different, also fixed, summation
+    order), which also serves K > 2^21 when no workspace was given."""
     torch = _torch()
     _need(X, torch.float32, "X", 2)
     _need(Wr, torch.float32, "Wr", 2)
@@ -641,9 +666,16 @@ def router_gemm_fp32_bf16x3(X, Wr, out=None, stream=None):
         if tuple(out.shape) != (M, N):
             raise ValueError(f"out has shape {tuple(out.shape)}, expected {(M, N)}")
     with _on_one_device(stream, X, Wr, out):
-        st = lib.router_gemm_fp32_bf16x3(X.data_ptr(), Wr.data_ptr(), M, N, K, out.data_ptr(),
-                                         _stream(X.device, stream))
-    _check(st, "router_gemm_fp32_bf16x3")
+        if workspace is False or (workspace is None and K > (1 << 21)):
+            st = lib.router_gemm_fp32_bf16x3(X.data_ptr(), Wr.data_ptr(), M, N, K, out.data_ptr(),
+                                             _stream(X.device, stream))
+            _check(st, "router_gemm_fp32_bf16x3")
+            return out
+        nbytes = router_workspace_size(M, N, K)
+        ws_ptr, ws_bytes = _workspace(X.device, nbytes, workspace, True, kind="router", stream=stream)
+        st = lib.router_gemm_fp32_bf16x3_ws(X.data_ptr(), Wr.data_ptr(), M, N, K, out.data_ptr(), ws_ptr, ws_bytes,
+                                            _stream(X.device, stream))
+    _check(st, "router_gemm_fp32_bf16x3_ws")
     return out
 
 

@@ -541,21 +541,74 @@ drgg_status batched_gemm_wgrad(const void* X, const void* G, const drgg_batched*
                      workspace_bytes, stream, L);
 }
 
-drgg_status router_gemm_fp32_bf16x3(const float* X, const float* Wr, int64_t M, int64_t N, int64_t K,
-                                    float* out, hipStream_t stream) {
-    if (!X || !Wr || !out) return DRGG_EINVAL;
-    // N, K <= 2^22 keep every per-lane byte offset inside a 128-row block of
+// Router argument checks shared by both entry points and the size query.
+static drgg_status check_router(int64_t M, int64_t N, int64_t K) {
+    // N, K <= 2^22 keep every per-lane byte offset inside a 256-row block of
     // the operands and of the output below 2^31
     if (M < 0 || N < 1 || K < 8 || M > INT32_MAX || N > (int64_t(1) << 22) || K > (int64_t(1) << 22))
         return DRGG_ESHAPE;
     if (K % 8 != 0 || N % 4 != 0) return DRGG_EALIGN;
-    if (!aligned16(X) || !aligned16(Wr) || !aligned16(out)) return DRGG_EALIGN;
     int64_t t;
-    if (!mul_ok(M, K, &t) || !mul_ok(t, 4, &t) || !mul_ok(M, N, &t) || !mul_ok(t, 4, &t) ||
+    if (!mul_ok(M, K, &t) || !mul_ok(t, 4, &t) || !mul_ok(M, N, &t) || !mul_ok(t, 32, &t) ||
         !mul_ok(N, K, &t) || !mul_ok(t, 4, &t))
         return DRGG_EOVERFLOW;
+    // one workgroup per 128x128 tile (the single-pass program; the sliced
+    // one has at most as many): the grid must fit its 32-bit size
+    if (ceil_div(M, 128) * ceil_div(N, 128) > INT32_MAX) return DRGG_ESHAPE;
+    return DRGG_OK;
+}
+
+// The sliced program loads 256-row blocks: K <= 2^21 keeps every per-lane
+// byte offset inside one below the buffer range (2^31).
+static drgg_status check_router_sliced(int64_t M, int64_t N, int64_t K) {
+    drgg_status st = check_router(M, N, K);
+    if (st != DRGG_OK) return st;
+    return K > (int64_t(1) << 21) ? DRGG_ESHAPE : DRGG_OK;
+}
+
+drgg_status router_gemm_fp32_bf16x3(const float* X, const float* Wr, int64_t M, int64_t N, int64_t K,
+                                    float* out, hipStream_t stream) {
+    if (!X || !Wr || !out) return DRGG_EINVAL;
+    drgg_status st = check_router(M, N, K);
+    if (st != DRGG_OK) return st;
+    if (!aligned16(X) || !aligned16(Wr) || !aligned16(out)) return DRGG_EALIGN;
     if (M == 0) return DRGG_OK;
     return launch_status(launch_router(X, Wr, out, M, N, K, stream));
+}
+
+drgg_status router_workspace_size(int64_t M, int64_t N, int64_t K, size_t* bytes) {
+    if (!bytes) return DRGG_EINVAL;
+    drgg_status st = check_router_sliced(M, N, K);
+    if (st != DRGG_OK) return st;
+    const RouterSplit r = router_split(M, N, K);
+    *bytes = (size_t)((r.ks - 1) * M * N * 4);
+    return DRGG_OK;
+}
+
+drgg_status drgg_router_split(int64_t M, int64_t N, int64_t K, int64_t* ks, int64_t* kq) {
+    if (!ks || !kq) return DRGG_EINVAL;
+    drgg_status st = check_router_sliced(M, N, K);
+    if (st != DRGG_OK) return st;
+    const RouterSplit r = router_split(M, N, K);
+    *ks = r.ks;
+    *kq = r.kq;
+    return DRGG_OK;
+}
+
+drgg_status router_gemm_fp32_bf16x3_ws(const float* X, const float* Wr, int64_t M, int64_t N, int64_t K,
+                                       float* out, void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream) {
+    if (!X || !Wr || !out) return DRGG_EINVAL;
+    drgg_status st = check_router_sliced(M, N, K);
+    if (st != DRGG_OK) return st;
+    if (!aligned16(X) || !aligned16(Wr) || !aligned16(out)) return DRGG_EALIGN;
+    const RouterSplit r = router_split(M, N, K);
+    const size_t need = (size_t)((r.ks - 1) * M * N * 4);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return DRGG_EWORKSPACE;
+    if (need > 0 && !aligned16(workspace)) return DRGG_EALIGN;
+    if (M == 0) return DRGG_OK;
+    return launch_status(
+        launch_router_ks(X, Wr, out, static_cast<float*>(workspace), M, N, K, r.ks, r.kq, stream));
 }
 
 drgg_status grouped_gemm_workspace_size(drgg_op op, int32_t E, int64_t M, int64_t N, int64_t K,

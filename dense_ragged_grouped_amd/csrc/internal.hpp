@@ -43,6 +43,8 @@ hipError_t launch_wgrad_det(int tile, const GemmArgs& a, bool bf16, hipStream_t 
 hipError_t launch_wgrad_atomic(int tile, const GemmArgs& a, int64_t grid_n, bool bf16, hipStream_t s);
 hipError_t launch_router(const float* X, const float* Wr, float* out, int64_t M, int64_t N, int64_t K,
                          hipStream_t s);
+hipError_t launch_router_ks(const float* X, const float* Wr, float* out, float* part, int64_t M, int64_t N,
+                            int64_t K, int64_t ks, int64_t kq, hipStream_t s);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 
 // The fixed device workspace of grouped_gemm_wgrad_noalloc: its size, and the

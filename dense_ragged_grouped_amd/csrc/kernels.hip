@@ -1892,10 +1892,23 @@ struct RouterArgs {
     int64_t M, N, K;
 };
 
-// Loads one 32-value stage of ROWS FP32 rows (128 bytes each) into LDS.
-template <int ROWS, int WAVES>
+// LDS rows of an FP32 stage: RB bytes (RB / 4 reduction values, RB / 16
+// chunks of four).  Chunk c of row r sits at c ^ swzF<RB>(r): swzK for
+// 128-byte rows; (r >> 2) & 3 for 64-byte rows, which puts the 16 rows of one
+// read pass (one chunk each) on 16 distinct 16-byte bank groups of a 256-byte
+// window.
+template <int RB>
+__device__ __forceinline__ int swzF(int row) {
+    static_assert(RB == 128 || RB == 64, "rows of 32 or 16 FP32 values");
+    if constexpr (RB == 128) return swzK(row);
+    else return (row >> 2) & 3;
+}
+
+// Loads one stage (RB / 4 values) of ROWS FP32 rows into LDS.
+template <int ROWS, int WAVES, int RB = 128>
 struct F32StageLoader {
-    static constexpr int kPerWave = ROWS * 128 / 1024 / WAVES;
+    static constexpr int kPerWave = ROWS * RB / 1024 / WAVES;
+    static_assert(kPerWave >= 1 && kPerWave * WAVES * 1024 == ROWS * RB, "whole 1 KB loads per wave");
     uint32_t off[kPerWave];   // byte offset of this lane's 16 bytes from the stage base (kOOB if masked)
     int32_t kp[kPerWave];     // reduction position of those 16 bytes within the stage
     const char* base;
@@ -1909,7 +1922,7 @@ struct F32StageLoader {
 #pragma unroll
         for (int i = 0; i < kPerWave; ++i) {
             const int bb = (wave * kPerWave + i) * 1024 + lane * 16;
-            const int row = bb / 128, logical = ((bb % 128) / 16) ^ swzK(row);
+            const int row = bb / RB, logical = ((bb % RB) / 16) ^ swzF<RB>(row);
             off[i] = row < nvalid ? (uint32_t)(row * ld * 4 + logical * 16) : kOOB;
             kp[i] = logical * 4;
         }
@@ -1917,15 +1930,18 @@ struct F32StageLoader {
 
     // stage L into `buf`; positions at or past klen read as zero
     __device__ __forceinline__ void issue(lds_t* buf, int L) const {
-        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-        const __amdgpu_buffer_rsrc_t r = make_rsrc(base + (int64_t)L * 128);
-        const int rem = klen - L * 32;
 #pragma unroll
-        for (int i = 0; i < kPerWave; ++i) {
-            const uint32_t o = kp[i] < rem ? off[i] : kOOB;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                r, (lds_void_t*)(buf + (wave * kPerWave + i) * 1024), 16, o, 0, 0, 0);
-        }
+        for (int i = 0; i < kPerWave; ++i) issue_one(buf, L, i);
+    }
+
+    // load i of this wave's share of stage L
+    __device__ __forceinline__ void issue_one(lds_t* buf, int L, int i) const {
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(base + (int64_t)L * RB);
+        const int rem = klen - L * (RB / 4);
+        const uint32_t o = kp[i] < rem ? off[i] : kOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(buf + (wave * kPerWave + i) * 1024), 16, o, 0,
+                                                 0, 0);
     }
 };
 
@@ -1933,13 +1949,28 @@ struct F32StageLoader {
 struct Raw8 {
     f32x4 x0, x1;
 };
+template <int RB = 128>
 __device__ __forceinline__ Raw8 read_raw(const lds_t* buf, int rb, int s, int l) {
     typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
     const int row = rb + (l & 31), c0 = 4 * s + 2 * (l >> 5);
     Raw8 r;
-    r.x0 = *reinterpret_cast<const lds_f32x4*>(buf + row * 128 + ((c0 ^ swzK(row)) << 4));
-    r.x1 = *reinterpret_cast<const lds_f32x4*>(buf + row * 128 + (((c0 + 1) ^ swzK(row)) << 4));
+    r.x0 = *reinterpret_cast<const lds_f32x4*>(buf + row * RB + ((c0 ^ swzF<RB>(row)) << 4));
+    r.x1 = *reinterpret_cast<const lds_f32x4*>(buf + row * RB + (((c0 + 1) ^ swzF<RB>(row)) << 4));
     return r;
+}
+
+// Split values 2p, 2p+1 of a raw fragment into BF16 hi = bf16(v) and
+// lo = bf16(v - hi), both rounded to nearest even (v - hi is exact in FP32).
+__device__ __forceinline__ void split_pair(const Raw8& r, int p, bf16x8& hi, bf16x8& lo) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const float x0 = p < 2 ? r.x0[2 * p] : r.x1[2 * p - 4], x1 = p < 2 ? r.x0[2 * p + 1] : r.x1[2 * p - 3];
+    const bf16x2 h = __builtin_convertvector((f32x2{x0, x1}), bf16x2);
+    const bf16x2 d = __builtin_convertvector((f32x2{x0 - (float)h[0], x1 - (float)h[1]}), bf16x2);
+    hi[2 * p] = h[0];
+    hi[2 * p + 1] = h[1];
+    lo[2 * p] = d[0];
+    lo[2 * p + 1] = d[1];
 }
 
 // Split 8 FP32 values into BF16 hi = bf16(v) and lo = bf16(v - hi), both
@@ -1983,7 +2014,7 @@ __device__ __forceinline__ void router_sched() {
     router_sched_impl<NM, NR, NL, NV>(std::make_integer_sequence<int, NM>{});
 }
 
-template <int BM, int BN, int WAVES>
+template <int BM, int BN, int WAVES, int RB = 128>
 struct RouterMma {
     static constexpr int kWGM = (WAVES == 8 && BM >= 256) ? 4 : 2;
     static constexpr int kWGN = WAVES / kWGM;
@@ -2013,9 +2044,9 @@ struct RouterMma {
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         const int oa = wave_row(wave), ob = wave_col(wave);
 #pragma unroll
-        for (int i = 0; i < kBI; ++i) ra[i] = read_raw(sA, oa + 32 * i, s, l);
+        for (int i = 0; i < kBI; ++i) ra[i] = read_raw<RB>(sA, oa + 32 * i, s, l);
 #pragma unroll
-        for (int j = 0; j < kBJ; ++j) rbv[j] = read_raw(sB, ob + 32 * j, s, l);
+        for (int j = 0; j < kBJ; ++j) rbv[j] = read_raw<RB>(sB, ob + 32 * j, s, l);
     }
 
     // split the raw fragments into set F
@@ -2025,6 +2056,79 @@ struct RouterMma {
         for (int i = 0; i < kBI; ++i) split8(ra[i], ah[F][i], al[F][i]);
 #pragma unroll
         for (int j = 0; j < kBJ; ++j) split8(rbv[j], bh[F][j], bl[F][j]);
+    }
+
+    // the raw fragments of one side (H = 0: the A side, 1: the B side) of
+    // sub-step s of the stage in buf
+    template <int H>
+    __device__ __forceinline__ void read_side(const lds_t* buf, int s) {
+        const int l = threadIdx.x & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        if constexpr (H == 0) {
+            const int oa = wave_row(wave);
+#pragma unroll
+            for (int i = 0; i < kBI; ++i) ra[i] = read_raw<RB>(buf, oa + 32 * i, s, l);
+        } else {
+            const int ob = wave_col(wave);
+#pragma unroll
+            for (int j = 0; j < kBJ; ++j) rbv[j] = read_raw<RB>(buf, ob + 32 * j, s, l);
+        }
+    }
+
+    // split the raw fragments of one side into set F
+    template <int F, int H>
+    __device__ __forceinline__ void split_side() {
+        if constexpr (H == 0) {
+#pragma unroll
+            for (int i = 0; i < kBI; ++i) split8(ra[i], ah[F][i], al[F][i]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < kBJ; ++j) split8(rbv[j], bh[F][j], bl[F][j]);
+        }
+    }
+
+    // one 16-byte half (hh) of the raw fragment fr of side H
+    template <int H, int FR, int HH>
+    __device__ __forceinline__ void read_one(const lds_t* buf, int s) {
+        typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+        const int l = threadIdx.x & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const int row = (H == 0 ? wave_row(wave) : wave_col(wave)) + 32 * FR + (l & 31);
+        const int c = 4 * s + 2 * (l >> 5) + HH;
+        const f32x4 v = *reinterpret_cast<const lds_f32x4*>(buf + row * RB + ((c ^ swzF<RB>(row)) << 4));
+        Raw8& r = H == 0 ? ra[FR] : rbv[FR];
+        if constexpr (HH == 0) r.x0 = v;
+        else r.x1 = v;
+    }
+
+    // values 2p, 2p+1 of raw fragment fr of side H into set F
+    template <int F, int H, int FR, int P>
+    __device__ __forceinline__ void split_one() {
+        if constexpr (H == 0) split_pair(ra[FR], P, ah[F][FR], al[F][FR]);
+        else split_pair(rbv[FR], P, bh[F][FR], bl[F][FR]);
+    }
+
+    // product p of mfma<F> (kind p / (kBI*kBJ) on block p % (kBI*kBJ))
+    template <int F, int P>
+    __device__ __forceinline__ void mfma_one() {
+        constexpr int NB = kBI * kBJ, kind = P / NB, i = (P % NB) / kBJ, j = P % kBJ;
+        const bf16x8& b = kind == 1 ? bl[F][j] : bh[F][j];
+        const bf16x8& a = kind == 2 ? al[F][i] : ah[F][i];
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, acc[i][j], 0, 0, 0);
+    }
+
+    // products P0 .. P1-1 of the 3 * kBI * kBJ of mfma<F>, in its order
+    // (product p is kind p / (kBI*kBJ) on block p % (kBI*kBJ))
+    template <int F, int P0, int P1>
+    __device__ __forceinline__ void mfma_range() {
+        constexpr int NB = kBI * kBJ;
+#pragma unroll
+        for (int p = P0; p < P1; ++p) {
+            const int kind = p / NB, i = (p % NB) / kBJ, j = p % kBJ;
+            const bf16x8& b = kind == 1 ? bl[F][j] : bh[F][j];
+            const bf16x8& a = kind == 2 ? al[F][i] : ah[F][i];
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, acc[i][j], 0, 0, 0);
+        }
     }
 
     // the three products of one 16-step, each over all blocks before the
@@ -2128,6 +2232,158 @@ __global__ __launch_bounds__(64 * kRouterWaves) void router_bf16x3_kernel(Router
     store_tile<false>(mma, a.out + m0 * a.N + n0, a.N, rows, cols);
 }
 
+// FP32 router with the reduction cut into slices (the same BF16x3 products,
+// flashinfer PR #8363, Summary).  One workgroup per 256x256 output tile and
+// reduction slice q (ks slices of kq values, whole 16-value stages): 4
+// waves in a 2x2 grid of 128x128 wave tiles, so every split fragment feeds
+// twice as many MFMAs as in the 128x128 kernel above, and every byte loaded
+// into LDS twice as many products.  Slice 0 writes its FP32 sum to `out`,
+// slice q > 0 to part[q - 1] ([M, N] each); router_fold_kernel then adds the
+// slices in order q = 1 .. ks-1, so the result is fixed: a function of (M, N,
+// K), never of the device.  Workgroups of one slice are adjacent (an XCD's L2
+// holds that slice of Wr); every X value is loaded by one workgroup.
+//
+// Pipeline over stages of 16 values in four LDS buffers (stage s in buffer
+// s % 4); each step (one stage) is cut in two by its one barrier:
+//   region 0: the first half of stage kt's MFMAs (fragment set kt%2); the B
+//             side of stage kt+1 is read and its A side (read in region 1 of
+//             step kt-1) split into set (kt+1)%2
+//   barrier:  after this wave's loads of stage kt+2 have landed; every wave
+//             has finished reading stage kt+1
+//   region 1: the loads of stage kt+5 into stage kt+1's buffer; the second
+//             half of the MFMAs; the A side of stage kt+2 is read and the B
+//             side of stage kt+1 split
+// so the reads and the split of a region are independent (the split always
+// consumes reads of the region before) and each load has about three steps
+// between its issue and its first read.
+constexpr int kRksBM = 256, kRksBN = 256, kRksStages = 4, kRksRowBytes = 64;
+
+// fn(integral_constant<int, T>) for T = 0, 1, ... in order
+template <class Fn, int... T>
+__device__ __forceinline__ void for_each_slot(std::integer_sequence<int, T...>, Fn&& fn) {
+    (fn(std::integral_constant<int, T>{}), ...);
+}
+
+struct RouterKsArgs {
+    const float* X;
+    const float* Wr;
+    float* out;
+    float* part;      // (ks - 1) x [M, N] slice sums, slices 1 .. ks-1
+    int64_t M, N, K;
+    int64_t kq;       // reduction values per slice (a multiple of 16)
+};
+
+__global__ __launch_bounds__(256) void router_ks_kernel(RouterKsArgs a) {
+    constexpr int BM = kRksBM, BN = kRksBN, S = kRksStages, RB = kRksRowBytes, KV = RB / 4;
+    static_assert(S == 4, "the stage buffers below are written out for four stages");
+    __shared__ __attribute__((aligned(256))) char sa0[BM * RB], sa1[BM * RB], sa2[BM * RB], sa3[BM * RB];
+    __shared__ __attribute__((aligned(256))) char sb0[BN * RB], sb1[BN * RB], sb2[BN * RB], sb3[BN * RB];
+    lds_t* const sa[S] = {(lds_t*)sa0, (lds_t*)sa1, (lds_t*)sa2, (lds_t*)sa3};
+    lds_t* const sb[S] = {(lds_t*)sb0, (lds_t*)sb1, (lds_t*)sb2, (lds_t*)sb3};
+    using Mma = RouterMma<BM, BN, 4, RB>;
+    using LA = F32StageLoader<BM, 4, RB>;
+    using LB = F32StageLoader<BN, 4, RB>;
+    constexpr int C = LA::kPerWave + LB::kPerWave;   // loads per wave per stage
+
+    const int64_t ntn = (a.N + BN - 1) / BN, tiles = ((a.M + BM - 1) / BM) * ntn;
+    const int64_t w = xcd_remap(blockIdx.x, gridDim.x);
+    const int64_t q = w / tiles, t = w % tiles;
+    const int64_t m0 = (t / ntn) * BM, n0 = (t % ntn) * BN, k0 = q * a.kq;
+    const int32_t rows = (int32_t)min<int64_t>(BM, a.M - m0);
+    const int32_t cols = (int32_t)min<int64_t>(BN, a.N - n0);
+    const int32_t klen = (int32_t)max<int64_t>(0, min<int64_t>(a.kq, a.K - k0));
+    LA la;
+    LB lb;
+    la.init(a.X + m0 * a.K + k0, a.K, rows, klen);
+    lb.init(a.Wr + n0 * a.K + k0, a.K, cols, klen);
+    const int nk = (klen + KV - 1) / KV;
+    const int nkS = ((nk + S - 1) / S) * S;
+    Mma mma;
+    la.issue(sa[0], 0);
+    lb.issue(sb[0], 0);
+    la.issue(sa[1], 1);
+    lb.issue(sb[1], 1);
+    la.issue(sa[2], 2);
+    lb.issue(sb[2], 2);
+    la.issue(sa[3], 3);
+    lb.issue(sb[3], 3);
+    // stages 0 and 1 have landed: stage 0 is split into set 0 and the A side
+    // of stage 1 read; once every wave is done with buffer 0, stage 4 goes there
+    wait_vm_lgkm<2 * C>();
+    barrier_nofence();
+    mma.template read_side<0>(sa[0], 0);
+    mma.template read_side<1>(sb[0], 0);
+    mma.template split_side<0, 0>();
+    mma.template split_side<0, 1>();
+    mma.template read_side<0>(sa[1], 0);
+    mma.zero();
+    wait_vm_lgkm<2 * C>();
+    barrier_nofence();
+    la.issue(sa[0], 4);
+    lb.issue(sb[0], 4);
+    constexpr int HALF = Mma::kMfmas / 2;   // 24 MFMA slots per region
+    static_assert(HALF == 24 && Mma::kBI == 4 && Mma::kBJ == 4 && C == 8, "the slot plan below");
+    // Region slot t (0 .. 23), in this order, nothing moved across slots:
+    //   one MFMA of stage kt; for t < 16 one pair of values of the side
+    //   being split (fragment t / 4, pair t % 4: 6 vector instructions); for
+    //   t < 8 one 16-byte read of the side being read (fragment t / 2, half
+    //   t % 2); in region 1, for t >= 16 one load of stage kt+5 (A side
+    //   t - 16 < 4, then B side).
+    auto region = [&](auto f_tag, auto r_tag, auto t_tag, const lds_t* rbuf, lds_t* lda, lds_t* ldb, int lstage) {
+        constexpr int F = decltype(f_tag)::value, R = decltype(r_tag)::value, T = decltype(t_tag)::value;
+        constexpr int SPLIT_SIDE = R == 0 ? 0 : 1, READ_SIDE = R == 0 ? 1 : 0;
+        mma.template mfma_one<F, R * HALF + T>();
+        if constexpr (T < 16) mma.template split_one<F ^ 1, SPLIT_SIDE, T / 4, T % 4>();
+        if constexpr (T < 8) mma.template read_one<READ_SIDE, T / 2, T % 2>(rbuf, 0);
+        if constexpr (R == 1 && T >= 16) {
+            if constexpr (T < 20) la.issue_one(lda, lstage, T - 16);
+            else lb.issue_one(ldb, lstage, T - 20);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto run_region = [&](auto f_tag, auto r_tag, const lds_t* rbuf, lds_t* lda, lds_t* ldb, int lstage) {
+        for_each_slot(std::make_integer_sequence<int, HALF>{},
+                      [&](auto t_tag) { region(f_tag, r_tag, t_tag, rbuf, lda, ldb, lstage); });
+    };
+    // Stages past nk load zeros, which add nothing.
+    auto step = [&](auto st_tag, int kt) {
+        constexpr int ST = decltype(st_tag)::value, F = ST & 1;
+        constexpr int B1 = (ST + 1) % S, B2 = (ST + 2) % S;
+        __builtin_amdgcn_sched_barrier(0);
+        // region 0: split the A side of stage kt+1, read its B side
+        run_region(std::integral_constant<int, F>{}, std::integral_constant<int, 0>{}, sb[B1], sa[B1], sb[B1], 0);
+        wait_vm_lgkm<2 * C>();
+        barrier_nofence();
+        // region 1: split the B side of stage kt+1, read the A side of stage
+        // kt+2, load stage kt+5 into stage kt+1's buffer
+        run_region(std::integral_constant<int, F>{}, std::integral_constant<int, 1>{}, sa[B2], sa[B1], sb[B1], kt + 5);
+    };
+    for (int kt = 0; kt < nkS; kt += S) {
+        step(std::integral_constant<int, 0>{}, kt);
+        step(std::integral_constant<int, 1>{}, kt + 1);
+        step(std::integral_constant<int, 2>{}, kt + 2);
+        step(std::integral_constant<int, 3>{}, kt + 3);
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // the masked loads past the end
+    float* dst = q == 0 ? a.out : a.part + (q - 1) * a.M * a.N;
+    store_tile<false>(mma, dst + m0 * a.N + n0, a.N, rows, cols);
+}
+
+// out += part[0], then += part[1], ... (the reduction slices in order), four
+// values per thread; n4 = M * N / 4 (N is a multiple of 4).
+__global__ __launch_bounds__(kThreads) void router_fold_kernel(float* out, const float* part, int64_t n4,
+                                                               int32_t nparts) {
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n4; i += (int64_t)gridDim.x * kThreads) {
+        f32x4 s = reinterpret_cast<const f32x4*>(out)[i];
+        for (int p = 0; p < nparts; ++p) {
+            const f32x4 v = reinterpret_cast<const f32x4*>(part)[p * n4 + i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) s[j] += v[j];
+        }
+        reinterpret_cast<f32x4*>(out)[i] = s;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // host launchers (called from api.cpp)
 
@@ -2221,6 +2477,26 @@ hipError_t launch_router(const float* X, const float* Wr, float* out, int64_t M,
     const int64_t tiles = ((M + kRouterBM - 1) / kRouterBM) * ((N + kRouterBN - 1) / kRouterBN);
     timing_mark("router_bf16x3_kernel", s);
     hipLaunchKernelGGL(router_bf16x3_kernel, dim3((unsigned)tiles), dim3(64 * kRouterWaves), 0, s, a);
+    timing_end(s);
+    return hipGetLastError();
+}
+
+hipError_t launch_router_ks(const float* X, const float* Wr, float* out, float* part, int64_t M, int64_t N,
+                            int64_t K, int64_t ks, int64_t kq, hipStream_t s) {
+    RouterKsArgs a{X, Wr, out, part, M, N, K, kq};
+    const int64_t tiles = ((M + kRksBM - 1) / kRksBM) * ((N + kRksBN - 1) / kRksBN);
+    timing_mark("router_ks_kernel", s);
+    hipLaunchKernelGGL(router_ks_kernel, dim3((unsigned)(tiles * ks)), dim3(256), 0, s, a);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || ks <= 1) {
+        timing_end(s);
+        return err;
+    }
+    const int64_t n4 = M * N / 4;
+    const int64_t blocks = std::min<int64_t>((n4 + kThreads - 1) / kThreads, 4096);
+    timing_mark("router_fold_kernel", s);
+    hipLaunchKernelGGL(router_fold_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, out, part, n4,
+                       (int32_t)(ks - 1));
     timing_end(s);
     return hipGetLastError();
 }

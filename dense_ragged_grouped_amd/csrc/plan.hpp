@@ -384,6 +384,25 @@ inline int64_t wgs_per_cu(TileShape t, bool fwd_dgrad, bool det_wgrad) {
     return n < 1 ? 1 : n;
 }
 
+// FP32 router with the reduction cut into slices (router_ks_kernel): 256x256
+// output tiles, and ks slices of kq values (whole 16-value stages) so that
+// tiles * ks reaches kRuleCUs workgroups; at most 8 slices and none shorter
+// than 256 values (ks = 1 when the tiles alone fill the workgroups).  A
+// function of (M, N, K) only: the slices are added in a fixed order.
+struct RouterSplit {
+    int64_t ks, kq;
+};
+inline RouterSplit router_split(int64_t M, int64_t N, int64_t K) {
+    const int64_t tiles = ceil_div(M, 256) * ceil_div(N, 256);
+    int64_t ks = tiles > 0 ? ceil_div(kRuleCUs, tiles) : 1;
+    const int64_t cap = K / 256 > 1 ? K / 256 : 1;
+    if (ks > cap) ks = cap;
+    if (ks > 8) ks = 8;
+    if (ks < 1) ks = 1;
+    const int64_t kq = round_up(ceil_div(K, ks), 16);
+    return {ceil_div(K, kq), kq};   // every slice non-empty
+}
+
 // Default output tile per program: 256x256, except the skinny weight
 // gradient (N <= 64: 64x256) and outputs of at most 128 columns (Y has N,
 // dX and dW have K), where a 256-wide tile would be at least half masked:

@@ -25,6 +25,10 @@ hipError_t launch_wgrad_atomic(int, const GemmArgs&, int64_t, bool, hipStream_t)
 hipError_t launch_router(const float*, const float*, float*, int64_t, int64_t, int64_t, hipStream_t) {
     no_gpu("router");
 }
+hipError_t launch_router_ks(const float*, const float*, float*, float*, int64_t, int64_t, int64_t, int64_t, int64_t,
+                            hipStream_t) {
+    no_gpu("router ks");
+}
 hipError_t launch_zero(void*, size_t, hipStream_t) { no_gpu("zero"); }
 hipError_t launch_hold_cus(int, uint64_t, hipStream_t) { no_gpu("hold"); }
 hipError_t scratch_buffer(void**) { no_gpu("scratch"); }
@@ -81,6 +85,22 @@ int main() {
     EXPECT(router_gemm_fp32_bf16x3(static_cast<float*>(A), static_cast<float*>(A), 16, (1 << 22) + 4, 16,
                                    static_cast<float*>(A), nullptr),
            DRGG_ESHAPE);
+    {
+        size_t rw = 0;
+        EXPECT(router_workspace_size(16384, 256, 4096, &rw), DRGG_OK);
+        EXPECT(rw == size_t(3) * 16384 * 256 * 4 ? DRGG_OK : DRGG_EINVAL, DRGG_OK);
+        EXPECT(router_gemm_fp32_bf16x3_ws(static_cast<float*>(A), static_cast<float*>(A), 16384, 256, 4096,
+                                          static_cast<float*>(A), nullptr, 0, nullptr),
+               DRGG_EWORKSPACE);
+        int64_t ks = 0, kq = 0;
+        for (int64_t M : {1, 255, 256, 16384, 65536})
+            for (int64_t K : {8, 200, 4096, 4104}) {
+                EXPECT(drgg_router_split(M, 256, K, &ks, &kq), DRGG_OK);
+                EXPECT(ks >= 1 && ks <= 8 && kq % 16 == 0 && (ks - 1) * kq < K && ks * kq >= K ? DRGG_OK
+                                                                                          : DRGG_EINVAL,
+                       DRGG_OK);
+            }
+    }
     // planning and the rules behind it, for a range of shapes and CU counts
     const int64_t shapes[][4] = {{8, 131072, 1536, 2048}, {32, 131072, 2048, 768}, {1, 16384, 48, 4096},
                                  {1, 16384, 4096, 4096}, {4, 512, 512, 256},     {1024, 3000, 8, 8},

@@ -250,11 +250,21 @@ def test_nondet_integer_inputs_match_det_bitwise(drgg):
 
 # ---- router ------------------------------------------------------------------
 
-@pytest.mark.parametrize("shape", [(300, 256, 520), (128, 128, 64), (1000, 40, 264), (1, 8, 8)])
-def test_router_bf16x3(drgg, shape):
+ROUTER_SHAPES = [(300, 256, 520), (128, 128, 64), (1000, 40, 264), (1, 8, 8), (777, 256, 4104), (513, 300, 1032)]
+
+
+@pytest.mark.parametrize("sliced", [True, False], ids=["sliced", "single_pass"])
+@pytest.mark.parametrize("shape", ROUTER_SHAPES)
+def test_router_bf16x3(drgg, shape, sliced):
+    """Both router programs against the step-by-step emulation and the exact
+    product; the sliced program's reduction slices (several of them, the last
+    one shorter, on the last two shapes) and masked tile rows and columns."""
     M, N, K = shape
     X, Wr = synth.router_inputs(M, N, K, cfg_seed=7)
-    out = parity.from_dev(drgg.router_gemm_fp32_bf16x3(parity.to_dev(X), parity.to_dev(Wr))).astype(np.float64)
+    print(f"router {shape} sliced={sliced} split={drgg.router_split(M, N, K)}", flush=True)
+    ws = None if sliced else False
+    out = parity.from_dev(drgg.router_gemm_fp32_bf16x3(parity.to_dev(X), parity.to_dev(Wr), workspace=ws))
+    out = out.astype(np.float64)
     emul = oracle.router_bf16x3(X, Wr)
     exact = oracle.router_exact(X, Wr)
     # against the step-by-step emulation: only the FP32 accumulation order differs
@@ -266,14 +276,36 @@ def test_router_bf16x3(drgg, shape):
     parity.check_fp32(out, exact, kred, ax, aw, what=f"router {shape}")
 
 
-def test_router_bf16_representable_inputs_exact(drgg):
+@pytest.mark.parametrize("sliced", [True, False], ids=["sliced", "single_pass"])
+def test_router_bf16_representable_inputs_exact(drgg, sliced):
     """Inputs with at most 8 significant bits make lo = 0; with small integers
-    every sum is exact too, so the router equals the exact product bit for bit."""
+    every sum is exact too, so the router equals the exact product bit for bit
+    (in the sliced program: 4 slices of 256)."""
     rng = np.random.default_rng(5)
-    X = rng.integers(-4, 5, size=(256, 512)).astype(np.float32)
-    Wr = rng.integers(-4, 5, size=(256, 512)).astype(np.float32)
-    out = parity.from_dev(drgg.router_gemm_fp32_bf16x3(parity.to_dev(X), parity.to_dev(Wr)))
+    X = rng.integers(-4, 5, size=(256, 1024)).astype(np.float32)
+    Wr = rng.integers(-4, 5, size=(256, 1024)).astype(np.float32)
+    assert drgg.router_split(256, 256, 1024) == (4, 256)
+    out = parity.from_dev(drgg.router_gemm_fp32_bf16x3(parity.to_dev(X), parity.to_dev(Wr),
+                                                       workspace=None if sliced else False))
     assert np.array_equal(out, oracle.round_f32(oracle.router_exact(X, Wr)))
+
+
+def test_router_sliced_is_reproducible_and_checks_its_workspace(drgg):
+    """The sliced program gives the same bits on every call (its slices are
+    added in a fixed order), with a caller-owned workspace too, and refuses a
+    workspace that is too small."""
+    X, Wr = synth.router_inputs(2048, 256, 4096, cfg_seed=9)
+    Xd, Wd = parity.to_dev(X), parity.to_dev(Wr)
+    ks, kq = drgg.router_split(2048, 256, 4096)
+    assert ks == 8 and kq == 512
+    nbytes = drgg.router_workspace_size(2048, 256, 4096)
+    assert nbytes == (ks - 1) * 2048 * 256 * 4
+    a = parity.from_dev(drgg.router_gemm_fp32_bf16x3(Xd, Wd))
+    ws = torch.full((nbytes,), 0x7F, dtype=torch.uint8, device="cuda")   # stale contents do not matter
+    b = parity.from_dev(drgg.router_gemm_fp32_bf16x3(Xd, Wd, workspace=ws))
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    with pytest.raises(drgg.DrggError):
+        drgg.router_gemm_fp32_bf16x3(Xd, Wd, workspace=ws[: nbytes - 16])
 
 
 # ---- edge cases --------------------------------------------------------------

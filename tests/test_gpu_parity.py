@@ -109,6 +109,32 @@ def test_integer_inputs_bitwise(drgg, program, det, tile):
         drgg.set_knob(drgg.KNOB_TILE, 0)
 
 
+# expert lengths covering the remainders of the 512-token unit: 0, 1, one
+# step minus and plus one, half a unit (256: the "k256 tail"), 257, 300, 511
+UNIT_REMAINDERS = [512 * a + r for a, r in ((2, 0), (2, 1), (3, 31), (2, 32), (2, 33), (2, 255), (3, 256),
+                                            (2, 257), (2, 300), (2, 511))]
+
+
+@pytest.mark.parametrize("det", [True, False])
+def test_wgrad_unit_remainders_bitwise(drgg, det):
+    """Weight gradients of experts whose lengths leave remainders 0, 1, 31,
+    32, 33, 255, 256, 257, 300 and 511 modulo the 512-token unit, each cut
+    into several chunks (in the split program whole units, the last one the
+    remainder): integer inputs, so both programs match the oracle bit for
+    bit."""
+    prob = synth.make_problem("unit_remainders", 301, UNIT_REMAINDERS, N=264, K=200, integer=True)
+    plan = drgg.plan(drgg.OP_WGRAD, prob.E, prob.M, prob.N, prob.K, drgg.FP32, True)
+    chunks = [drgg.wgrad_chunking(int(t), plan["chunk_max"]) for t in UNIT_REMAINDERS]
+    assert all(n > 1 for _, n in chunks), chunks
+    print(f"unit remainders det={det} chunks={chunks}", flush=True)
+    dv = dev_inputs(prob)
+    for out_dtype in (torch.float32, torch.bfloat16):
+        out = run_program(drgg, "wgrad", dv, out_dtype, det)
+        torch.cuda.synchronize()
+        parity.compare(prob, "wgrad", parity.from_dev(out), out_dtype == torch.bfloat16, integer=True,
+                       what=f"unit remainders det={det}")
+
+
 SPLIT_CASE = (106, 3, 4000, 264, 520, (1,))   # two experts of about 2000 tokens: cut into chunks
 MEDIUM_SPLIT = [SPLIT_CASE, (107, 1, 9000, 64, 392, ())]
 
