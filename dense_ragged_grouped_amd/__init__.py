@@ -634,7 +634,8 @@ def batched_gemm_wgrad(X, G, out_dtype=None, deterministic=True, out=None, works
 
 
 def router_split(M: int, N: int, K: int):
-    """(slices, values per slice) of the sliced router call."""
+    """(slices, values per slice) of the router call: (0, K) for the
+    single-pass program."""
     ks, kq = ctypes.c_int64(), ctypes.c_int64()
     _check(lib.drgg_router_split(M, N, K, ctypes.byref(ks), ctypes.byref(kq)), "drgg_router_split")
     return ks.value, kq.value
@@ -647,11 +648,11 @@ def router_workspace_size(M: int, N: int, K: int) -> int:
 
 
 def router_gemm_fp32_bf16x3(X, Wr, out=None, stream=None, workspace=None):
-    """FP32 router GEMM out = X Wr^T on BF16 MFMA via the BF16x3 split.
-    `workspace` (a Workspace, a device tensor, or None for the default
-    buffer) holds the reduction slices of the sliced program; False runs the
-    single-pass program (no workspace; a different, also fixed, summation
-    order), which also serves K > 2^21 when no workspace was given."""
+    """FP32 router GEMM out = X Wr^T on BF16 MFMA via the BF16x3 split, in
+    the program router_split(M, N, K) names (single pass, or reduction slices
+    added in a fixed order).  `workspace` (a Workspace, a device tensor, or
+    None for the default buffer) holds the slices; False always runs the
+    single-pass program (no workspace)."""
     torch = _torch()
     _need(X, torch.float32, "X", 2)
     _need(Wr, torch.float32, "Wr", 2)
@@ -666,7 +667,7 @@ def router_gemm_fp32_bf16x3(X, Wr, out=None, stream=None, workspace=None):
         if tuple(out.shape) != (M, N):
             raise ValueError(f"out has shape {tuple(out.shape)}, expected {(M, N)}")
     with _on_one_device(stream, X, Wr, out):
-        if workspace is False or (workspace is None and K > (1 << 21)):
+        if workspace is False:
             st = lib.router_gemm_fp32_bf16x3(X.data_ptr(), Wr.data_ptr(), M, N, K, out.data_ptr(),
                                              _stream(X.device, stream))
             _check(st, "router_gemm_fp32_bf16x3")

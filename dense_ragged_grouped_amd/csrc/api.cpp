@@ -558,13 +558,7 @@ static drgg_status check_router(int64_t M, int64_t N, int64_t K) {
     return DRGG_OK;
 }
 
-// The sliced program loads 256-row blocks: K <= 2^21 keeps every per-lane
-// byte offset inside one below the buffer range (2^31).
-static drgg_status check_router_sliced(int64_t M, int64_t N, int64_t K) {
-    drgg_status st = check_router(M, N, K);
-    if (st != DRGG_OK) return st;
-    return K > (int64_t(1) << 21) ? DRGG_ESHAPE : DRGG_OK;
-}
+
 
 drgg_status router_gemm_fp32_bf16x3(const float* X, const float* Wr, int64_t M, int64_t N, int64_t K,
                                     float* out, hipStream_t stream) {
@@ -578,16 +572,16 @@ drgg_status router_gemm_fp32_bf16x3(const float* X, const float* Wr, int64_t M, 
 
 drgg_status router_workspace_size(int64_t M, int64_t N, int64_t K, size_t* bytes) {
     if (!bytes) return DRGG_EINVAL;
-    drgg_status st = check_router_sliced(M, N, K);
+    drgg_status st = check_router(M, N, K);
     if (st != DRGG_OK) return st;
     const RouterSplit r = router_split(M, N, K);
-    *bytes = (size_t)((r.ks - 1) * M * N * 4);
+    *bytes = r.ks > 1 ? (size_t)((r.ks - 1) * M * N * 4) : 0;
     return DRGG_OK;
 }
 
 drgg_status drgg_router_split(int64_t M, int64_t N, int64_t K, int64_t* ks, int64_t* kq) {
     if (!ks || !kq) return DRGG_EINVAL;
-    drgg_status st = check_router_sliced(M, N, K);
+    drgg_status st = check_router(M, N, K);
     if (st != DRGG_OK) return st;
     const RouterSplit r = router_split(M, N, K);
     *ks = r.ks;
@@ -599,14 +593,15 @@ drgg_status router_gemm_fp32_bf16x3_ws(const float* X, const float* Wr, int64_t 
                                        float* out, void* workspace, size_t workspace_bytes,
                                        hipStream_t stream) {
     if (!X || !Wr || !out) return DRGG_EINVAL;
-    drgg_status st = check_router_sliced(M, N, K);
+    drgg_status st = check_router(M, N, K);
     if (st != DRGG_OK) return st;
     if (!aligned16(X) || !aligned16(Wr) || !aligned16(out)) return DRGG_EALIGN;
     const RouterSplit r = router_split(M, N, K);
-    const size_t need = (size_t)((r.ks - 1) * M * N * 4);
+    const size_t need = r.ks > 1 ? (size_t)((r.ks - 1) * M * N * 4) : 0;
     if (need > 0 && (!workspace || workspace_bytes < need)) return DRGG_EWORKSPACE;
     if (need > 0 && !aligned16(workspace)) return DRGG_EALIGN;
     if (M == 0) return DRGG_OK;
+    if (r.ks == 0) return launch_status(launch_router(X, Wr, out, M, N, K, stream));
     return launch_status(
         launch_router_ks(X, Wr, out, static_cast<float*>(workspace), M, N, K, r.ks, r.kq, stream));
 }

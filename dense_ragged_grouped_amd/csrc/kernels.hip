@@ -1892,23 +1892,11 @@ struct RouterArgs {
     int64_t M, N, K;
 };
 
-// LDS rows of an FP32 stage: RB bytes (RB / 4 reduction values, RB / 16
-// chunks of four).  Chunk c of row r sits at c ^ swzF<RB>(r): swzK for
-// 128-byte rows; (r >> 2) & 3 for 64-byte rows, which puts the 16 rows of one
-// read pass (one chunk each) on 16 distinct 16-byte bank groups of a 256-byte
-// window.
-template <int RB>
-__device__ __forceinline__ int swzF(int row) {
-    static_assert(RB == 128 || RB == 64, "rows of 32 or 16 FP32 values");
-    if constexpr (RB == 128) return swzK(row);
-    else return (row >> 2) & 3;
-}
-
-// Loads one stage (RB / 4 values) of ROWS FP32 rows into LDS.
-template <int ROWS, int WAVES, int RB = 128>
+// Loads one 32-value stage of ROWS FP32 rows (128 bytes each) into LDS.
+template <int ROWS, int WAVES>
 struct F32StageLoader {
-    static constexpr int kPerWave = ROWS * RB / 1024 / WAVES;
-    static_assert(kPerWave >= 1 && kPerWave * WAVES * 1024 == ROWS * RB, "whole 1 KB loads per wave");
+    static constexpr int kPerWave = ROWS * 128 / 1024 / WAVES;
+    static_assert(kPerWave >= 1 && kPerWave * WAVES * 1024 == ROWS * 128, "whole 1 KB loads per wave");
     uint32_t off[kPerWave];   // byte offset of this lane's 16 bytes from the stage base (kOOB if masked)
     int32_t kp[kPerWave];     // reduction position of those 16 bytes within the stage
     const char* base;
@@ -1922,7 +1910,7 @@ struct F32StageLoader {
 #pragma unroll
         for (int i = 0; i < kPerWave; ++i) {
             const int bb = (wave * kPerWave + i) * 1024 + lane * 16;
-            const int row = bb / RB, logical = ((bb % RB) / 16) ^ swzF<RB>(row);
+            const int row = bb / 128, logical = ((bb % 128) / 16) ^ swzK(row);
             off[i] = row < nvalid ? (uint32_t)(row * ld * 4 + logical * 16) : kOOB;
             kp[i] = logical * 4;
         }
@@ -1937,8 +1925,8 @@ struct F32StageLoader {
     // load i of this wave's share of stage L
     __device__ __forceinline__ void issue_one(lds_t* buf, int L, int i) const {
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-        const __amdgpu_buffer_rsrc_t r = make_rsrc(base + (int64_t)L * RB);
-        const int rem = klen - L * (RB / 4);
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(base + (int64_t)L * 128);
+        const int rem = klen - L * 32;
         const uint32_t o = kp[i] < rem ? off[i] : kOOB;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(buf + (wave * kPerWave + i) * 1024), 16, o, 0,
                                                  0, 0);
@@ -1949,13 +1937,12 @@ struct F32StageLoader {
 struct Raw8 {
     f32x4 x0, x1;
 };
-template <int RB = 128>
 __device__ __forceinline__ Raw8 read_raw(const lds_t* buf, int rb, int s, int l) {
     typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
     const int row = rb + (l & 31), c0 = 4 * s + 2 * (l >> 5);
     Raw8 r;
-    r.x0 = *reinterpret_cast<const lds_f32x4*>(buf + row * RB + ((c0 ^ swzF<RB>(row)) << 4));
-    r.x1 = *reinterpret_cast<const lds_f32x4*>(buf + row * RB + (((c0 + 1) ^ swzF<RB>(row)) << 4));
+    r.x0 = *reinterpret_cast<const lds_f32x4*>(buf + row * 128 + ((c0 ^ swzK(row)) << 4));
+    r.x1 = *reinterpret_cast<const lds_f32x4*>(buf + row * 128 + (((c0 + 1) ^ swzK(row)) << 4));
     return r;
 }
 
@@ -2014,7 +2001,7 @@ __device__ __forceinline__ void router_sched() {
     router_sched_impl<NM, NR, NL, NV>(std::make_integer_sequence<int, NM>{});
 }
 
-template <int BM, int BN, int WAVES, int RB = 128>
+template <int BM, int BN, int WAVES>
 struct RouterMma {
     static constexpr int kWGM = (WAVES == 8 && BM >= 256) ? 4 : 2;
     static constexpr int kWGN = WAVES / kWGM;
@@ -2044,9 +2031,9 @@ struct RouterMma {
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         const int oa = wave_row(wave), ob = wave_col(wave);
 #pragma unroll
-        for (int i = 0; i < kBI; ++i) ra[i] = read_raw<RB>(sA, oa + 32 * i, s, l);
+        for (int i = 0; i < kBI; ++i) ra[i] = read_raw(sA, oa + 32 * i, s, l);
 #pragma unroll
-        for (int j = 0; j < kBJ; ++j) rbv[j] = read_raw<RB>(sB, ob + 32 * j, s, l);
+        for (int j = 0; j < kBJ; ++j) rbv[j] = read_raw(sB, ob + 32 * j, s, l);
     }
 
     // split the raw fragments into set F
@@ -2067,11 +2054,11 @@ struct RouterMma {
         if constexpr (H == 0) {
             const int oa = wave_row(wave);
 #pragma unroll
-            for (int i = 0; i < kBI; ++i) ra[i] = read_raw<RB>(buf, oa + 32 * i, s, l);
+            for (int i = 0; i < kBI; ++i) ra[i] = read_raw(buf, oa + 32 * i, s, l);
         } else {
             const int ob = wave_col(wave);
 #pragma unroll
-            for (int j = 0; j < kBJ; ++j) rbv[j] = read_raw<RB>(buf, ob + 32 * j, s, l);
+            for (int j = 0; j < kBJ; ++j) rbv[j] = read_raw(buf, ob + 32 * j, s, l);
         }
     }
 
@@ -2095,7 +2082,7 @@ struct RouterMma {
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         const int row = (H == 0 ? wave_row(wave) : wave_col(wave)) + 32 * FR + (l & 31);
         const int c = 4 * s + 2 * (l >> 5) + HH;
-        const f32x4 v = *reinterpret_cast<const lds_f32x4*>(buf + row * RB + ((c ^ swzF<RB>(row)) << 4));
+        const f32x4 v = *reinterpret_cast<const lds_f32x4*>(buf + row * 128 + ((c ^ swzK(row)) << 4));
         Raw8& r = H == 0 ? ra[FR] : rbv[FR];
         if constexpr (HH == 0) r.x0 = v;
         else r.x1 = v;
@@ -2234,29 +2221,34 @@ __global__ __launch_bounds__(64 * kRouterWaves) void router_bf16x3_kernel(Router
 
 // FP32 router with the reduction cut into slices (the same BF16x3 products,
 // flashinfer PR #8363, Summary).  One workgroup per 256x256 output tile and
-// reduction slice q (ks slices of kq values, whole 16-value stages): 4
-// waves in a 2x2 grid of 128x128 wave tiles, so every split fragment feeds
-// twice as many MFMAs as in the 128x128 kernel above, and every byte loaded
-// into LDS twice as many products.  Slice 0 writes its FP32 sum to `out`,
-// slice q > 0 to part[q - 1] ([M, N] each); router_fold_kernel then adds the
-// slices in order q = 1 .. ks-1, so the result is fixed: a function of (M, N,
-// K), never of the device.  Workgroups of one slice are adjacent (an XCD's L2
-// holds that slice of Wr); every X value is loaded by one workgroup.
+// reduction slice q (ks slices of kq values): 4 waves in a 2x2 grid of
+// 128x128 wave tiles, so every split fragment feeds twice as many MFMAs as in
+// the 128x128 kernel above, and every byte loaded into LDS twice as many
+// products.  Slice 0 writes its FP32 sum to `out`, slice q > 0 to
+// part[q - 1] ([M, N] each); router_fold_kernel then adds the slices in order
+// q = 1 .. ks-1, so the result is fixed: a function of (M, N, K), never of the
+// device.  Workgroups of one slice are adjacent (an XCD's L2 holds that slice
+// of Wr); every X value is loaded by one workgroup.
 //
-// Pipeline over stages of 16 values in four LDS buffers (stage s in buffer
-// s % 4); each step (one stage) is cut in two by its one barrier:
-//   region 0: the first half of stage kt's MFMAs (fragment set kt%2); the B
-//             side of stage kt+1 is read and its A side (read in region 1 of
+// Steps of 16 values; the operands are loaded in pairs of steps (32 values:
+// whole 128-byte rows, the layout of the kernel above) into two pair buffers
+// of 64 KB.  Each step is cut in two by its one barrier:
+//   region 0: the first half of step kt's MFMAs (fragment set kt%2); the B
+//             side of step kt+1 is read and its A side (read in region 1 of
 //             step kt-1) split into set (kt+1)%2
-//   barrier:  after this wave's loads of stage kt+2 have landed; every wave
-//             has finished reading stage kt+1
-//   region 1: the loads of stage kt+5 into stage kt+1's buffer; the second
-//             half of the MFMAs; the A side of stage kt+2 is read and the B
-//             side of stage kt+1 split
+//   barrier:  every wave has finished reading step kt+1's B side, and (even
+//             steps) the pair holding step kt+2 has landed
+//   region 1: on even steps the loads of the pair two ahead (steps kt+4,
+//             kt+5) into the buffer of steps kt, kt+1; the second half of the
+//             MFMAs; the A side of step kt+2 is read and the B side of step
+//             kt+1 split
 // so the reads and the split of a region are independent (the split always
-// consumes reads of the region before) and each load has about three steps
-// between its issue and its first read.
-constexpr int kRksBM = 256, kRksBN = 256, kRksStages = 4, kRksRowBytes = 64;
+// consumes reads of the region before).  Within a region each MFMA slot
+// carries one product, one pair of the split, and one read or one load, in
+// that order, fenced so that the compiler keeps the interleave (left to
+// itself it clustered the MFMAs and the split and ran no faster than the
+// kernel above).
+constexpr int kRksBM = 256, kRksBN = 256;
 
 // fn(integral_constant<int, T>) for T = 0, 1, ... in order
 template <class Fn, int... T>
@@ -2274,16 +2266,15 @@ struct RouterKsArgs {
 };
 
 __global__ __launch_bounds__(256) void router_ks_kernel(RouterKsArgs a) {
-    constexpr int BM = kRksBM, BN = kRksBN, S = kRksStages, RB = kRksRowBytes, KV = RB / 4;
-    static_assert(S == 4, "the stage buffers below are written out for four stages");
-    __shared__ __attribute__((aligned(256))) char sa0[BM * RB], sa1[BM * RB], sa2[BM * RB], sa3[BM * RB];
-    __shared__ __attribute__((aligned(256))) char sb0[BN * RB], sb1[BN * RB], sb2[BN * RB], sb3[BN * RB];
-    lds_t* const sa[S] = {(lds_t*)sa0, (lds_t*)sa1, (lds_t*)sa2, (lds_t*)sa3};
-    lds_t* const sb[S] = {(lds_t*)sb0, (lds_t*)sb1, (lds_t*)sb2, (lds_t*)sb3};
-    using Mma = RouterMma<BM, BN, 4, RB>;
-    using LA = F32StageLoader<BM, 4, RB>;
-    using LB = F32StageLoader<BN, 4, RB>;
-    constexpr int C = LA::kPerWave + LB::kPerWave;   // loads per wave per stage
+    constexpr int BM = kRksBM, BN = kRksBN, KV = 16;   // 16-value steps in 32-value pairs
+    __shared__ __attribute__((aligned(256))) char sa0[BM * 128], sa1[BM * 128];
+    __shared__ __attribute__((aligned(256))) char sb0[BN * 128], sb1[BN * 128];
+    lds_t* const sa[2] = {(lds_t*)sa0, (lds_t*)sa1};
+    lds_t* const sb[2] = {(lds_t*)sb0, (lds_t*)sb1};
+    using Mma = RouterMma<BM, BN, 4>;
+    using LA = F32StageLoader<BM, 4>;
+    using LB = F32StageLoader<BN, 4>;
+    constexpr int C2 = LA::kPerWave + LB::kPerWave;   // loads per wave per pair
 
     const int64_t ntn = (a.N + BN - 1) / BN, tiles = ((a.M + BM - 1) / BM) * ntn;
     const int64_t w = xcd_remap(blockIdx.x, gridDim.x);
@@ -2297,68 +2288,56 @@ __global__ __launch_bounds__(256) void router_ks_kernel(RouterKsArgs a) {
     la.init(a.X + m0 * a.K + k0, a.K, rows, klen);
     lb.init(a.Wr + n0 * a.K + k0, a.K, cols, klen);
     const int nk = (klen + KV - 1) / KV;
-    const int nkS = ((nk + S - 1) / S) * S;
+    const int nkS = ((nk + 3) / 4) * 4;
     Mma mma;
     la.issue(sa[0], 0);
     lb.issue(sb[0], 0);
     la.issue(sa[1], 1);
     lb.issue(sb[1], 1);
-    la.issue(sa[2], 2);
-    lb.issue(sb[2], 2);
-    la.issue(sa[3], 3);
-    lb.issue(sb[3], 3);
-    // stages 0 and 1 have landed: stage 0 is split into set 0 and the A side
-    // of stage 1 read; once every wave is done with buffer 0, stage 4 goes there
-    wait_vm_lgkm<2 * C>();
+    wait_vm_lgkm<C2>();
     barrier_nofence();
     mma.template read_side<0>(sa[0], 0);
     mma.template read_side<1>(sb[0], 0);
     mma.template split_side<0, 0>();
     mma.template split_side<0, 1>();
-    mma.template read_side<0>(sa[1], 0);
+    mma.template read_side<0>(sa[0], 1);
     mma.zero();
-    wait_vm_lgkm<2 * C>();
-    barrier_nofence();
-    la.issue(sa[0], 4);
-    lb.issue(sb[0], 4);
-    constexpr int HALF = Mma::kMfmas / 2;   // 24 MFMA slots per region
-    static_assert(HALF == 24 && Mma::kBI == 4 && Mma::kBJ == 4 && C == 8, "the slot plan below");
-    // Region slot t (0 .. 23), in this order, nothing moved across slots:
-    //   one MFMA of stage kt; for t < 16 one pair of values of the side
-    //   being split (fragment t / 4, pair t % 4: 6 vector instructions); for
-    //   t < 8 one 16-byte read of the side being read (fragment t / 2, half
-    //   t % 2); in region 1, for t >= 16 one load of stage kt+5 (A side
-    //   t - 16 < 4, then B side).
-    auto region = [&](auto f_tag, auto r_tag, auto t_tag, const lds_t* rbuf, lds_t* lda, lds_t* ldb, int lstage) {
+    constexpr int HALF = Mma::kMfmas / 2;
+    static_assert(HALF == 24 && Mma::kBI == 4 && Mma::kBJ == 4 && C2 == 16, "the slot plan below");
+    auto region = [&](auto f_tag, auto r_tag, auto t_tag, auto h_tag, auto ld_tag, const lds_t* rbuf, lds_t* lda,
+                      lds_t* ldb, int lpair) __attribute__((always_inline)) {
         constexpr int F = decltype(f_tag)::value, R = decltype(r_tag)::value, T = decltype(t_tag)::value;
+        constexpr int H = decltype(h_tag)::value, LD = decltype(ld_tag)::value;
         constexpr int SPLIT_SIDE = R == 0 ? 0 : 1, READ_SIDE = R == 0 ? 1 : 0;
         mma.template mfma_one<F, R * HALF + T>();
         if constexpr (T < 16) mma.template split_one<F ^ 1, SPLIT_SIDE, T / 4, T % 4>();
-        if constexpr (T < 8) mma.template read_one<READ_SIDE, T / 2, T % 2>(rbuf, 0);
-        if constexpr (R == 1 && T >= 16) {
-            if constexpr (T < 20) la.issue_one(lda, lstage, T - 16);
-            else lb.issue_one(ldb, lstage, T - 20);
+        if constexpr (T < 8) mma.template read_one<READ_SIDE, T / 2, T % 2>(rbuf, H);
+        if constexpr (R == 1 && LD && T >= 8) {
+            if constexpr (T < 16) la.issue_one(lda, lpair, T - 8);
+            else lb.issue_one(ldb, lpair, T - 16);
         }
         __builtin_amdgcn_sched_barrier(0);
     };
-    auto run_region = [&](auto f_tag, auto r_tag, const lds_t* rbuf, lds_t* lda, lds_t* ldb, int lstage) {
-        for_each_slot(std::make_integer_sequence<int, HALF>{},
-                      [&](auto t_tag) { region(f_tag, r_tag, t_tag, rbuf, lda, ldb, lstage); });
+    auto run_region = [&](auto f_tag, auto r_tag, auto h_tag, auto ld_tag, const lds_t* rbuf, lds_t* lda,
+                          lds_t* ldb, int lpair) __attribute__((always_inline)) {
+        for_each_slot(std::make_integer_sequence<int, HALF>{}, [&](auto t_tag) __attribute__((always_inline)) {
+            region(f_tag, r_tag, t_tag, h_tag, ld_tag, rbuf, lda, ldb, lpair);
+        });
     };
-    // Stages past nk load zeros, which add nothing.
-    auto step = [&](auto st_tag, int kt) {
+    auto step = [&](auto st_tag, int kt) __attribute__((always_inline)) {
         constexpr int ST = decltype(st_tag)::value, F = ST & 1;
-        constexpr int B1 = (ST + 1) % S, B2 = (ST + 2) % S;
+        constexpr int P1 = ((ST + 1) / 2) % 2, H1 = (ST + 1) % 2, P2 = ((ST + 2) / 2) % 2, H2 = (ST + 2) % 2;
+        constexpr int LD = (ST % 2) == 0, PB = ST / 2;
         __builtin_amdgcn_sched_barrier(0);
-        // region 0: split the A side of stage kt+1, read its B side
-        run_region(std::integral_constant<int, F>{}, std::integral_constant<int, 0>{}, sb[B1], sa[B1], sb[B1], 0);
-        wait_vm_lgkm<2 * C>();
+        run_region(std::integral_constant<int, F>{}, std::integral_constant<int, 0>{}, std::integral_constant<int, H1>{},
+                   std::integral_constant<int, 0>{}, sb[P1], sa[PB], sb[PB], 0);
+        if constexpr (LD) wait_vm_lgkm<0>();
+        else wait_vm_lgkm<C2>();
         barrier_nofence();
-        // region 1: split the B side of stage kt+1, read the A side of stage
-        // kt+2, load stage kt+5 into stage kt+1's buffer
-        run_region(std::integral_constant<int, F>{}, std::integral_constant<int, 1>{}, sa[B2], sa[B1], sb[B1], kt + 5);
+        run_region(std::integral_constant<int, F>{}, std::integral_constant<int, 1>{}, std::integral_constant<int, H2>{},
+                   std::integral_constant<int, LD>{}, sa[P2], sa[PB], sb[PB], kt / 2 + 2);
     };
-    for (int kt = 0; kt < nkS; kt += S) {
+    for (int kt = 0; kt < nkS; kt += 4) {
         step(std::integral_constant<int, 0>{}, kt);
         step(std::integral_constant<int, 1>{}, kt + 1);
         step(std::integral_constant<int, 2>{}, kt + 2);

@@ -384,22 +384,25 @@ inline int64_t wgs_per_cu(TileShape t, bool fwd_dgrad, bool det_wgrad) {
     return n < 1 ? 1 : n;
 }
 
-// FP32 router with the reduction cut into slices (router_ks_kernel): 256x256
-// output tiles, and ks slices of kq values (whole 16-value stages) so that
-// tiles * ks reaches kRuleCUs workgroups; at most 8 slices and none shorter
-// than 256 values (ks = 1 when the tiles alone fill the workgroups).  A
-// function of (M, N, K) only: the slices are added in a fixed order.
+// FP32 router program choice and slices.  The single-pass program (128x128
+// tiles) runs when its tiles alone fill kRuleCUs workgroups, or for K > 2^21
+// (ks = 0, kq = K); otherwise the sliced program (router_ks_kernel): 256x256
+// output tiles and ks slices of kq values (a multiple of 32: whole 128-byte
+// rows) so that tiles * ks reaches kRuleCUs workgroups, at most 8 slices and
+// none shorter than 256 values.  A function of (M, N, K) only: the slices are
+// added in a fixed order.
 struct RouterSplit {
     int64_t ks, kq;
 };
 inline RouterSplit router_split(int64_t M, int64_t N, int64_t K) {
+    if (ceil_div(M, 128) * ceil_div(N, 128) >= kRuleCUs || K > (int64_t(1) << 21)) return {0, K};
     const int64_t tiles = ceil_div(M, 256) * ceil_div(N, 256);
     int64_t ks = tiles > 0 ? ceil_div(kRuleCUs, tiles) : 1;
     const int64_t cap = K / 256 > 1 ? K / 256 : 1;
     if (ks > cap) ks = cap;
     if (ks > 8) ks = 8;
     if (ks < 1) ks = 1;
-    const int64_t kq = round_up(ceil_div(K, ks), 16);
+    const int64_t kq = round_up(ceil_div(K, ks), 32);
     return {ceil_div(K, kq), kq};   // every slice non-empty
 }
 

@@ -242,18 +242,20 @@ drgg_status router_gemm_fp32_bf16x3(const float *X, const float *Wr, int64_t M, 
                                     int64_t K, float *out, hipStream_t stream);
 
 /*
- * The same FP32 router GEMM (the same BF16x3 products, PR #8363, Summary)
- * on 256x256 output tiles with the reduction cut into ks slices of kq values
- * (drgg_router_split): slice 0 is summed into `out`, slices 1 .. ks-1 into
- * the workspace, and a second kernel adds them to `out` in slice order, so
- * the result is deterministic (a function of M, N, K; it is not bitwise the
- * single-pass call above, whose sum runs over all of K in one chain).
- * Arguments and limits as router_gemm_fp32_bf16x3, except K <= 2^21
- * (DRGG_ESHAPE otherwise); `workspace` is a DEVICE
- * buffer of at least router_workspace_size bytes, 16-byte aligned (may be
- * NULL when that size is 0), owned by the caller and overwritten; calls that
- * share one workspace must not overlap.  DRGG_EWORKSPACE if it is missing or
- * too small, DRGG_EALIGN if misaligned.
+ * The same FP32 router GEMM (the same BF16x3 products, PR #8363, Summary),
+ * in the program drgg_router_split picks from (M, N, K): when the single-pass
+ * program's 128x128 tiles alone fill 256 workgroups (or K > 2^21) that
+ * program runs, as router_gemm_fp32_bf16x3; otherwise the sliced program:
+ * 256x256 output tiles with the reduction cut into ks slices of kq values,
+ * slice 0 summed into `out`, slices 1 .. ks-1 into the workspace, and a second
+ * kernel adding them to `out` in slice order.  Deterministic either way (a
+ * function of M, N, K; the sliced result is not bitwise the single-pass one,
+ * whose sum runs over all of K in one chain).  Arguments and limits as
+ * router_gemm_fp32_bf16x3; `workspace` is a DEVICE buffer of at least
+ * router_workspace_size bytes, 16-byte aligned (may be NULL when that size is
+ * 0), owned by the caller and overwritten; calls that share one workspace
+ * must not overlap.  DRGG_EWORKSPACE if it is missing or too small,
+ * DRGG_EALIGN if misaligned.
  */
 drgg_status router_gemm_fp32_bf16x3_ws(const float *X, const float *Wr, int64_t M, int64_t N,
                                        int64_t K, float *out, void *workspace,
@@ -261,16 +263,18 @@ drgg_status router_gemm_fp32_bf16x3_ws(const float *X, const float *Wr, int64_t 
 
 /*
  * Workspace bytes (to *bytes, a HOST pointer) of router_gemm_fp32_bf16x3_ws:
- * (ks - 1) * M * N * 4 (PR #8363, Summary, the router GEMM).  Shape errors as
- * router_gemm_fp32_bf16x3_ws.
+ * (ks - 1) * M * N * 4 for the sliced program, else 0 (PR #8363, Summary,
+ * the router GEMM).  Shape errors as router_gemm_fp32_bf16x3.
  */
 drgg_status router_workspace_size(int64_t M, int64_t N, int64_t K, size_t *bytes);
 
 /*
- * The reduction slices of router_gemm_fp32_bf16x3_ws (host only): *ks slices
- * of *kq values (a multiple of 16; the last slice may be shorter), with
- * ceil(M/256) * ceil(N/256) * ks workgroups reaching 256 where K allows
- * (at most 8 slices, none shorter than 256 values).  HOST pointers.
+ * The program router_gemm_fp32_bf16x3_ws runs (host only, HOST pointers):
+ * *ks = 0 (and *kq = K) for the single-pass program, which runs when
+ * ceil(M/128) * ceil(N/128) >= 256 or K > 2^21; else *ks slices of *kq values
+ * (a multiple of 32; the last slice may be shorter), with
+ * ceil(M/256) * ceil(N/256) * ks workgroups reaching 256 where K allows (at
+ * most 8 slices, none shorter than 256 values).
  */
 drgg_status drgg_router_split(int64_t M, int64_t N, int64_t K, int64_t *ks, int64_t *kq);
 

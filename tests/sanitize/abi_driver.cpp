@@ -87,18 +87,20 @@ int main() {
            DRGG_ESHAPE);
     {
         size_t rw = 0;
+        EXPECT(router_workspace_size(2048, 256, 4096, &rw), DRGG_OK);
+        EXPECT(rw == size_t(7) * 2048 * 256 * 4 ? DRGG_OK : DRGG_EINVAL, DRGG_OK);
         EXPECT(router_workspace_size(16384, 256, 4096, &rw), DRGG_OK);
-        EXPECT(rw == size_t(3) * 16384 * 256 * 4 ? DRGG_OK : DRGG_EINVAL, DRGG_OK);
-        EXPECT(router_gemm_fp32_bf16x3_ws(static_cast<float*>(A), static_cast<float*>(A), 16384, 256, 4096,
+        EXPECT(rw == 0 ? DRGG_OK : DRGG_EINVAL, DRGG_OK);
+        EXPECT(router_gemm_fp32_bf16x3_ws(static_cast<float*>(A), static_cast<float*>(A), 2048, 256, 4096,
                                           static_cast<float*>(A), nullptr, 0, nullptr),
                DRGG_EWORKSPACE);
         int64_t ks = 0, kq = 0;
         for (int64_t M : {1, 255, 256, 16384, 65536})
             for (int64_t K : {8, 200, 4096, 4104}) {
                 EXPECT(drgg_router_split(M, 256, K, &ks, &kq), DRGG_OK);
-                EXPECT(ks >= 1 && ks <= 8 && kq % 16 == 0 && (ks - 1) * kq < K && ks * kq >= K ? DRGG_OK
-                                                                                          : DRGG_EINVAL,
-                       DRGG_OK);
+                const bool single = ks == 0 && kq == K;
+                const bool sliced = ks >= 1 && ks <= 8 && kq % 32 == 0 && (ks - 1) * kq < K && ks * kq >= K;
+                EXPECT(single || sliced ? DRGG_OK : DRGG_EINVAL, DRGG_OK);
             }
     }
     // planning and the rules behind it, for a range of shapes and CU counts

@@ -145,8 +145,13 @@ def test_dense_square_bf16(drgg, program):
     assert np.array_equal(bits(run_program(drgg, program, dv, torch.bfloat16, True)), bits(out))
 
 
-def test_router_full_size(drgg):
+@pytest.mark.parametrize("rows", [16384, 8192])
+def test_router_full_size(drgg, rows):
+    """The router workload (16384 tokens: the single-pass program) and its
+    first 8192 tokens (the sliced program, 8 reduction slices)."""
     X, Wr = synth.router_inputs()
+    X = np.ascontiguousarray(X[:rows])
+    print(f"router {rows} tokens: program {drgg.router_split(rows, Wr.shape[0], X.shape[1])}", flush=True)
     out = drgg.router_gemm_fp32_bf16x3(parity.to_dev(X), parity.to_dev(Wr))
     o = parity.from_dev(out).ravel().astype(np.float64)
     rng = np.random.default_rng(0)

@@ -149,28 +149,31 @@ def test_router_sliced_argument_checks_and_split_rule(drgg):
     ws_status = {int(s) for s in range(0, 12) if "workspace" in drgg.status_string(s)}
     assert r(0, A16, 16, 256, 16, A16, None, 0, None) == 1
     assert r(A16, A16, 16, 256, 12, A16, None, 0, None) == 3
-    assert r(A16, A16, 16, 256, 2 ** 21 + 8, A16, None, 0, None) == 2          # 256-row blocks: K <= 2^21
-    assert r(A16, A16, 16384, 256, 4096, A16, None, 0, None) in ws_status      # 3 slices need 48 MiB
-    assert r(A16, A16, 16384, 256, 4096, A16, A16 + 4, 3 * 16384 * 256 * 4, None) == 3
-    # the rule: ceil(M/256) * ceil(N/256) * ks reaches 256 workgroups, at most
-    # 8 slices, none shorter than 256 values, whole 16-value stages
-    assert drgg.router_split(16384, 256, 4096) == (4, 1024)
+    assert r(A16, A16, 16, 256, 2 ** 22 + 8, A16, None, 0, None) == 2
+    assert r(A16, A16, 2048, 256, 4096, A16, None, 0, None) in ws_status      # 7 slices need 14 MiB
+    assert r(A16, A16, 2048, 256, 4096, A16, A16 + 4, 7 * 2048 * 256 * 4, None) == 3
+    # the program: single pass (ks = 0) once its 128x128 tiles fill 256
+    # workgroups; else slices so that ceil(M/256) * ceil(N/256) * ks reaches
+    # 256, at most 8, none shorter than 256 values, whole 32-value pairs
+    assert drgg.router_split(16384, 256, 4096) == (0, 4096)
+    assert drgg.router_split(65536, 256, 4096) == (0, 4096)
+    assert drgg.router_split(16, 256, 2 ** 21 + 8) == (0, 2 ** 21 + 8)
+    assert drgg.router_split(8192, 256, 4096) == (8, 512)
     assert drgg.router_split(2048, 256, 4096) == (8, 512)
-    assert drgg.router_split(65536, 256, 4096) == (1, 4096)
-    assert drgg.router_split(300, 256, 520) == (2, 272)
+    assert drgg.router_split(300, 256, 520) == (2, 288)
     assert drgg.router_split(128, 128, 64) == (1, 64)
-    assert drgg.router_workspace_size(16384, 256, 4096) == 3 * 16384 * 256 * 4
-    assert drgg.router_workspace_size(65536, 256, 4096) == 0
+    assert drgg.router_workspace_size(2048, 256, 4096) == 7 * 2048 * 256 * 4
+    assert drgg.router_workspace_size(16384, 256, 4096) == 0
     rng = np.random.default_rng(3)
-    for _ in range(200):
+    for _ in range(300):
         M, N, K = int(rng.integers(1, 1 << 17)), 4 * int(rng.integers(1, 300)), 8 * int(rng.integers(1, 2048))
         ks, kq = drgg.router_split(M, N, K)
-        tiles = -(-M // 256) * -(-N // 256)
-        assert 1 <= ks <= 8 and kq % 16 == 0 and (ks - 1) * kq < K <= ks * kq
-        assert ks == 1 or kq >= 256 or K < 512
-        assert tiles * ks <= max(256 + tiles, tiles)
-    with pytest.raises(drgg.DrggError):
-        drgg.router_split(16, 256, 2 ** 21 + 8)
+        if ks == 0:
+            assert kq == K and -(-M // 128) * -(-N // 128) >= 256
+            continue
+        assert -(-M // 128) * -(-N // 128) < 256
+        assert 1 <= ks <= 8 and kq % 32 == 0 and (ks - 1) * kq < K <= ks * kq
+        assert ks == 1 or kq >= 256
 
 
 def test_knob_checks(drgg):
