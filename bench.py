@@ -20,7 +20,8 @@ algorithmic FLOP per step / time per step), plus
   HIP-graph replays, the pages' timing protocol);
 * other_workloads: every other configuration (tiny MoE, the dense weight
   gradients, the gate_up split program, the Zipf-routed down weight
-  gradient, the square projection and the FP32 router), each program
+  gradient, the square projection and the FP32 router, also at 8192
+  tokens where it runs the program with reduction slices), each program
   measured the same way; with --all also the head-batched projection and
   the checkpointed step.
 
@@ -270,7 +271,8 @@ def trace_mark(torch):
 OTHER_ORDER = (["tiny_moe_fwd", "tiny_moe_dgrad", "tiny_moe_wgrad_det", "tiny_moe_wgrad_splitk"] +
                [f"dense_wgrad_n{d}_{v}" for d in (48, 64, 512, 1024) for v in ("det", "splitk")] +
                ["moe_gate_up_wgrad_splitk", "moe_down_zipf_wgrad_det", "moe_down_zipf_wgrad_splitk",
-                "dense_square_fwd", "dense_square_dgrad", "dense_square_wgrad", "router_fp32_bf16x3"])
+                "dense_square_fwd", "dense_square_dgrad", "dense_square_wgrad", "router_fp32_bf16x3",
+                "router_fp32_bf16x3_t8192"])
 OTHER_ORDER_ALL = OTHER_ORDER + ["mla_heads_fwd", "mla_heads_dgrad", "mla_heads_wgrad",
                                  "moe_gate_up_ckpt", "moe_gate_up_ckpt_es"]
 
@@ -349,20 +351,25 @@ def config_workloads(torch, drgg, synth, flush, args, prob3):
         out[name] = program_entry(torch, drgg, fn, flop, flush, args, out=o)
         log(f"{name}: {out[name]['us']:.1f} us warm, cold eager {out[name].get('cold_eager_us')}")
     del X, W, G, Y, dX, dW
-    # FP32 router as a BF16x3 split
-    Xr, Wr = synth.router_inputs()
-    Xr, Wr = torch.from_numpy(Xr).cuda(), torch.from_numpy(Wr).cuda()
-    R = torch.empty((Xr.shape[0], Wr.shape[0]), dtype=torch.float32, device="cuda")
-    flop = 2.0 * Xr.shape[0] * Wr.shape[0] * Xr.shape[1]
-    byt = 4.0 * (Xr.numel() + Wr.numel() + R.numel())
-    trace_mark(torch)
-    e = program_entry(torch, drgg, lambda: drgg.router_gemm_fp32_bf16x3(Xr, Wr, out=R), flop, flush, args, out=R,
-                      byt=byt)
-    e["tflops_fp32_logical"] = e.pop("tflops")
-    e["tflops_mfma"] = 3 * e["tflops_fp32_logical"]
-    e["pct_peak_mfma"] = 3 * e.pop("pct_peak")
-    out["router_fp32_bf16x3"] = e
-    log(f"router: {e['us']:.1f} us warm, cold eager {e.get('cold_eager_us')}")
+    # FP32 router as a BF16x3 split: the 16384-token workload (single-pass
+    # program) and its first 8192 tokens (the program with reduction slices)
+    Xr0, Wr = synth.router_inputs()
+    Wr = torch.from_numpy(Wr).cuda()
+    for key, rows in (("router_fp32_bf16x3", Xr0.shape[0]), ("router_fp32_bf16x3_t8192", 8192)):
+        Xr = torch.from_numpy(np.ascontiguousarray(Xr0[:rows])).cuda()
+        R = torch.empty((rows, Wr.shape[0]), dtype=torch.float32, device="cuda")
+        flop = 2.0 * rows * Wr.shape[0] * Xr.shape[1]
+        byt = 4.0 * (Xr.numel() + Wr.numel() + R.numel())
+        trace_mark(torch)
+        e = program_entry(torch, drgg, lambda: drgg.router_gemm_fp32_bf16x3(Xr, Wr, out=R), flop, flush, args,
+                          out=R, byt=byt)
+        e["tflops_fp32_logical"] = e.pop("tflops")
+        e["tflops_mfma"] = 3 * e["tflops_fp32_logical"]
+        e["pct_peak_mfma"] = 3 * e.pop("pct_peak")
+        e["program"] = dict(zip(("slices", "values_per_slice"), drgg.router_split(rows, Wr.shape[0], Xr.shape[1])))
+        out[key] = e
+        log(f"{key}: {e['us']:.1f} us warm, cold eager {e.get('cold_eager_us')}")
+        del Xr, R
     return out
 
 
