@@ -173,6 +173,17 @@ def test_deterministic_on_fewer_cus(drgg, n_cus):
                     finally:
                         drgg.set_knob(drgg.KNOB_GRID, 0)
                     assert np.array_equal(bits(out), ref), f"{program}: {n_cus} CUs (grid {grid}) changed the bits"
+        # the router's sliced program (8 reduction slices here) and its fold
+        X, Wr = synth.router_inputs(1024, 256, 2048, cfg_seed=11)
+        Xd, Wd = parity.to_dev(X), parity.to_dev(Wr)
+        assert drgg.router_split(1024, 256, 2048)[0] == 8
+        ref = drgg.router_gemm_fp32_bf16x3(Xd, Wd).view(torch.int32).cpu()
+        print(f"fewer CUs: {n_cus} CUs, router", flush=True)
+        ws = torch.empty(drgg.router_workspace_size(1024, 256, 2048), dtype=torch.uint8, device="cuda")
+        with torch.cuda.stream(ext):
+            out = drgg.router_gemm_fp32_bf16x3(Xd, Wd, workspace=ws)
+        ext.synchronize()
+        assert torch.equal(out.view(torch.int32).cpu(), ref), f"router: {n_cus} CUs changed the bits"
     finally:
         torch.cuda.synchronize()
         hip.hipStreamDestroy(stream)
