@@ -543,8 +543,9 @@ drgg_status batched_gemm_wgrad(const void* X, const void* G, const drgg_batched*
 
 // Router argument checks shared by both entry points and the size query.
 static drgg_status check_router(int64_t M, int64_t N, int64_t K) {
-    // N, K <= 2^22 keep every per-lane byte offset inside a 256-row block of
-    // the operands and of the output below 2^31
+    // N, K <= 2^22 keep every per-lane byte offset inside a 128-row block of
+    // the operands (the single-pass program; the sliced one, with 256-row
+    // blocks, runs only for K <= 2^21) and of the output below 2^31
     if (M < 0 || N < 1 || K < 8 || M > INT32_MAX || N > (int64_t(1) << 22) || K > (int64_t(1) << 22))
         return DRGG_ESHAPE;
     if (K % 8 != 0 || N % 4 != 0) return DRGG_EALIGN;
