@@ -8,6 +8,7 @@ Integer-valued inputs are compared bit for bit in every mode.
 import numpy as np
 import pytest
 
+import oracle
 import synth
 from tests import parity
 
@@ -133,6 +134,26 @@ def test_wgrad_unit_remainders_bitwise(drgg, det):
         torch.cuda.synchronize()
         parity.compare(prob, "wgrad", parity.from_dev(out), out_dtype == torch.bfloat16, integer=True,
                        what=f"unit remainders det={det}")
+
+
+def test_wgrad_share_clamp_skewed_bitwise(drgg):
+    """A skewed routing where the chunk rule raises the chunk length to one
+    reference CU's share (64 Zipf-routed experts, 4 of them empty: the
+    balanced expert stays whole, the long ones are cut into chunks of at
+    least 768 tokens); integer inputs, every element of both programs bit for
+    bit (one oracle evaluation for both)."""
+    counts = synth.zipf_counts(4321, 24576, 64, 4, 1.2)
+    prob = synth.make_problem("share_clamp", 302, counts, N=512, K=1024, integer=True)
+    cm = drgg.plan(drgg.OP_WGRAD, prob.E, prob.M, prob.N, prob.K, drgg.FP32, True)["chunk_max"]
+    assert cm == 768 and drgg.wgrad_chunking(int(counts.max()), cm)[1] > 1
+    dv = dev_inputs(prob)
+    want = oracle.round_f32(parity.oracle_program(prob, "wgrad", None)[0]).view(np.uint32)
+    for det in (True, False):
+        print(f"share clamp det={det} chunk_max={cm} max T={counts.max()}", flush=True)
+        out = run_program(drgg, "wgrad", dv, torch.float32, det)
+        torch.cuda.synchronize()
+        got = parity.from_dev(out).astype(np.float32).view(np.uint32)
+        assert np.array_equal(got.ravel(), want.ravel()), f"share clamp det={det}: integer inputs must match bit for bit"
 
 
 SPLIT_CASE = (106, 3, 4000, 264, 520, (1,))   # two experts of about 2000 tokens: cut into chunks
