@@ -177,8 +177,8 @@ __device__ void build_schedule(Sched& s, const int32_t* __restrict__ offs, int E
 // prefix of work(p) over positions p < npos (a plan may give an expert more
 // than one position: the tail-only plan of the deterministic weight
 // gradient has its whole tiles at p and its chunks at E + p).  `scr` is
-// 8 KB of LDS that is free until the first stage load; `clen(T)` is an
-// expert's chunk length.  Both must be called by all threads and end with a
+// 4 KB of LDS that is free until the first stage load; `clen(e)` is expert
+// e's chunk length.  Both must be called by all threads and end with a
 // barrier; rank_experts after build_schedule.
 static_assert(kMaxExperts <= 2 * kMaxGemmThreads && kMaxExperts <= 32767, "16-bit expert order in Sched::scan");
 __device__ __forceinline__ int expert_at(const Sched& s, int p) {
@@ -189,7 +189,7 @@ __device__ void rank_experts(Sched& s, lds_t* scr, int E, LenFn clen) {
     static_assert(kMaxExperts <= 4 * kGemmThreads, "at most four experts per thread");
     const int tid = threadIdx.x, nthr = blockDim.x;
     auto* key = reinterpret_cast<__attribute__((address_space(3))) int32_t*>(scr);
-    for (int e = tid; e < E; e += nthr) key[e] = clen(s.offs[e + 1] - s.offs[e]);
+    for (int e = tid; e < E; e += nthr) key[e] = clen(e);
     __syncthreads();
     // rank of expert e: experts with a longer chunk, or as long and a lower
     // index, go first; each thread ranks its (up to four) experts in one
@@ -201,10 +201,19 @@ __device__ void rank_experts(Sched& s, lds_t* scr, int E, LenFn clen) {
         k4[u] = e < E ? key[e] : 0;
         r4[u] = 0;
     }
-    for (int f = 0; f < E; ++f) {
-        const int32_t kf = key[f];
+    if (E <= nthr) {
+        // one expert per thread; waves without an expert skip the pass
+        if ((tid & ~63) < E)
+            for (int f = 0; f < E; ++f) {
+                const int32_t kf = key[f];
+                r4[0] += kf > k4[0] || (kf == k4[0] && f < tid);
+            }
+    } else {
+        for (int f = 0; f < E; ++f) {
+            const int32_t kf = key[f];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) r4[u] += kf > k4[u] || (kf == k4[u] && f < tid + u * nthr);
+            for (int u = 0; u < 4; ++u) r4[u] += kf > k4[u] || (kf == k4[u] && f < tid + u * nthr);
+        }
     }
     __syncthreads();   // the keys are read; s.scan may be overwritten
     int16_t* perm = reinterpret_cast<int16_t*>(s.scan);
@@ -229,11 +238,6 @@ __device__ void position_prefix(Sched& s, lds_t* scr, int npos, WorkFn work) {
     }
     if (tid == 0) s.prefix[npos] = total;
     __syncthreads();
-}
-template <class LenFn, class WorkFn>
-__device__ void order_longest_first(Sched& s, lds_t* scr, int E, LenFn clen, WorkFn work) {
-    rank_experts(s, scr, E, clen);
-    position_prefix(s, scr, E, [&](int q) { return work(s.offs[expert_at(s, q) + 1] - s.offs[expert_at(s, q)]); });
 }
 
 // Work item of round r for the workgroup at (XCD-remapped) index wb of G:
@@ -260,16 +264,42 @@ __device__ __forceinline__ int find_expert(const Sched& s, int n, int32_t w) {
 }
 
 // The deterministic weight gradient's chunk rule (device side of
-// wgrad_chunking in plan.hpp).
+// wgrad_chunking in plan.hpp), in 32-bit unsigned arithmetic: T < 2^31, and a
+// chunk_max of T or more gives one chunk, so it is clamped to T first.  (A
+// 64-bit division is a long integer sequence on this GPU; the prologues
+// evaluate these per expert and the walk per tile.)
 __device__ __forceinline__ int32_t chunk_len_dev(int32_t T, int64_t chunk_max) {
     if (T <= 0) return 0;
-    int64_t s = (T + chunk_max - 1) / chunk_max;
-    int64_t l = (T + s - 1) / s;
+    const uint32_t t = (uint32_t)T;
+    const uint32_t cm = chunk_max < (int64_t)t ? (uint32_t)chunk_max : t;
+    const uint32_t s = (t + cm - 1) / cm;
+    const uint32_t l = (t + s - 1) / s;
     return (int32_t)(((l + kTileK - 1) / kTileK) * kTileK);
 }
 __device__ __forceinline__ int32_t chunks_dev(int32_t T, int64_t chunk_max) {
-    int32_t l = chunk_len_dev(T, chunk_max);
-    return l ? (T + l - 1) / l : 0;
+    const int32_t l = chunk_len_dev(T, chunk_max);
+    return l ? (int32_t)(((uint32_t)T + (uint32_t)l - 1) / (uint32_t)l) : 0;
+}
+
+// Maximum / minimum of a 64-bit value over the lanes of a wave (butterfly
+// shuffles).  An LDS atomic issued by every lane is expanded by the compiler
+// into a loop over the active lanes, 64 dependent steps per wave; reducing
+// first leaves one atomic per wave.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+        const uint64_t o = __shfl_xor((unsigned long long)v, m, 64);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+        const uint64_t o = __shfl_xor((unsigned long long)v, m, 64);
+        v = o < v ? o : v;
+    }
+    return v;
 }
 
 // Estimated time of a planned walk on `workers` workgroups: the items
@@ -278,25 +308,31 @@ __device__ __forceinline__ int32_t chunks_dev(int32_t T, int64_t chunk_max) {
 // tokens; returns the largest per-workgroup load.  The deterministic weight
 // gradient chooses between its two plans with it on kRuleCUs reference
 // workgroups (a function of the plan only, never of the device); the split
-// program on its live grid.  `red` is an LDS word.  Must be called by all
-// threads; ends with a barrier.
+// program on its live grid.  `red` is an LDS word; `tab` is LDS scratch for
+// npos words (the lengths, read once per position).  A workgroup's items
+// have increasing indices, so their positions are found by advancing one
+// pointer.  Must be called by all threads; ends with a barrier.
 template <class LenFn>
 __device__ uint64_t walk_makespan(const Sched& s, int npos, LenFn len, unsigned long long* red,
-                                  int64_t workers = kRuleCUs) {
+                                  __attribute__((address_space(3))) uint32_t* tab, int64_t workers = kRuleCUs) {
     if (threadIdx.x == 0) *red = 0;
+    for (int q = threadIdx.x; q < npos; q += blockDim.x) tab[q] = (uint32_t)len(q);
     __syncthreads();
     const int64_t total = s.prefix[npos];
     uint64_t worst = 0;
     for (int64_t b = threadIdx.x; b < workers; b += blockDim.x) {
         uint64_t load = 0;
+        int q = 0;
         for (int64_t r = 0;; ++r) {
             const int64_t i = snake_item(r, b, workers);
             if (i >= total) break;   // later rounds hold only larger indices
-            load += (uint64_t)len(find_expert(s, npos, (int32_t)i)) + (uint64_t)kItemOverheadTokens;
+            while (s.prefix[q + 1] <= i) ++q;   // stops below npos: i < prefix[npos]
+            load += (uint64_t)tab[q] + (uint64_t)kItemOverheadTokens;
         }
         worst = load > worst ? load : worst;
     }
-    atomicMax(red, (unsigned long long)worst);
+    worst = wave_max_u64(worst);
+    if ((threadIdx.x & 63) == 0) atomicMax(red, (unsigned long long)worst);
     __syncthreads();
     const uint64_t m = *red;
     __syncthreads();
@@ -1316,56 +1352,66 @@ __global__ __launch_bounds__((64 * wgrad_det_waves<BM, BN>())) void gg_wgrad_det
     const int64_t cmax = a.chunk_max;
     const int E = a.E;
     build_schedule(sch, a.offs, E, a.M, a.T, [=](int, int32_t T) { return P * chunks_dev(T, cmax); });
-    // partial slots: experts cut into more than one chunk, in expert order
+    // Per-expert table in three stage buffers, which are free until the first
+    // stage load: chunk length L_e, chunks S_e and, for S_e > 1, the whole
+    // 256-row bands of the tail-only plan (wgrad_whole_rows).  Computed once
+    // here, so that the plan estimates below read it instead of deriving it
+    // again for every position and item.  Only the prologue reads it.
+    typedef __attribute__((address_space(3))) int32_t lds_i32;
+    lds_i32* const tL = reinterpret_cast<lds_i32*>(stg.b[1]);
+    lds_i32* const tS = reinterpret_cast<lds_i32*>(stg.b[2]);
+    lds_i32* const tB = reinterpret_cast<lds_i32*>(stg.b[3]);
+    auto* const tab = reinterpret_cast<__attribute__((address_space(3))) uint32_t*>(stg.a[1]);   // walk scratch
+    int keeps_whole = 0;
+    // ... and the partial slots: experts cut into more than one chunk, in
+    // expert order
     {
         const int nthr = blockDim.x, per = (E + nthr - 1) / nthr;
         const int lo = min((int)threadIdx.x * per, E), hi = min(lo + per, E);
-        auto slots = [&](int x) {
-            const int32_t c = chunks_dev(sch.offs[x + 1] - sch.offs[x], cmax);
-            return c > 1 ? c : 0;
-        };
         int32_t run = 0;
-        for (int x = lo; x < hi; ++x) run += slots(x);
+        for (int x = lo; x < hi; ++x) {
+            const int32_t T = sch.offs[x + 1] - sch.offs[x];
+            const int32_t L = chunk_len_dev(T, cmax);
+            const int32_t S = L ? (int32_t)(((uint32_t)T + (uint32_t)L - 1) / (uint32_t)L) : 0;
+            const int32_t B = S > 1 ? (int32_t)wgrad_whole_rows(T, a.M, a.N, a.K, S) : 0;
+            tL[x] = L;
+            tS[x] = S;
+            tB[x] = B;
+            keeps_whole |= S > 1 && B > 0;
+            run += S > 1 ? S : 0;
+        }
         int32_t total;
-        int32_t acc = block_exclusive_scan(run, reinterpret_cast<__attribute__((address_space(3))) int32_t*>(stg.b[0]),
-                                           &total);
+        int32_t acc = block_exclusive_scan(run, reinterpret_cast<lds_i32*>(stg.b[0]), &total);
         for (int x = lo; x < hi; ++x) {
             slot_base[x] = acc;
-            acc += slots(x);
+            acc += tS[x] > 1 ? tS[x] : 0;
         }
         if (threadIdx.x == 0) slot_base[E] = total;
     }
-    rank_experts(sch, stg.b[0], E, [=](int32_t T) { return chunk_len_dev(T, cmax); });
-    auto T_at = [&](int q) { const int e = expert_at(sch, q); return sch.offs[e + 1] - sch.offs[e]; };
-    // whole 256-row bands of an expert with T tokens in the tail-only plan
-    auto bands = [&](int32_t T) { return (int32_t)wgrad_whole_rows(T, a.M, a.N, a.K, chunks_dev(T, cmax)); };
+    rank_experts(sch, stg.b[0], E, [&](int e) { return tL[e]; });
+    auto e_at = [&](int q) { return expert_at(sch, q); };
+    auto T_of = [&](int e) { return sch.offs[e + 1] - sch.offs[e]; };
     // plan choice on the reference tile (only when some split expert keeps
     // whole bands, else the two plans are the same)
     int tail = 0;
-    int keeps_whole = 0;
-    for (int e = threadIdx.x; e < E; e += blockDim.x) {
-        const int32_t T = sch.offs[e + 1] - sch.offs[e];
-        keeps_whole |= chunks_dev(T, cmax) > 1 && bands(T) > 0;
-    }
     if (E <= kTailPlanMaxExperts && __syncthreads_or(keeps_whole)) {
-        const uint64_t mk_split = [&] {
-            position_prefix(sch, stg.b[0], E, [&](int q) { return P0 * chunks_dev(T_at(q), cmax); });
-            return walk_makespan(sch, E, [&](int q) {
-                const int32_t T = T_at(q);
-                return chunks_dev(T, cmax) > 1 ? chunk_len_dev(T, cmax) : T;
-            }, &s_red);
-        }();
+        position_prefix(sch, stg.b[0], E, [&](int q) { return P0 * tS[e_at(q)]; });
+        const uint64_t mk_split = walk_makespan(sch, E, [&](int q) {
+            const int e = e_at(q);
+            return tS[e] > 1 ? tL[e] : T_of(e);
+        }, &s_red, tab);
         position_prefix(sch, stg.b[0], 2 * E, [&](int q) {
-            const int32_t T = T_at(q < E ? q : q - E), S = chunks_dev(T, cmax);
+            const int e = e_at(q < E ? q : q - E);
+            const int32_t S = tS[e];
             if (S == 0) return 0;                // no tokens: no items
             if (S == 1) return q < E ? 0 : P0;
-            const int32_t w0 = bands(T) * tk0;   // whole reference tiles
+            const int32_t w0 = tB[e] * tk0;      // whole reference tiles
             return q < E ? w0 : (P0 - w0) * S;
         });
         const uint64_t mk_tail = walk_makespan(sch, 2 * E, [&](int q) {
-            const int32_t T = T_at(q < E ? q : q - E);
-            return q < E || chunks_dev(T, cmax) <= 1 ? T : chunk_len_dev(T, cmax);
-        }, &s_red);
+            const int e = e_at(q < E ? q : q - E);
+            return q < E || tS[e] <= 1 ? T_of(e) : tL[e];
+        }, &s_red, tab);
         tail = mk_tail <= mk_split;
     }
     // the fold kernel's per-expert table (the same values from every
@@ -1373,20 +1419,22 @@ __global__ __launch_bounds__((64 * wgrad_det_waves<BM, BN>())) void gg_wgrad_det
     // first row of the partials (rows above it were stored directly)
     if (blockIdx.x == 0)
         for (int e = threadIdx.x; e < E; e += blockDim.x) {
-            const int32_t T = sch.offs[e + 1] - sch.offs[e], S = chunks_dev(T, cmax);
-            const int32_t row0 = tail && S > 1 ? (int32_t)min<int64_t>(a.N, (int64_t)bands(T) * 256) : 0;
-            *reinterpret_cast<int4*>(a.fold_info + 4 * e) = int4{T, S, slot_base[e], row0};
+            const int32_t S = tS[e];
+            const int32_t row0 = tail && S > 1 ? (int32_t)min<int64_t>(a.N, (int64_t)tB[e] * 256) : 0;
+            *reinterpret_cast<int4*>(a.fold_info + 4 * e) = int4{T_of(e), S, slot_base[e], row0};
         }
-    // whole kernel tiles of an expert (a prefix of its row-major tiles)
-    auto nwhole = [&](int32_t T) {
-        return tail && chunks_dev(T, cmax) > 1 ? (int32_t)min<int64_t>(tn, (int64_t)bands(T) * (256 / BM)) * tk : 0;
+    // whole kernel tiles of an expert with S chunks and B whole bands (a
+    // prefix of its row-major tiles)
+    auto whole_tiles = [&](int32_t S, int32_t B) {
+        return tail && S > 1 ? (int32_t)min<int64_t>(tn, (int64_t)B * (256 / BM)) * tk : 0;
     };
     const int npos = tail ? 2 * E : E;
     position_prefix(sch, stg.b[0], npos, [&](int q) {
-        const int32_t T = T_at(q < E ? q : q - E), S = chunks_dev(T, cmax);
+        const int e = e_at(q < E ? q : q - E);
+        const int32_t S = tS[e];
         if (!tail || S == 0) return P * S;   // (no tokens: no items)
         if (S == 1) return q < E ? 0 : P;
-        const int32_t nw = nwhole(T);
+        const int32_t nw = whole_tiles(S, tB[e]);
         return q < E ? nw : (P - nw) * S;
     });
     const int64_t total = uni(sch.prefix[npos]);
@@ -1401,7 +1449,7 @@ __global__ __launch_bounds__((64 * wgrad_det_waves<BM, BN>())) void gg_wgrad_det
         const int32_t oe = uni(sch.offs[e]), oe1 = uni(sch.offs[e + 1]);
         const int32_t T = oe1 - oe;
         const int32_t clen = chunk_len_dev(T, cmax);
-        const int32_t nch = (T + clen - 1) / clen;
+        const int32_t nch = (int32_t)(((uint32_t)T + (uint32_t)clen - 1) / (uint32_t)clen);
         const int32_t local = (int32_t)w - uni(sch.prefix[pos]);
         int32_t tile, chunk = 0;
         bool whole;
@@ -1409,7 +1457,8 @@ __global__ __launch_bounds__((64 * wgrad_det_waves<BM, BN>())) void gg_wgrad_det
             tile = local;
             whole = true;
         } else if (nch > 1) {           // a chunk item: chunk-major, tiles of a chunk adjacent
-            const int32_t nw = nwhole(T), ps = P - nw;
+            const int32_t nw = tail ? whole_tiles(nch, (int32_t)wgrad_whole_rows(T, a.M, a.N, a.K, nch)) : 0;
+            const int32_t ps = P - nw;
             chunk = local / ps;
             tile = nw + local % ps;
             whole = false;
@@ -1590,9 +1639,10 @@ __global__ __launch_bounds__(kGemmThreads) void gg_wgrad_atomic_kernel(GemmArgs 
     const int64_t G = gridDim.x;
     const int tid = threadIdx.x, nthr = blockDim.x;
     build_schedule(sch, a.offs, E, a.M, a.T, [=](int, int32_t) { return 0; });
-    rank_experts(sch, stg.b[0], E, [=](int32_t T) { return unit_chunk_len(T, cmax); });
+    rank_experts(sch, stg.b[0], E, [&](int e) { return unit_chunk_len(sch.offs[e + 1] - sch.offs[e], cmax); });
     auto T_at = [&](int q) { const int e = expert_at(sch, q); return sch.offs[e + 1] - sch.offs[e]; };
     const bool banded = E <= kTailPlanMaxExperts;
+    auto* const tab = reinterpret_cast<__attribute__((address_space(3))) uint32_t*>(stg.a[1]);   // walk scratch
     // whole tiles of each expert: a prefix of its row-major tiles (none for
     // an expert without tokens, which has no items at all); computed once,
     // so that the per-tile decode is a table read
@@ -1659,8 +1709,12 @@ __global__ __launch_bounds__(kGemmThreads) void gg_wgrad_atomic_kernel(GemmArgs 
                 hi = l > hi ? l : hi;
                 lo = l < lo ? l : lo;
             }
-            atomicMax(&s_red, (unsigned long long)hi);
-            atomicMin(&s_min, (unsigned long long)lo);
+            hi = wave_max_u64(hi);
+            lo = wave_min_u64(lo);
+            if ((tid & 63) == 0) {
+                atomicMax(&s_red, (unsigned long long)hi);
+                atomicMin(&s_min, (unsigned long long)lo);
+            }
             __syncthreads();
             const uint64_t lmax = s_red, lmin = s_min;
             // slack placement needs at least the longest tail tile to fit
@@ -1687,7 +1741,8 @@ __global__ __launch_bounds__(kGemmThreads) void gg_wgrad_atomic_kernel(GemmArgs 
                 if (slack) {
                     if (tid == 0) s_red = lmax;
                     __syncthreads();
-                    atomicMax(&s_red, (unsigned long long)top);
+                    top = wave_max_u64(top);
+                    if ((tid & 63) == 0) atomicMax(&s_red, (unsigned long long)top);
                     __syncthreads();
                 }
             }
@@ -1706,12 +1761,12 @@ __global__ __launch_bounds__(kGemmThreads) void gg_wgrad_atomic_kernel(GemmArgs 
                 } else {
                     band_walk();
                     mk_band = walk_makespan(sch, 2 * E, [&](int q) { return q < E ? T_at(q) : L_at(q - E); }, &s_red,
-                                            G);
+                                            tab, G);
                 }
                 split_walk();
                 const uint64_t mk_split = walk_makespan(sch, E, [&](int q) {
                     return S_at(q) > 1 ? L_at(q) : T_at(q);
-                }, &s_red, G);
+                }, &s_red, tab, G);
                 use_band = mk_band <= mk_split;
             }
             slack = slack && use_band;
