@@ -128,10 +128,61 @@ __device__ int32_t block_exclusive_scan(int32_t v, Ptr tmp, int32_t* total) {
 // work(e, T_e).  With no offsets array (a batched call) the groups are
 // uniform: offs[e] = e * T.  Must be called by all threads; ends with a
 // barrier.
+// Lanes of one wave exchanging data through LDS: the fences order each
+// lane's accesses before and after this point for the compiler (no
+// instruction is emitted; the wave's DS instructions execute in order).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Inclusive scans (maximum, sum) over the 64 lanes of a wave.  With fewer
+// than kWaveExperts experts the prologue steps below run on wave 0 alone:
+// shuffles instead of the workgroup scans, one barrier instead of three or
+// more per step (each costs a few hundred cycles at kernel start).
+constexpr int kWaveExperts = 64;
+__device__ __forceinline__ int32_t wave_incl_max(int32_t x) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int32_t y = __shfl_up(x, d, 64);
+        if (lane >= d) x = max(x, y);
+    }
+    return x;
+}
+__device__ __forceinline__ int32_t wave_incl_sum(int32_t x) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int32_t y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+    }
+    return x;
+}
+
 template <class WorkFn>
 __device__ void build_schedule(Sched& s, const int32_t* __restrict__ offs, int E, int64_t M, int64_t T,
                                WorkFn work) {
     const int tid = threadIdx.x, nthr = blockDim.x;
+    if (E < kWaveExperts) {
+        // lane e of wave 0 holds offset e (e <= E)
+        if (tid < 64) {
+            int64_t v = 0;
+            if (tid <= E) v = offs ? (int64_t)offs[tid] : tid * T;
+            v = v < 0 ? 0 : (v > M ? M : v);
+            const int32_t o = wave_incl_max(tid <= E ? (int32_t)v : 0);
+            const int32_t o1 = __shfl_down(o, 1, 64);
+            const int32_t wk = tid < E ? work(tid, o1 - o) : 0;
+            const int32_t incl = wave_incl_sum(wk);
+            if (tid <= E) {
+                s.offs[tid] = o;
+                s.prefix[tid] = incl - wk;
+            }
+        }
+        __syncthreads();
+        return;
+    }
     int32_t* tmp = s.scan;   // free until the prefix is written
     for (int e = tid; e <= E; e += nthr) {
         int64_t v = offs ? (int64_t)offs[e] : e * T;
@@ -189,6 +240,21 @@ __device__ void rank_experts(Sched& s, lds_t* scr, int E, LenFn clen) {
     static_assert(kMaxExperts <= 4 * kGemmThreads, "at most four experts per thread");
     const int tid = threadIdx.x, nthr = blockDim.x;
     auto* key = reinterpret_cast<__attribute__((address_space(3))) int32_t*>(scr);
+    if (E < kWaveExperts) {   // wave 0: lane e ranks expert e (keys exchanged through LDS)
+        if (tid < 64) {
+            const int32_t k0 = tid < E ? clen(tid) : 0;
+            if (tid < E) key[tid] = k0;
+            wave_lds_sync();
+            int32_t r = 0;
+            for (int f = 0; f < E; ++f) {
+                const int32_t kf = key[f];
+                r += kf > k0 || (kf == k0 && f < tid);
+            }
+            if (tid < E) reinterpret_cast<int16_t*>(s.scan)[r] = (int16_t)tid;
+        }
+        __syncthreads();
+        return;
+    }
     for (int e = tid; e < E; e += nthr) key[e] = clen(e);
     __syncthreads();
     // rank of expert e: experts with a longer chunk, or as long and a lower
@@ -225,6 +291,18 @@ __device__ void rank_experts(Sched& s, lds_t* scr, int E, LenFn clen) {
 template <class WorkFn>
 __device__ void position_prefix(Sched& s, lds_t* scr, int npos, WorkFn work) {
     const int tid = threadIdx.x, nthr = blockDim.x;
+    if (npos <= 2 * kWaveExperts) {   // wave 0: lane l holds positions 2l and 2l+1
+        if (tid < 64) {
+            const int q0 = 2 * tid, q1 = q0 + 1;
+            const int32_t w0 = q0 < npos ? work(q0) : 0, w1 = q1 < npos ? work(q1) : 0;
+            const int32_t incl = wave_incl_sum(w0 + w1);
+            if (q0 < npos) s.prefix[q0] = incl - w0 - w1;
+            if (q1 < npos) s.prefix[q1] = incl - w1;
+            if (tid == 63) s.prefix[npos] = incl;
+        }
+        __syncthreads();
+        return;
+    }
     // per-thread runs of positions, then a scan of the run sums
     const int per = (npos + nthr - 1) / nthr;
     const int lo = min(tid * per, npos), hi = min(lo + per, npos);
@@ -716,15 +794,6 @@ __device__ __forceinline__ void store_tile(const Mma& mma, void* out, int64_t ld
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-}
-
-// Lanes of one wave exchanging data through LDS: the fences order each
-// lane's accesses before and after this point for the compiler (no
-// instruction is emitted; the wave's DS instructions execute in order).
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // Write a finished tile like store_tile, but so that every global store
@@ -1364,8 +1433,28 @@ __global__ __launch_bounds__((64 * wgrad_det_waves<BM, BN>())) void gg_wgrad_det
     auto* const tab = reinterpret_cast<__attribute__((address_space(3))) uint32_t*>(stg.a[1]);   // walk scratch
     int keeps_whole = 0;
     // ... and the partial slots: experts cut into more than one chunk, in
-    // expert order
-    {
+    // expert order (wave 0 alone with few experts; the ranking below ends
+    // with the barrier that publishes both)
+    if (E < kWaveExperts) {
+        if (threadIdx.x < 64) {
+            const int x = threadIdx.x;
+            int32_t S = 0;
+            if (x < E) {
+                const int32_t T = sch.offs[x + 1] - sch.offs[x];
+                const int32_t L = chunk_len_dev(T, cmax);
+                S = L ? (int32_t)(((uint32_t)T + (uint32_t)L - 1) / (uint32_t)L) : 0;
+                const int32_t B = S > 1 ? (int32_t)wgrad_whole_rows(T, a.M, a.N, a.K, S) : 0;
+                tL[x] = L;
+                tS[x] = S;
+                tB[x] = B;
+                keeps_whole = S > 1 && B > 0;
+            }
+            const int32_t sl = S > 1 ? S : 0;
+            const int32_t incl = wave_incl_sum(sl);
+            if (x < E) slot_base[x] = incl - sl;
+            if (x == 63) slot_base[E] = incl;
+        }
+    } else {
         const int nthr = blockDim.x, per = (E + nthr - 1) / nthr;
         const int lo = min((int)threadIdx.x * per, E), hi = min(lo + per, E);
         int32_t run = 0;
