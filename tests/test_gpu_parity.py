@@ -136,6 +136,29 @@ def test_wgrad_unit_remainders_bitwise(drgg, det):
                        what=f"unit remainders det={det}")
 
 
+@pytest.mark.parametrize("E", [63, 64, 65])
+def test_expert_count_around_one_wave_bitwise(drgg, E):
+    """Up to 63 experts (64 offsets) the kernels build their schedule, the
+    weight gradient its per-expert table, ranking and walk prefixes on one
+    wave; from 64 on with the workgroup-wide scans.  Skewed (Zipf) routing
+    with three empty experts and some experts cut into chunks, integer
+    inputs: all three programs and both weight-gradient programs match the
+    oracle bit for bit on either side of the boundary."""
+    counts = synth.zipf_counts(500 + E, 10000, E, 3, 1.0)
+    prob = synth.make_problem(f"wave_boundary_E{E}", 500 + E, counts, N=264, K=200, integer=True)
+    plan = drgg.plan(drgg.OP_WGRAD, prob.E, prob.M, prob.N, prob.K, drgg.FP32, True)
+    chunks = [drgg.wgrad_chunking(int(t), plan["chunk_max"])[1] for t in counts]
+    assert max(chunks) > 1 and int((counts == 0).sum()) == 3, (chunks, counts.tolist())
+    dv = dev_inputs(prob)
+    for program in PROGRAMS:
+        for det in ((True, False) if program == "wgrad" else (True,)):
+            print(f"wave boundary E={E} {program} det={det}", flush=True)
+            out = run_program(drgg, program, dv, torch.float32, det)
+            torch.cuda.synchronize()
+            parity.compare(prob, program, parity.from_dev(out), False, integer=True,
+                           what=f"wave boundary E={E} {program} det={det}")
+
+
 def test_wgrad_share_clamp_skewed_bitwise(drgg):
     """A skewed routing where the chunk rule raises the chunk length to one
     reference CU's share (64 Zipf-routed experts, 4 of them empty: the
