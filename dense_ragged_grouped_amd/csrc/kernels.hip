@@ -123,11 +123,6 @@ __device__ int32_t block_exclusive_scan(int32_t v, Ptr tmp, int32_t* total) {
     return r;
 }
 
-// Fills s.offs[0..E] with the offsets clamped into [0, M] (and made
-// non-decreasing), and s.prefix[0..E] with the exclusive prefix of
-// work(e, T_e).  With no offsets array (a batched call) the groups are
-// uniform: offs[e] = e * T.  Must be called by all threads; ends with a
-// barrier.
 // Lanes of one wave exchanging data through LDS: the fences order each
 // lane's accesses before and after this point for the compiler (no
 // instruction is emitted; the wave's DS instructions execute in order).
@@ -161,6 +156,12 @@ __device__ __forceinline__ int32_t wave_incl_sum(int32_t x) {
     return x;
 }
 
+// Fills s.offs[0..E] with the offsets clamped into [0, M] (and made
+// non-decreasing), and s.prefix[0..E] with the exclusive prefix of
+// work(e, T_e).  With no offsets array (a batched call) the groups are
+// uniform: offs[e] = e * T.  With fewer than kWaveExperts experts wave 0
+// does it all (offsets on lanes 0..E, shuffle scans).  Must be called by all
+// threads; ends with a barrier.
 template <class WorkFn>
 __device__ void build_schedule(Sched& s, const int32_t* __restrict__ offs, int E, int64_t M, int64_t T,
                                WorkFn work) {
