@@ -159,6 +159,28 @@ def test_expert_count_around_one_wave_bitwise(drgg, E):
                            what=f"wave boundary E={E} {program} det={det}")
 
 
+def test_forward_and_data_gradient_same_bits_across_one_wave_boundary(drgg):
+    """The same 63 experts as a 63-expert call (one-wave schedule) and as a
+    64-expert call whose last expert is empty (workgroup-wide schedule):
+    the forward and data gradient compute the same tiles the same way, so
+    their outputs are equal bit for bit (random inputs, FP32 and BF16)."""
+    counts = np.append(synth.zipf_counts(640, 9000, 63, 2, 1.0), 0)
+    prob = synth.make_problem("wave_boundary_pair", 640, counts, N=200, K=328)
+    dv = dev_inputs(prob)
+    offs63 = dv["offs"][:64].clone()
+    W63 = dv["W"][:63].contiguous()
+    for out_dtype in (torch.float32, torch.bfloat16):
+        y64 = drgg.grouped_gemm_fwd(dv["X"], dv["W"], dv["offs"], out_dtype=out_dtype)
+        y63 = drgg.grouped_gemm_fwd(dv["X"], W63, offs63, out_dtype=out_dtype)
+        g64 = drgg.grouped_gemm_dgrad(dv["G"], dv["W"], dv["offs"], out_dtype=out_dtype)
+        g63 = drgg.grouped_gemm_dgrad(dv["G"], W63, offs63, out_dtype=out_dtype)
+        torch.cuda.synchronize()
+        iv = torch.int32 if out_dtype == torch.float32 else torch.int16
+        assert torch.equal(y64.view(iv), y63.view(iv)), f"forward {out_dtype}"
+        assert torch.equal(g64.view(iv), g63.view(iv)), f"data gradient {out_dtype}"
+    parity.compare(prob, "fwd", parity.from_dev(y64), True, what="wave boundary pair forward")
+
+
 def test_wgrad_share_clamp_skewed_bitwise(drgg):
     """A skewed routing where the chunk rule raises the chunk length to one
     reference CU's share (64 Zipf-routed experts, 4 of them empty: the
