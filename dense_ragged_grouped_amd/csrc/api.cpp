@@ -389,6 +389,9 @@ drgg_status run_wgrad(const void* X, const void* G, const int32_t* group_offsets
         a.fold_info = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + p.max_partials * N * K * 4);
         a.chunk_max = p.chunk_max;
         a.items_max = M > 0 ? p.grid : 0;
+        // an expert has at most M tokens: with chunk_max >= M none is cut
+        // into chunks, and the fold would only zero the empty experts
+        a.zero_empty = M > 0 && p.chunk_max >= M;
         return launch_status(launch_wgrad_det(p.tile, a, bf16, stream));
     }
     const int64_t P = ceil_div(N, p.ts.bm) * ceil_div(K, p.ts.bn);

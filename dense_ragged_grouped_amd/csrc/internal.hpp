@@ -34,6 +34,8 @@ struct GemmArgs {
     int32_t reverse;       // walk work items in reverse (test knob)
     int32_t delay_seed;    // split program: seeded delays before tail arrivals (test knob; 0 = off)
     int32_t* report;       // split program: if set, workgroup 0 writes its tail decision here (test aid)
+    int32_t zero_empty;    // det wgrad: no expert can have two chunks, so no fold runs and the chunk
+                           // kernel writes the zero output of experts without tokens itself
 };
 
 // op 0: forward; 1: data gradient; 2: data gradient with a.B = W^T [E][K][N]

@@ -1529,6 +1529,27 @@ __global__ __launch_bounds__((64 * wgrad_det_waves<BM, BN>())) void gg_wgrad_det
     });
     const int64_t total = uni(sch.prefix[npos]);
     const int64_t G = gridDim.x;
+    if (a.zero_empty) {
+        // no fold kernel follows: the experts without tokens (which have no
+        // items) get their zero output here, spread over all workgroups
+        int any = 0;
+        for (int e = threadIdx.x; e < E; e += blockDim.x) any |= T_of(e) == 0;
+        if (__syncthreads_or(any)) {
+            const int64_t nk8 = a.N * a.K / 8;   // K is a multiple of 8
+            const int64_t n8 = (int64_t)E * nk8;
+            for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += G * blockDim.x) {
+                const int e = (int)(i / nk8);
+                if (T_of(e) != 0) continue;
+                if constexpr (OUT_BF16) {
+                    *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.out) + i * 8) = u32x4{0u, 0u, 0u, 0u};
+                } else {
+                    f32x4* d = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + i * 8);
+                    d[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    d[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+        }
+    }
     int64_t wb = xcd_remap(blockIdx.x, G), round = 0;
     if (a.reverse) wb = G - 1 - wb;
     int64_t w = snake_item(0, wb, G);
@@ -2555,6 +2576,10 @@ static hipError_t launch_wgrad_det_t(const GemmArgs& a, bool bf16, hipStream_t s
         else hipLaunchKernelGGL((gg_wgrad_det_kernel<BM, BN, false>), grid, block, 0, s, a);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
+    }
+    if (a.zero_empty && a.items_max > 0) {   // nothing to fold (see zero_empty)
+        timing_end(s);
+        return hipSuccess;
     }
     const int64_t nk = a.N * a.K;
     dim3 fgrid((unsigned)((nk + kThreads * 8 - 1) / (kThreads * 8)), (unsigned)a.E);

@@ -181,6 +181,33 @@ def test_forward_and_data_gradient_same_bits_across_one_wave_boundary(drgg):
     parity.compare(prob, "fwd", parity.from_dev(y64), True, what="wave boundary pair forward")
 
 
+@pytest.mark.parametrize("out_dtype", ["fp32", "bf16"])
+def test_wgrad_without_fold_zeroes_empty_experts(drgg, out_dtype):
+    """When no expert can be cut into chunks (chunk_max >= M) the
+    deterministic weight gradient runs without its fold kernel, and the
+    chunk kernel itself writes the zero output of experts without tokens:
+    here 8 of 16 experts are empty and the output buffer starts as NaN;
+    integer inputs, so every expert matches the oracle bit for bit."""
+    counts = np.zeros(16, dtype=np.int64)
+    counts[[0, 2, 3, 7, 8, 11, 13, 15]] = [61, 5, 77, 1, 40, 99, 18, 63]
+    prob = synth.make_problem("no_fold_empty", 660, counts, N=72, K=136, integer=True)
+    plan = drgg.plan(drgg.OP_WGRAD, prob.E, prob.M, prob.N, prob.K, drgg.FP32, True)
+    assert plan["chunk_max"] >= prob.M, plan
+    dv = dev_inputs(prob)
+    dt = torch.float32 if out_dtype == "fp32" else torch.bfloat16
+    dW = torch.full((prob.E, prob.N, prob.K), float("nan"), dtype=dt, device="cuda")
+    drgg.set_knob(drgg.KNOB_TIMING, 1)
+    try:
+        drgg.grouped_gemm_wgrad(dv["X"], dv["G"], dv["offs"], out_dtype=dt, deterministic=True, out=dW)
+        kernels = [name for name, _ in drgg.last_call_kernel_times()]
+    finally:
+        drgg.set_knob(drgg.KNOB_TIMING, 0)
+    torch.cuda.synchronize()
+    assert kernels == ["gg_wgrad_det_kernel"], kernels
+    parity.compare(prob, "wgrad", parity.from_dev(dW), out_dtype == "bf16", integer=True,
+                   what=f"no fold, empty experts, {out_dtype}")
+
+
 def test_wgrad_share_clamp_skewed_bitwise(drgg):
     """A skewed routing where the chunk rule raises the chunk length to one
     reference CU's share (64 Zipf-routed experts, 4 of them empty: the
