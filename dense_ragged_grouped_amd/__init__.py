@@ -27,6 +27,7 @@ BF16, FP32 = 0, 1
 OP_FWD, OP_DGRAD, OP_WGRAD = 0, 1, 2
 KNOB_TILE, KNOB_GRID, KNOB_REVERSE, KNOB_TIMING, KNOB_NONDET = 1, 2, 3, 4, 5
 KNOB_CHECK_OFFSETS, KNOB_CHECK_WORKSPACE, KNOB_DELAY_SEED, KNOB_SPLIT_REPORT = 6, 7, 8, 9
+KNOB_DGRAD_WT = 10
 TILE_AUTO, TILE_256x256, TILE_128x128, TILE_256x128, TILE_128x256, TILE_64x256 = range(6)
 
 # the symbols include/drgg.h declares
@@ -450,7 +451,9 @@ def grouped_gemm_dgrad(G, W, group_offsets, out_dtype=None, deterministic=True, 
                        stream=None):
     """dX[t] = G[t] W[e(t)] with FP32 accumulation.  `workspace` (a Workspace,
     a device tensor, None for the default buffer, or False for none) holds
-    W^T, which makes the product faster; the result is bitwise the same."""
+    W^T, which makes the product faster when the experts average at least
+    3072 tokens (below that no W^T is made and the default buffer is not
+    allocated); the result is bitwise the same either way."""
     torch = _torch()
     _need(G, torch.bfloat16, "G", 2)
     _need(W, torch.bfloat16, "W", 3)

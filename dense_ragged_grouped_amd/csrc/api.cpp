@@ -30,6 +30,8 @@ std::atomic<int64_t> g_knob_check_offsets{0}, g_knob_check_ws{0};
 // Split-program test aids: seeded delays before tail arrivals, and a device
 // address (4 int32) where the kernel reports its tail decision.
 std::atomic<int64_t> g_knob_delay{0}, g_knob_report{0};
+// DRGG_KNOB_DGRAD_WT: 1 = the data gradient uses a W^T workspace whatever its token count
+std::atomic<int64_t> g_knob_dgrad_wt{0};
 
 bool env_flag(const char* name) {
     const char* v = std::getenv(name);
@@ -203,7 +205,8 @@ drgg_status make_plan(drgg_op op, int32_t E, int64_t M, int64_t N, int64_t K, in
         if (op == DRGG_OP_DGRAD) {   // optional: room for W^T
             int64_t b;
             if (!mul_ok((int64_t)E * N, K, &b) || !mul_ok(b, 2, &b)) return DRGG_EOVERFLOW;
-            p->ws_bytes = (size_t)round_up(b, 256);
+            const bool wt = g_knob_dgrad_wt.load() != 0 || dgrad_transposes_w(E, M);
+            p->ws_bytes = wt ? (size_t)round_up(b, 256) : 0;
         }
         return p->grid > INT32_MAX ? DRGG_ESHAPE : DRGG_OK;
     }
@@ -758,6 +761,9 @@ drgg_status drgg_set_knob(int knob, int64_t value) {
         case DRGG_KNOB_SPLIT_REPORT:
             if (value < 0 || (value & 15) != 0) return DRGG_EINVAL;
             g_knob_report.store(value);
+            return DRGG_OK;
+        case DRGG_KNOB_DGRAD_WT:
+            g_knob_dgrad_wt.store(value != 0);
             return DRGG_OK;
         default:
             return DRGG_EINVAL;

@@ -81,6 +81,16 @@ DRGG_HD inline void wgrad_chunking(int64_t T, int64_t chunk_max, int64_t* len, i
 // steps.
 constexpr int64_t kItemOverheadTokens = 256;
 
+// The data gradient transposes W into its workspace (W^T, so that both
+// operands are reduction-contiguous) only when the experts average at least
+// this many tokens.  The transposed program saves a fraction of the
+// product's time, which grows with the tokens that meet each W element,
+// while the transpose costs a read and a write of every W element and a
+// launch; on MI355X it pays from about 4096 tokens per expert on and loses
+// at 2048 and below.
+constexpr int64_t kTransposeMinTokens = 3072;
+DRGG_HD inline bool dgrad_transposes_w(int64_t E, int64_t M) { return M >= kTransposeMinTokens * E; }
+
 // Deterministic weight gradient, chunk rule part 1 (host): the longest chunk
 // an expert's token range is cut into.  A function of (E, M, N, K) only.
 //   P0    = output tiles per expert at a 256x256 reference tile

@@ -128,13 +128,16 @@ drgg_status grouped_gemm_fwd(const void *X, const void *W, const int32_t *group_
 
 /*
  * Data gradient: dX[t,k] = sum_n G[t,n] * W[e(t),n,k].  G [M,N] BF16,
- * W [E,N,K] BF16, dX [M,K] out_dtype.  The workspace is optional: with at
- * least grouped_gemm_workspace_size(DRGG_OP_DGRAD, ...) bytes (E*N*K*2,
- * rounded up to 256; 16-byte aligned) W is first transposed into it
+ * W [E,N,K] BF16, dX [M,K] out_dtype.  The workspace is optional: when the
+ * experts average at least 3072 tokens (M >= 3072 * E) and the workspace has
+ * at least grouped_gemm_workspace_size(DRGG_OP_DGRAD, ...) bytes (E*N*K*2,
+ * rounded up to 256; 16-byte aligned), W is first transposed into it
  * (W^T [E,K,N]) and the product runs with both operands
- * reduction-contiguous, which is faster; with less (or NULL) W is read
- * transposed by the kernel.  The results are bitwise the same either way.
- * The workspace needs no initialisation and holds W^T after the call.
+ * reduction-contiguous, which is faster at those token counts; otherwise
+ * (fewer tokens per expert, a smaller workspace, or NULL) W is read
+ * transposed by the kernel, and the workspace size is 0 below that count.
+ * The results are bitwise the same either way.  The workspace needs no
+ * initialisation and holds W^T after a call that used it.
  */
 drgg_status grouped_gemm_dgrad(const void *G, const void *W, const int32_t *group_offsets,
                                int32_t E, int64_t M, int64_t N, int64_t K,
@@ -282,7 +285,8 @@ drgg_status drgg_router_split(int64_t M, int64_t N, int64_t K, int64_t *ks, int6
  * Workspace bytes (written to *bytes, a HOST pointer) that a call with these
  * arguments needs; they do not depend on the CU count (cu_count is accepted
  * for symmetry with drgg_plan and ignored).  0 bytes for fwd; for dgrad the
- * optional W^T buffer; for wgrad the buffers of the variant's reduction:
+ * optional W^T buffer (0 when the experts average fewer than 3072 tokens);
+ * for wgrad the buffers of the variant's reduction:
  * the deterministic variant's per-chunk FP32 partials, folded in a fixed
  * order, or the split program's shared FP32 tile sums and per-tile tickets
  * (flashinfer PR #8258, Summary: the split tail adds FP32 partial tiles into
@@ -350,11 +354,14 @@ drgg_status drgg_wgrad_chunking(int64_t T, int64_t chunk_max, int64_t *chunk_len
  *                         where the split program writes {slack placement
  *                         taken (0/1), tail tiles of the banded walk, banded
  *                         walk taken (0/1), grid}; 0 = off
+ *   DRGG_KNOB_DGRAD_WT    1 = the data gradient transposes W into its
+ *                         workspace at every size (0 = only when the experts
+ *                         average at least 3072 tokens)
  * None of them changes the arithmetic of the deterministic variant.
  */
 enum { DRGG_KNOB_TILE = 1, DRGG_KNOB_GRID = 2, DRGG_KNOB_REVERSE = 3, DRGG_KNOB_TIMING = 4,
        DRGG_KNOB_NONDET = 5, DRGG_KNOB_CHECK_OFFSETS = 6, DRGG_KNOB_CHECK_WORKSPACE = 7,
-       DRGG_KNOB_DELAY_SEED = 8, DRGG_KNOB_SPLIT_REPORT = 9 };
+       DRGG_KNOB_DELAY_SEED = 8, DRGG_KNOB_SPLIT_REPORT = 9, DRGG_KNOB_DGRAD_WT = 10 };
 drgg_status drgg_set_knob(int knob, int64_t value);
 
 /*

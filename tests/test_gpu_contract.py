@@ -664,6 +664,14 @@ def test_graph_replays_match_eager(drgg):
     between them, gives the eager results bit for bit.  The split program in
     its own graph: every replay matches the oracle and leaves its workspace
     zero."""
+    drgg.set_knob(drgg.KNOB_DGRAD_WT, 1)   # W^T at these 768 tokens per expert too
+    try:
+        _graph_replays(drgg)
+    finally:
+        drgg.set_knob(drgg.KNOB_DGRAD_WT, 0)
+
+
+def _graph_replays(drgg):
     prob = _tail_problem()
     dv = dev_inputs(prob)
     small = ragged_problem(*DET_CASE)   # within the fixed array of the call that allocates nothing

@@ -471,3 +471,20 @@ def test_plans_give_experts_without_tokens_no_items(drgg):
         assert drgg.wgrad_tail_plan(_offs(counts), 768, 1024)[0] is True
         # 4 tail tiles (one 256-row band of 4 tiles) for each of the 31 experts with tokens
         assert drgg.wgrad_split_plan(_offs(counts), 768, 1024, banded=True) == (False, 31 * 4, True)
+
+
+def test_dgrad_transposes_w_only_from_3072_tokens_per_expert(drgg):
+    """The data gradient's W^T workspace (and with it the transpose) is
+    planned only when the experts average at least 3072 tokens; the test
+    knob forces it at any size."""
+    cases = [((4, 512, 512, 256), 0), ((8, 16384, 1024, 1024), 0), ((3, 9215, 64, 64), 0),
+             ((3, 9216, 64, 64), 3 * 64 * 64 * 2), ((8, 131072, 1536, 2048), 8 * 1536 * 2048 * 2),
+             ((1, 16384, 4096, 4096), 4096 * 4096 * 2), ((5, 20000, 72, 136), 5 * 72 * 136 * 2)]
+    for (E, M, N, K), want in cases:
+        got = drgg.workspace_size(drgg.OP_DGRAD, E, M, N, K, drgg.BF16, True)
+        assert got == -(-want // 256) * 256, (E, M, N, K, got)
+    drgg.set_knob(drgg.KNOB_DGRAD_WT, 1)
+    try:
+        assert drgg.workspace_size(drgg.OP_DGRAD, 4, 512, 512, 256, drgg.BF16, True) == 4 * 512 * 256 * 2
+    finally:
+        drgg.set_knob(drgg.KNOB_DGRAD_WT, 0)
