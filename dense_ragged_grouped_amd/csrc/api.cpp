@@ -186,7 +186,7 @@ drgg_status make_plan(drgg_op op, int32_t E, int64_t M, int64_t N, int64_t K, in
     int tile = (int)g_knob_tile.load();
     if (tile < kTileAuto || tile > kTile64x256) tile = kTileAuto;
     if (tile == kTile64x256 && op != DRGG_OP_WGRAD) tile = kTileAuto;
-    if (tile == kTileAuto) tile = default_tile((int)op, N, K);
+    if (tile == kTileAuto) tile = default_tile((int)op, M, N, K);
     p->tile = tile;
     p->ts = tile_shape(tile);
     const int64_t bm = p->ts.bm, bn = p->ts.bn;
@@ -682,7 +682,7 @@ drgg_status drgg_wgrad_split_plan(const int32_t* group_offsets, int32_t E, int64
     if (!group_offsets || !slack || !tail_tiles || E < 1 || E > kMaxExperts || N < 8 || K < 8 || grid < 1 ||
         tile < kTileAuto || tile > kTile64x256)
         return DRGG_EINVAL;
-    const TileShape ts = tile_shape(tile == kTileAuto ? default_tile(DRGG_OP_WGRAD, N, K) : tile);
+    const TileShape ts = tile_shape(tile == kTileAuto ? default_tile(DRGG_OP_WGRAD, 0, N, K) : tile);
     int64_t out[2];
     *slack = wgrad_split_plan(group_offsets, E, N, K, ts.bm, ts.bn, grid, out) ? 1 : 0;
     *tail_tiles = out[0];

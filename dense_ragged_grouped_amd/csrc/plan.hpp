@@ -420,11 +420,24 @@ inline RouterSplit router_split(int64_t M, int64_t N, int64_t K) {
 // gradient (N <= 64: 64x256) and outputs of at most 128 columns (Y has N,
 // dX and dW have K), where a 256-wide tile would be at least half masked:
 // 128x128 (measured on per-head projections with K = 128: data gradient
-// -12 %, weight gradient -5 %).
-inline int default_tile(int op, int64_t N, int64_t K) {
+// -12 %, weight gradient -5 %).  A forward or data gradient whose 256x256
+// tiles cannot fill half of the CUs even with every group's rows packed
+// (ceil(M/256) * ceil(cols/256) <= kRuleCUs / 2) also takes 128x128: its
+// persistent grid then runs one 256x256 tile per busy workgroup while most
+// CUs idle, and four times the tiles of a quarter the work finish sooner
+// (measured, kernel times: 4 groups of 128 tokens with K = 256, N = 512:
+// forward 12.6 -> 10.0 us, data gradient 17.4 -> 12.5 us; one group of
+// 2048 tokens at 4096 x 4096: 89 -> 71 us and 93 -> 77 us; 128 groups of
+// 64 tokens at 1024 x 1024: 60 -> 52 us and 71 -> 62 us).  From a full wave
+// of 256x256 tiles on, 256x256 was as fast or faster at every measured
+// point.  The output bits do not depend on the tile (every element sums its
+// reduction in the same order).  The weight gradient keeps 256x256: its
+// deterministic program already cuts the token range into chunks.
+inline int default_tile(int op, int64_t M, int64_t N, int64_t K) {
     if (op == 2 && N <= 64) return kTile64x256;
     const int64_t cols = op == 0 ? N : K;
     if (cols <= 128) return kTile128x128;
+    if (op != 2 && ceil_div(M, 256) * ceil_div(cols, 256) <= kRuleCUs / 2) return kTile128x128;
     return kTile256x256;
 }
 

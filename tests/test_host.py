@@ -488,3 +488,26 @@ def test_dgrad_transposes_w_only_from_3072_tokens_per_expert(drgg):
         assert drgg.workspace_size(drgg.OP_DGRAD, 4, 512, 512, 256, drgg.BF16, True) == 4 * 512 * 256 * 2
     finally:
         drgg.set_knob(drgg.KNOB_DGRAD_WT, 0)
+
+
+def test_small_forward_and_data_gradient_take_128_tiles(drgg):
+    """A forward or data gradient whose 256x256 tiles could fill at most half
+    of 256 CUs (ceil(M/256) * ceil(cols/256) <= 128, cols = N forward, K data
+    gradient) is planned on 128x128 tiles; larger calls and every weight
+    gradient keep their tiles."""
+    def tile(op, E, M, N, K):
+        p = drgg.plan(op, E, M, N, K)
+        return p["tile_m"], p["tile_n"]
+    F, D, W = drgg.OP_FWD, drgg.OP_DGRAD, drgg.OP_WGRAD
+    assert tile(F, 4, 512, 512, 256) == (128, 128)            # 2 x 2 tiles
+    assert tile(D, 4, 512, 512, 256) == (128, 128)
+    assert tile(F, 1, 32768, 256, 4096) == (128, 128)         # 128 x 1: exactly half
+    assert tile(F, 1, 32769, 256, 4096) == (256, 256)         # 129 x 1
+    assert tile(D, 1, 32769, 4096, 256) == (256, 256)         # data gradient counts K's columns
+    assert tile(D, 1, 32768, 4096, 256) == (128, 128)
+    assert tile(F, 1, 32768, 4096, 256) == (256, 256)         # 128 x 16
+    assert tile(F, 8, 131072, 1536, 2048) == (256, 256)
+    assert tile(D, 32, 8192, 2048, 768) == (128, 128)         # 32 x 3
+    assert tile(F, 32, 8192, 2048, 768) == (256, 256)         # 32 x 8
+    assert tile(W, 4, 512, 512, 256) == (256, 256)
+    assert tile(W, 1, 16384, 48, 4096) == (64, 256)
