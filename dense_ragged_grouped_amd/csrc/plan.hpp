@@ -420,24 +420,40 @@ inline RouterSplit router_split(int64_t M, int64_t N, int64_t K) {
 // gradient (N <= 64: 64x256) and outputs of at most 128 columns (Y has N,
 // dX and dW have K), where a 256-wide tile would be at least half masked:
 // 128x128 (measured on per-head projections with K = 128: data gradient
-// -12 %, weight gradient -5 %).  A forward or data gradient whose 256x256
-// tiles cannot fill half of the CUs even with every group's rows packed
-// (ceil(M/256) * ceil(cols/256) <= kRuleCUs / 2) also takes 128x128: its
-// persistent grid then runs one 256x256 tile per busy workgroup while most
-// CUs idle, and four times the tiles of a quarter the work finish sooner
-// (measured, kernel times: 4 groups of 128 tokens with K = 256, N = 512:
-// forward 12.6 -> 10.0 us, data gradient 17.4 -> 12.5 us; one group of
-// 2048 tokens at 4096 x 4096: 89 -> 71 us and 93 -> 77 us; 128 groups of
-// 64 tokens at 1024 x 1024: 60 -> 52 us and 71 -> 62 us).  From a full wave
-// of 256x256 tiles on, 256x256 was as fast or faster at every measured
-// point.  The output bits do not depend on the tile (every element sums its
+// -12 %, weight gradient -5 %).  The forward and data gradient then look at
+// how many 256x256 tiles the call has: between lo = ceil(M/256) * ct (every
+// group's rows packed, ct = ceil(cols/256)) and hi = floor((M + 255 E)/256)
+// * ct (each group adds at most one partial row tile).
+//  * lo <= kRuleCUs / 2: 128x128.  The persistent grid would run one
+//    256x256 tile per busy workgroup while most CUs idle; four times the
+//    tiles of a quarter the work finish sooner (kernel times, 4 groups of 128
+//    tokens with K = 256, N = 512: forward 12.6 -> 10.0 us, data gradient
+//    17.4 -> 12.5 us; one group of 2048 tokens at 4096 x 4096: 89 -> 71 us
+//    and 93 -> 77 us; 128 groups of 64 tokens at 1024 x 1024: 60 -> 52 us
+//    and 71 -> 62 us).
+//  * kRuleCUs < lo and hi <= 3 kRuleCUs / 2 (between one and one and a half
+//    waves), with both operands reduction-contiguous (the forward, and the
+//    data gradient on W^T): 128x256.  A second round of 256x256 tiles would
+//    run at most half full; 128x256 tiles (4 waves) fill their rounds better
+//    (8 groups of 1536 tokens at gate_up's N = 1536, K = 2048: forward 105.5
+//    -> 100.9 us, data gradient 90.8 -> 83.5 us; one group of 5120 / 6144
+//    tokens at 4096 x 4096: forward 207.9 -> 186.7 / 211.6 -> 200.3 us, data
+//    gradient 206.2 -> 186.0 / 210.7 -> 194.4 us).  At one wave and from
+//    1.9 waves on 256x256 was as fast or faster at every measured point, and
+//    the data gradient that reads W transposed lost 15 % on 128x256.
+// The output bits do not depend on the tile (every element sums its
 // reduction in the same order).  The weight gradient keeps 256x256: its
 // deterministic program already cuts the token range into chunks.
-inline int default_tile(int op, int64_t M, int64_t N, int64_t K) {
+inline int default_tile(int op, int64_t E, int64_t M, int64_t N, int64_t K, bool kmajor) {
     if (op == 2 && N <= 64) return kTile64x256;
     const int64_t cols = op == 0 ? N : K;
     if (cols <= 128) return kTile128x128;
-    if (op != 2 && ceil_div(M, 256) * ceil_div(cols, 256) <= kRuleCUs / 2) return kTile128x128;
+    if (op == 2) return kTile256x256;
+    const int64_t ct = ceil_div(cols, 256);
+    const int64_t lo = ceil_div(M, 256) * ct;
+    const int64_t hi = (M + 255 * E) / 256 * ct;
+    if (lo <= kRuleCUs / 2) return kTile128x128;
+    if (kmajor && lo > kRuleCUs && hi <= kRuleCUs * 3 / 2) return kTile128x256;
     return kTile256x256;
 }
 

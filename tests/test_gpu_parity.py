@@ -181,6 +181,40 @@ def test_forward_and_data_gradient_same_bits_across_one_wave_boundary(drgg):
     parity.compare(prob, "fwd", parity.from_dev(y64), True, what="wave boundary pair forward")
 
 
+PLANNER_TILE_CASES = [
+    # program, seed, E, M, N, K, the planner's tile
+    ("fwd", 650, 2, 8448, 2304, 264, (128, 256)),     # 297 .. 306 tiles of 256x256
+    ("dgrad", 651, 1, 5120, 264, 4096, (128, 256)),   # on W^T, 320 tiles
+    ("fwd", 652, 2, 700, 2304, 264, (128, 128)),      # 27 tiles
+    ("dgrad", 653, 2, 8448, 2304, 264, (128, 128)),   # 66 tiles
+]
+
+
+@pytest.mark.parametrize("case", PLANNER_TILE_CASES, ids=lambda c: f"{c[0]}_M{c[3]}_N{c[4]}_K{c[5]}")
+def test_planner_tiles_match_256_tiles_bitwise(drgg, case):
+    """Calls the planner puts on 128x256 tiles (between one and one and a
+    half waves of 256x256 tiles) or 128x128 tiles (at most half a wave) give
+    the bits of the 256x256 tile; the oracle checks a sample."""
+    program, seed, E, M, N, K, want = case
+    prob = synth.make_problem(f"planner_tile_{seed}", seed, synth.ragged_counts(seed, M, E), N=N, K=K)
+    plan = drgg.plan(drgg.OP_FWD if program == "fwd" else drgg.OP_DGRAD, E, M, N, K)
+    print(f"planner tile {program} E={E} M={M} N={N} K={K}: {plan['tile_m']}x{plan['tile_n']}", flush=True)
+    assert (plan["tile_m"], plan["tile_n"]) == want
+    dv = dev_inputs(prob)
+    for out_dtype in (torch.float32, torch.bfloat16):
+        got = run_program(drgg, program, dv, out_dtype, True)
+        drgg.set_knob(drgg.KNOB_TILE, 1)
+        try:
+            ref = run_program(drgg, program, dv, out_dtype, True)
+        finally:
+            drgg.set_knob(drgg.KNOB_TILE, 0)
+        torch.cuda.synchronize()
+        iv = torch.int32 if out_dtype == torch.float32 else torch.int16
+        assert torch.equal(got.view(iv), ref.view(iv)), f"{program} {out_dtype}"
+    parity.compare(prob, program, parity.from_dev(got), True, idx=parity.sample_indices(prob, program),
+                   what=f"planner tile {program} M={M}")
+
+
 @pytest.mark.parametrize("out_dtype", ["fp32", "bf16"])
 def test_wgrad_without_fold_zeroes_empty_experts(drgg, out_dtype):
     """When no expert can be cut into chunks (chunk_max >= M) the

@@ -511,3 +511,29 @@ def test_small_forward_and_data_gradient_take_128_tiles(drgg):
     assert tile(F, 32, 8192, 2048, 768) == (256, 256)         # 32 x 8
     assert tile(W, 4, 512, 512, 256) == (256, 256)
     assert tile(W, 1, 16384, 48, 4096) == (64, 256)
+
+
+def test_one_to_one_and_a_half_waves_take_128x256_tiles(drgg):
+    """Between one and one and a half waves of 256x256 tiles (more than 256
+    even with every group's rows packed, at most 384 even with one partial
+    row tile per group), a forward or a data gradient on W^T runs 128x256
+    tiles; a data gradient that reads W transposed keeps 256x256."""
+    def tile(op, E, M, N, K):
+        p = drgg.plan(op, E, M, N, K)
+        return p["tile_m"], p["tile_n"]
+    F, D = drgg.OP_FWD, drgg.OP_DGRAD
+    assert tile(F, 8, 12288, 1536, 2048) == (128, 256)        # 288 .. 330 tiles
+    assert tile(F, 1, 5120, 4096, 4096) == (128, 256)         # 320
+    assert tile(D, 1, 5120, 4096, 4096) == (128, 256)         # W^T: 5120 tokens per expert
+    assert tile(D, 1, 6144, 4096, 4096) == (128, 256)         # 384
+    assert tile(F, 1, 6400, 4096, 4096) == (256, 256)         # 400
+    assert tile(F, 1, 4096, 4096, 4096) == (256, 256)         # 256: one full wave
+    assert tile(D, 8, 12288, 2048, 1536) == (256, 256)        # 1536 tokens per expert: W read transposed
+    assert tile(D, 8, 12288, 1536, 2048) == (256, 256)        # 384 packed, up to 440
+    assert tile(F, 64, 16384 + 64, 1536, 2048) == (256, 256)  # 390 packed: beyond the band
+    assert tile(F, 40, 11264, 1536, 2048) == (256, 256)       # 264 packed, up to 498 with partial tiles
+    drgg.set_knob(drgg.KNOB_DGRAD_WT, 1)
+    try:
+        assert tile(D, 8, 12288, 2048, 1536) == (128, 256)    # on W^T: 288 .. 330 tiles
+    finally:
+        drgg.set_knob(drgg.KNOB_DGRAD_WT, 0)
