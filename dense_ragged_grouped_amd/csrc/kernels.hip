@@ -1506,8 +1506,9 @@ __global__ __launch_bounds__((64 * wgrad_det_waves<BM, BN>())) void gg_wgrad_det
     }
     // the fold kernel's per-expert table (the same values from every
     // workgroup; workgroup 0 writes it): T_e, chunks, first partial slot,
-    // first row of the partials (rows above it were stored directly)
-    if (blockIdx.x == 0)
+    // first row of the partials (rows above it were stored directly).  With
+    // zero_empty no fold runs and the call has no workspace.
+    if (blockIdx.x == 0 && !a.zero_empty)
         for (int e = threadIdx.x; e < E; e += blockDim.x) {
             const int32_t S = tS[e];
             const int32_t row0 = tail && S > 1 ? (int32_t)min<int64_t>(a.N, (int64_t)tB[e] * 256) : 0;

@@ -347,9 +347,10 @@ inline bool wgrad_split_plan(const int32_t* offs, int32_t E, int64_t N, int64_t 
 // Partial slots the deterministic weight gradient may need: only experts cut
 // into more than one chunk write partials.  Such an expert has
 // T > chunk_max and at most T / chunk_max + 1 < 2 T / chunk_max chunks, so the
-// total is below 2 M / chunk_max.
+// total is below 2 M / chunk_max.  With M <= chunk_max no expert can be cut
+// (T <= M): no slots, no fold, and no workspace at all.
 inline int64_t wgrad_max_partials(int64_t M, int64_t chunk_max) {
-    return M <= 0 ? 0 : (2 * M) / chunk_max + 1;
+    return M <= chunk_max ? 0 : (2 * M) / chunk_max + 1;
 }
 
 // The tail-split rule of a persistent schedule (flashinfer PR #7516, the

@@ -151,7 +151,8 @@ drgg_status grouped_gemm_dgrad(const void *G, const void *W, const int32_t *grou
  * Workspace: at least grouped_gemm_workspace_size(DRGG_OP_WGRAD, ...) bytes.
  *   deterministic != 0: FP32 chunk partials and a small per-expert table
  *     that the chunk kernel writes for the ordered fold; no initialisation
- *     needed.
+ *     needed.  None (size 0, the pointer may be null) when no expert can be
+ *     cut into chunks (M at most the plan's chunk_max).
  *   deterministic == 0, routed (the default): as deterministic != 0.
  *   deterministic == 0, split program (DRGG_KNOB_NONDET = 1): FP32 tile sums
  *     and tickets that must be zero before the first call

@@ -537,3 +537,15 @@ def test_one_to_one_and_a_half_waves_take_128x256_tiles(drgg):
         assert tile(D, 8, 12288, 2048, 1536) == (128, 256)    # on W^T: 288 .. 330 tiles
     finally:
         drgg.set_knob(drgg.KNOB_DGRAD_WT, 0)
+
+
+def test_wgrad_without_chunks_needs_no_workspace(drgg):
+    """A deterministic weight gradient whose experts can never be cut into
+    chunks (M at most chunk_max) writes no partials and runs no fold: its
+    workspace size is 0, so the call takes a null workspace."""
+    for E, M, N, K in ((4, 512, 512, 256), (1, 512, 2048, 2048), (8, 256, 1024, 1024)):
+        p = drgg.plan(drgg.OP_WGRAD, E, M, N, K, drgg.FP32, True)
+        assert p["chunk_max"] >= M and p["max_partials"] == 0 and p["workspace_bytes"] == 0, (E, M, N, K, p)
+        assert drgg.workspace_size(drgg.OP_WGRAD, E, M, N, K, drgg.FP32, True) == 0
+    p = drgg.plan(drgg.OP_WGRAD, 8, 1024, 1024, 1024, drgg.FP32, True)
+    assert p["chunk_max"] < 1024 and p["max_partials"] > 0 and p["workspace_bytes"] > 0
