@@ -189,7 +189,7 @@ drgg_status make_plan(drgg_op op, int32_t E, int64_t M, int64_t N, int64_t K, in
     // the data gradient reads W^T (its workspace) when the experts average
     // enough tokens, or when the test knob asks for it
     const bool dgrad_wt = op == DRGG_OP_DGRAD && (g_knob_dgrad_wt.load() != 0 || dgrad_transposes_w(E, M));
-    if (tile == kTileAuto) tile = default_tile((int)op, E, M, N, K, op == DRGG_OP_FWD || dgrad_wt);
+    if (tile == kTileAuto) tile = default_tile((int)op, E, M, N, K, op == DRGG_OP_FWD || dgrad_wt, det != 0);
     p->tile = tile;
     p->ts = tile_shape(tile);
     const int64_t bm = p->ts.bm, bn = p->ts.bn;
@@ -684,7 +684,7 @@ drgg_status drgg_wgrad_split_plan(const int32_t* group_offsets, int32_t E, int64
     if (!group_offsets || !slack || !tail_tiles || E < 1 || E > kMaxExperts || N < 8 || K < 8 || grid < 1 ||
         tile < kTileAuto || tile > kTile64x256)
         return DRGG_EINVAL;
-    const TileShape ts = tile_shape(tile == kTileAuto ? default_tile(DRGG_OP_WGRAD, E, 0, N, K, false) : tile);
+    const TileShape ts = tile_shape(tile == kTileAuto ? default_tile(DRGG_OP_WGRAD, E, 0, N, K, false, false) : tile);
     int64_t out[2];
     *slack = wgrad_split_plan(group_offsets, E, N, K, ts.bm, ts.bn, grid, out) ? 1 : 0;
     *tail_tiles = out[0];

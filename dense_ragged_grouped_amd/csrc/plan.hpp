@@ -443,13 +443,31 @@ inline RouterSplit router_split(int64_t M, int64_t N, int64_t K) {
 //    1.9 waves on 256x256 was as fast or faster at every measured point, and
 //    the data gradient that reads W transposed lost 15 % on 128x256.
 // The output bits do not depend on the tile (every element sums its
-// reduction in the same order).  The weight gradient keeps 256x256: its
-// deterministic program already cuts the token range into chunks.
-inline int default_tile(int op, int64_t E, int64_t M, int64_t N, int64_t K, bool kmajor) {
+// reduction in the same order).  The weight gradient keeps 256x256 where its
+// deterministic program cuts the token ranges into chunks (those fill the
+// CUs), and in the split program (det false); when no expert can be cut
+// (M <= chunk_max), the deterministic program's E * ceil(N/256) *
+// ceil(K/256) output tiles are all the parallelism there is, and smaller
+// tiles spread it: at most kRuleCUs / 8 of them take 128x128, at most
+// kRuleCUs / 2 take 128x256 (kernel times, 256x256 -> chosen tile: 4 groups
+// of 128 tokens at N = 512, K = 256: 17.0 -> 13.4 us; 2 groups of 256 at 1024
+// x 512: 19.5 -> 14.9 us; one group of 384 at 768 x 768: 21.0 -> 15.6 us; one
+// group of 512 at 2048 x 2048: 27.0 -> 24.6 us; 8 groups of 64 at 1024 x
+// 1024: 20.8 -> 19.1 us; at 256 tiles 256x256 stays faster, 29.6 against
+// 31.5 us).  Unchunked, the sum of every element runs over the group's
+// tokens in order whatever the tile, so the bits do not change either.
+inline int default_tile(int op, int64_t E, int64_t M, int64_t N, int64_t K, bool kmajor, bool det) {
     if (op == 2 && N <= 64) return kTile64x256;
     const int64_t cols = op == 0 ? N : K;
     if (cols <= 128) return kTile128x128;
-    if (op == 2) return kTile256x256;
+    if (op == 2) {
+        if (det && M > 0 && M <= wgrad_chunk_max((int32_t)E, M, N, K)) {
+            const int64_t t = E * ceil_div(N, 256) * ceil_div(K, 256);
+            if (t <= kRuleCUs / 8) return kTile128x128;
+            if (t <= kRuleCUs / 2) return kTile128x256;
+        }
+        return kTile256x256;
+    }
     const int64_t ct = ceil_div(cols, 256);
     const int64_t lo = ceil_div(M, 256) * ct;
     const int64_t hi = (M + 255 * E) / 256 * ct;
