@@ -306,7 +306,15 @@ drgg_status drgg_workspace_init(void *workspace, size_t workspace_bytes, hipStre
 
 /*
  * The plan a call would use, for inspection (HOST only, touches no GPU when
- * cu_count > 0).  Fields are written to *out (a host pointer).
+ * cu_count > 0).  Fields are written to *out (a host pointer).  The output
+ * tile is 256x256 unless the call is too small to fill the CUs with it: a
+ * forward or data gradient with at most half a wave of 256x256 tiles (even
+ * with every group's rows packed) takes 128x128, one with between one and
+ * one and a half waves (both operands reduction-contiguous) 128x256; a
+ * deterministic weight gradient none of whose groups can be cut into chunks
+ * takes 128x128 up to 32 tiles of 256x256 and 128x256 up to 128; outputs of
+ * at most 128 columns take 128x128 and weight gradients with N <= 64 64x256.
+ * The results do not depend on the tile.
  */
 typedef struct {
     int32_t tile_m, tile_n, tile_k;   /* output tile and reduction step        */
