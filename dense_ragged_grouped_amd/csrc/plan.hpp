@@ -443,28 +443,37 @@ inline RouterSplit router_split(int64_t M, int64_t N, int64_t K) {
 //    1.9 waves on 256x256 was as fast or faster at every measured point, and
 //    the data gradient that reads W transposed lost 15 % on 128x256.
 // The output bits do not depend on the tile (every element sums its
-// reduction in the same order).  The weight gradient keeps 256x256 where its
-// deterministic program cuts the token ranges into chunks (those fill the
-// CUs), and in the split program (det false); when no expert can be cut
-// (M <= chunk_max), the deterministic program's E * ceil(N/256) *
-// ceil(K/256) output tiles are all the parallelism there is, and smaller
-// tiles spread it: at most kRuleCUs / 8 of them take 128x128, at most
-// kRuleCUs / 2 take 128x256 (kernel times, 256x256 -> chosen tile: 4 groups
-// of 128 tokens at N = 512, K = 256: 17.0 -> 13.4 us; 2 groups of 256 at 1024
-// x 512: 19.5 -> 14.9 us; one group of 384 at 768 x 768: 21.0 -> 15.6 us; one
-// group of 512 at 2048 x 2048: 27.0 -> 24.6 us; 8 groups of 64 at 1024 x
-// 1024: 20.8 -> 19.1 us; at 256 tiles 256x256 stays faster, 29.6 against
-// 31.5 us).  Unchunked, the sum of every element runs over the group's
-// tokens in order whatever the tile, so the bits do not change either.
+// reduction in the same order).  The deterministic weight gradient's work
+// items are output tiles over token chunks; with few of them smaller tiles
+// spread the work (the chunks do not depend on the tile, so neither do the
+// bits).  Unchunked (M <= chunk_max: no expert can be cut, every item is a
+// whole expert's tile, often of few tokens) the E * ceil(N/256) *
+// ceil(K/256) items take 128x128 up to kRuleCUs / 8 and 128x256 up to
+// kRuleCUs / 2 (kernel times, 256x256 -> chosen tile: 4 groups of 128 tokens
+// at N = 512, K = 256: 17.0 -> 13.4 us; one group of 384 at 768 x 768: 21.0
+// -> 15.6 us; one group of 512 at 2048 x 2048: 27.0 -> 24.6 us; 8 groups of
+// 64 at 1024 x 1024: 20.8 -> 19.1 us; at 256 items 256x256 stays faster,
+// 29.6 against 31.5 us).  Chunked, U = ceil(N/256) * ceil(K/256) * (E +
+// M / chunk_max) bounds the items; U <= kRuleCUs / 2 takes 128x128, whose
+// four times as many items still fit one round of two workgroups per CU
+// (one group of 4096 tokens at N = 256, K = 1024, U = 36: 35.6 -> 28.5 us;
+// 8192 tokens, U = 68: 39.8 -> 34.3 us; 4 groups, 8192 tokens at 512 x 512,
+// U = 80: 39.9 -> 36.0 us; at U = 160, 144 items, 128x128 lost 23 %).  The
+// split program (det false) keeps 256x256.
 inline int default_tile(int op, int64_t E, int64_t M, int64_t N, int64_t K, bool kmajor, bool det) {
     if (op == 2 && N <= 64) return kTile64x256;
     const int64_t cols = op == 0 ? N : K;
     if (cols <= 128) return kTile128x128;
     if (op == 2) {
-        if (det && M > 0 && M <= wgrad_chunk_max((int32_t)E, M, N, K)) {
-            const int64_t t = E * ceil_div(N, 256) * ceil_div(K, 256);
+        if (!det || M <= 0) return kTile256x256;
+        const int64_t cm = wgrad_chunk_max((int32_t)E, M, N, K);
+        const int64_t p0 = ceil_div(N, 256) * ceil_div(K, 256);
+        if (M <= cm) {
+            const int64_t t = E * p0;
             if (t <= kRuleCUs / 8) return kTile128x128;
             if (t <= kRuleCUs / 2) return kTile128x256;
+        } else if (p0 * (E + M / cm) <= kRuleCUs / 2) {
+            return kTile128x128;
         }
         return kTile256x256;
     }

@@ -312,7 +312,8 @@ drgg_status drgg_workspace_init(void *workspace, size_t workspace_bytes, hipStre
  * with every group's rows packed) takes 128x128, one with between one and
  * one and a half waves (both operands reduction-contiguous) 128x256; a
  * deterministic weight gradient none of whose groups can be cut into chunks
- * takes 128x128 up to 32 tiles of 256x256 and 128x256 up to 128; outputs of
+ * takes 128x128 up to 32 tiles of 256x256 and 128x256 up to 128, one with
+ * chunks 128x128 up to 128 work items (tiles x chunks); outputs of
  * at most 128 columns take 128x128 and weight gradients with N <= 64 64x256.
  * The results do not depend on the tile.
  */

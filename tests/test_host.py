@@ -509,7 +509,7 @@ def test_small_forward_and_data_gradient_take_128_tiles(drgg):
     assert tile(F, 8, 131072, 1536, 2048) == (256, 256)
     assert tile(D, 32, 8192, 2048, 768) == (128, 128)         # 32 x 3
     assert tile(F, 32, 8192, 2048, 768) == (256, 256)         # 32 x 8
-    assert tile(W, 4, 8192, 512, 256) == (256, 256)           # experts cut into chunks
+    assert tile(W, 8, 131072, 1536, 2048) == (256, 256)       # experts cut into chunks, many items
     assert tile(W, 1, 16384, 48, 4096) == (64, 256)
 
 
@@ -551,11 +551,12 @@ def test_wgrad_without_chunks_needs_no_workspace(drgg):
     assert p["chunk_max"] < 1024 and p["max_partials"] > 0 and p["workspace_bytes"] > 0
 
 
-def test_unchunked_weight_gradients_take_smaller_tiles(drgg):
+def test_weight_gradients_with_few_items_take_smaller_tiles(drgg):
     """A deterministic weight gradient none of whose experts can be cut into
     chunks (M <= chunk_max) spreads its E * ceil(N/256) * ceil(K/256) output
     tiles: at most 32 take 128x128, at most 128 take 128x256 (rows over N);
-    the split program and chunked calls keep 256x256."""
+    a chunked one with at most 128 items (bound U) takes 128x128; the split
+    program keeps 256x256."""
     def tile(E, M, N, K, det=True):
         p = drgg.plan(drgg.OP_WGRAD, E, M, N, K, drgg.FP32, det)
         return p["tile_m"], p["tile_n"]
@@ -566,7 +567,12 @@ def test_unchunked_weight_gradients_take_smaller_tiles(drgg):
     assert tile(8, 512, 1024, 1024) == (128, 256)     # 128
     assert tile(64, 512, 512, 512) == (256, 256)      # 256
     assert tile(1, 4096, 4096, 4096) == (256, 256)    # 256
-    assert tile(4, 1024, 512, 512) == (256, 256)      # chunked (chunk_max 512)
+    # chunked: U = ceil(N/256) * ceil(K/256) * (E + M // chunk_max) items at most
+    assert tile(4, 1024, 512, 512) == (128, 128)      # U = 4 * (4 + 2) = 24
+    assert tile(1, 8192, 256, 1024) == (128, 128)     # U = 4 * (1 + 16) = 68
+    assert tile(4, 8192, 512, 512) == (128, 128)      # U = 4 * (4 + 16) = 80
+    assert tile(1, 16384, 256, 1024) == (256, 256)    # U = 4 * (1 + 32) = 132
+    assert tile(2, 4096, 1024, 1024) == (256, 256)    # U = 16 * (2 + 8) = 160
     drgg.set_knob(drgg.KNOB_NONDET, 1)
     try:
         assert tile(4, 512, 512, 256, det=False) == (256, 256)
