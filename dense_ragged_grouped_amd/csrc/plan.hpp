@@ -431,7 +431,12 @@ inline RouterSplit router_split(int64_t M, int64_t N, int64_t K) {
 //    tokens with K = 256, N = 512: forward 12.6 -> 10.0 us, data gradient
 //    17.4 -> 12.5 us; one group of 2048 tokens at 4096 x 4096: 89 -> 71 us
 //    and 93 -> 77 us; 128 groups of 64 tokens at 1024 x 1024: 60 -> 52 us
-//    and 71 -> 62 us).
+//    and 71 -> 62 us).  The same when the groups average fewer than 128
+//    tokens (M < 128 E), whatever lo says: 256-row tiles would then be at
+//    least half padding (64 groups of 86 tokens on average, N = 4096, K =
+//    1024: forward 125.3 -> 111.5 us; 32 groups of 70 at 768 x 4096: data
+//    gradient 50.7 -> 41.5 us; 128x128 was the fastest tile at all 18 such
+//    points measured).
 //  * kRuleCUs < lo and hi <= 3 kRuleCUs / 2 (between one and one and a half
 //    waves), with both operands reduction-contiguous (the forward, and the
 //    data gradient on W^T): 128x256.  A second round of 256x256 tiles would
@@ -480,7 +485,7 @@ inline int default_tile(int op, int64_t E, int64_t M, int64_t N, int64_t K, bool
     const int64_t ct = ceil_div(cols, 256);
     const int64_t lo = ceil_div(M, 256) * ct;
     const int64_t hi = (M + 255 * E) / 256 * ct;
-    if (lo <= kRuleCUs / 2) return kTile128x128;
+    if (lo <= kRuleCUs / 2 || M < 128 * E) return kTile128x128;
     if (kmajor && lo > kRuleCUs && hi <= kRuleCUs * 3 / 2) return kTile128x256;
     return kTile256x256;
 }

@@ -309,7 +309,8 @@ drgg_status drgg_workspace_init(void *workspace, size_t workspace_bytes, hipStre
  * cu_count > 0).  Fields are written to *out (a host pointer).  The output
  * tile is 256x256 unless the call is too small to fill the CUs with it: a
  * forward or data gradient with at most half a wave of 256x256 tiles (even
- * with every group's rows packed) takes 128x128, one with between one and
+ * with every group's rows packed), or whose groups average fewer than 128
+ * tokens, takes 128x128, one with between one and
  * one and a half waves (both operands reduction-contiguous) 128x256; a
  * deterministic weight gradient none of whose groups can be cut into chunks
  * takes 128x128 up to 32 tiles of 256x256 and 128x256 up to 128, one with

@@ -510,6 +510,8 @@ def test_small_forward_and_data_gradient_take_128_tiles(drgg):
     assert tile(D, 32, 8192, 2048, 768) == (128, 128)         # 32 x 3
     assert tile(F, 32, 8192, 2048, 768) == (256, 256)         # 32 x 8
     assert tile(W, 8, 131072, 1536, 2048) == (256, 256)       # experts cut into chunks, many items
+    assert tile(F, 64, 5515, 4096, 1024) == (128, 128)        # lo 352, but under 128 tokens per group
+    assert tile(F, 64, 8192, 4096, 1024) == (256, 256)        # 128 tokens per group on average
     assert tile(W, 1, 16384, 48, 4096) == (64, 256)
 
 
