@@ -580,3 +580,23 @@ def test_weight_gradients_with_few_items_take_smaller_tiles(drgg):
         assert tile(4, 512, 512, 256, det=False) == (256, 256)
     finally:
         drgg.set_knob(drgg.KNOB_NONDET, 0)
+
+
+def test_measured_workloads_tiles(drgg):
+    """The tiles the planner gives the measured workloads (a change here
+    changes what bench.py measures)."""
+    def tile(op, E, M, N, K):
+        p = drgg.plan(op, E, M, N, K)
+        return p["tile_m"], p["tile_n"]
+    F, D, W = drgg.OP_FWD, drgg.OP_DGRAD, drgg.OP_WGRAD
+    # tiny MoE: E=4, 512 tokens, N=512, K=256
+    assert [tile(op, 4, 512, 512, 256) for op in (F, D, W)] == [(128, 128)] * 3
+    # dense projection weight gradients, 16384 tokens, K=4096
+    assert tile(W, 1, 16384, 48, 4096) == (64, 256)
+    assert tile(W, 1, 16384, 64, 4096) == (64, 256)
+    assert tile(W, 1, 16384, 512, 4096) == (256, 256)
+    assert tile(W, 1, 16384, 1024, 4096) == (256, 256)
+    # MoE gate_up (the headline), Zipf down weight gradient, square dense
+    assert [tile(op, 8, 131072, 1536, 2048) for op in (F, D, W)] == [(256, 256)] * 3
+    assert tile(W, 32, 131072, 2048, 768) == (256, 256)
+    assert [tile(op, 1, 16384, 4096, 4096) for op in (F, D, W)] == [(256, 256)] * 3
